@@ -1,0 +1,219 @@
+"""Plain float64 CPU oracle for Linformer low-rank self-attention (one non-causal encoder layer).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this module: only the
+tests, the package's smoke check and the benchmark's CPU-baseline leg use it.  It shares no code
+with the HIP path; its only inputs are plain numpy arrays.
+
+What it computes (per batch item b and head h), written out as the definition, in float64, on the
+exact input values:
+
+  * sequence projection (Linformer 요약 설명, section "Model"; Linformer summary card, section
+    方法适配 "method"; efficient-Transformer survey, section on the low-rank improvement):
+    the keys and values are mixed along the sequence axis by E, F of shape k x n,
+        Kbar = E . K,   Vbar = F . V,   giving k x d matrices.
+    Each row of E holds the weights that combine the n positions into one projected key.
+  * compressed scaled dot-product attention (Linformer 요약 설명, sections "Model" and
+    "Transformer and Self-Attention"; survey, section 2.1): an n x k score matrix, softmax over
+    the k projected slots for each query, then the weighted sum of Vbar; the queries are not
+    compressed, so the output is n x d.  Scale = 1/sqrt(d) unless given.
+  * projection sharing (Linformer summary card, section 方法适配; Linformer 요약 설명, section
+    "Additional Efficiency Techniques"): unshared per-head E_h, F_h; headwise (one E and one F
+    for all heads); key-value (one matrix, E = F, for all heads); layerwise (one matrix for
+    every head, both K and V, and every layer -- within one layer it computes what key-value
+    sharing computes).
+  * padding to a fixed maximum length (Linformer 요약 설명, section "Model": E, F are sized for the
+    maximum length, so shorter inputs are padded).  Reading: positions t >= L_b contribute
+    nothing to Kbar, Vbar (exactly what zero padding gives), the softmax still runs over all k
+    slots, and output rows i >= L_b are zero.
+
+Library primitives used as single steps: ``numpy.matmul`` (dense products) and ``numpy.exp``.
+No blocking, fusion or reordering beyond the definition.
+
+Every function here is pinned by the "not gpu" tests (hand-derived fixtures under
+tests/golden/, a separately written brute-force textbook attention, closed forms and
+invariants); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+SHARE_NONE = 0
+SHARE_HEADWISE = 1
+SHARE_KV = 2
+SHARE_LAYERWISE = 3
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def head_projections(E: np.ndarray, F: Optional[np.ndarray], share: int, heads: int
+                     ) -> Tuple[list, list]:
+    """The (E_h, F_h) pair each head uses, per the sharing mode.
+
+    Linformer summary card, section 方法适配: headwise, key-value and layerwise sharing; the
+    layerwise mode uses a single projection matrix for the whole model.  E and F are stored as
+    [H_E, k, n] with H_E = heads for unshared projections and 1 otherwise.  For key-value and
+    layerwise sharing F must be None or equal to E.  Unshared mode also accepts F = None, which
+    means E_h = F_h per head.
+    """
+    E = _f64(E)
+    if share == SHARE_NONE:
+        if E.shape[0] != heads:
+            raise ValueError("unshared projections need one E per head")
+        Fm = E if F is None else _f64(F)
+        if Fm.shape != E.shape:
+            raise ValueError("E and F shapes differ")
+        return [E[h] for h in range(heads)], [Fm[h] for h in range(heads)]
+    if E.shape[0] != 1:
+        raise ValueError("shared projections store a single E")
+    if share == SHARE_HEADWISE:
+        if F is None:
+            raise ValueError("headwise sharing keeps a separate F")
+        Fm = _f64(F)
+        return [E[0]] * heads, [Fm[0]] * heads
+    if share in (SHARE_KV, SHARE_LAYERWISE):
+        if F is not None and not np.array_equal(_f64(F), E):
+            raise ValueError("key-value / layerwise sharing uses E = F")
+        return [E[0]] * heads, [E[0]] * heads
+    raise ValueError(f"unknown sharing mode {share}")
+
+
+def project(P: np.ndarray, X: np.ndarray, length: Optional[int] = None) -> np.ndarray:
+    """Sequence projection Pbar = P . X over the valid positions.
+
+    Linformer 요약 설명, section "Model": P (E or F) is k x n, X (K or V) is n x d, the product is
+    k x d.  Positions t >= length contribute nothing (the padding reading), which is the same as
+    multiplying by X with those rows set to zero.
+    """
+    P = _f64(P)
+    X = _f64(X)
+    n = X.shape[0]
+    L = n if length is None else max(0, min(int(length), n))
+    return np.matmul(P[:, :L], X[:L, :])
+
+
+def scores(Q: np.ndarray, Kbar: np.ndarray, scale: float) -> np.ndarray:
+    """n x k context scores scale * Q . Kbar^T (scaled dot product against the projected keys)."""
+    return float(scale) * np.matmul(_f64(Q), _f64(Kbar).T)
+
+
+def softmax_rows(S: np.ndarray) -> np.ndarray:
+    """Softmax of each row (one query) over its k entries: exp(s - max) / sum exp(s - max).
+
+    Linformer 요약 설명, section "Transformer and Self-Attention": the softmax runs per query along
+    the key axis.  Subtracting the row maximum changes nothing mathematically and keeps exp finite.
+    """
+    S = _f64(S)
+    m = S.max(axis=1, keepdims=True)
+    w = np.exp(S - m)
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def attention_weights(Q: np.ndarray, Kbar: np.ndarray, scale: float) -> np.ndarray:
+    """P-bar = softmax(scale * Q . Kbar^T), the n x k context matrix of one head."""
+    return softmax_rows(scores(Q, Kbar, scale))
+
+
+def attend(Q: np.ndarray, Kbar: np.ndarray, Vbar: np.ndarray, scale: Optional[float] = None,
+           length: Optional[int] = None) -> np.ndarray:
+    """O = softmax(scale * Q . Kbar^T) . Vbar for one head, rows >= length set to zero.
+
+    Linformer 요약 설명, section "Model": queries are not compressed, so there is one output row
+    per input position (n x d).  ``length`` None computes every row.
+    """
+    Q = _f64(Q)
+    d = Q.shape[1]
+    s = (1.0 / np.sqrt(d)) if (scale is None or scale == 0.0) else float(scale)
+    O = np.matmul(attention_weights(Q, Kbar, s), _f64(Vbar))
+    if length is not None:
+        L = max(0, min(int(length), Q.shape[0]))
+        O[L:, :] = 0.0
+    return O
+
+
+def forward(Q, K, V, E, F, share: int, lengths: Optional[Sequence[int]] = None,
+            scale: Optional[float] = None, pairs: Optional[Sequence[Tuple[int, int]]] = None,
+            return_intermediates: bool = False):
+    """Linformer attention for a [B, H, n, d] batch: project K and V, then attend.
+
+    ``pairs`` restricts the work to the listed (b, h) slices (the others stay zero), for bounded
+    checks of large workloads.  With ``return_intermediates`` it also returns Kbar, Vbar
+    ([B, H, k, d]) so each half of the path can be checked on its own.
+    """
+    Q = _f64(Q)
+    B, H, n, d = Q.shape
+    Es, Fs = head_projections(E, F, share, H)
+    k = Es[0].shape[0]
+    O = np.zeros((B, H, n, d))
+    Kb = np.zeros((B, H, k, d))
+    Vb = np.zeros((B, H, k, d))
+    todo = [(b, h) for b in range(B) for h in range(H)] if pairs is None else list(pairs)
+    for b, h in todo:
+        L = None if lengths is None else int(lengths[b])
+        Kb[b, h] = project(Es[h], K[b, h], L)
+        Vb[b, h] = project(Fs[h], V[b, h], L)
+        O[b, h] = attend(Q[b, h], Kb[b, h], Vb[b, h], scale, L)
+    if return_intermediates:
+        return O, Kb, Vb
+    return O
+
+
+def dense_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: Optional[float] = None,
+                    length: Optional[int] = None) -> np.ndarray:
+    """Standard softmax attention of one head: softmax(scale * Q . K^T) . V with an n x n matrix.
+
+    Linformer 요약 설명, section "Transformer and Self-Attention"; survey, section 2.1 (scaled dot
+    product).  With a ``length``, keys at positions >= length are left out of each softmax (the
+    same padding reading as for the projection: padded positions contribute nothing) and output
+    rows >= length are zero.  This is the comparison baseline's definition.
+    """
+    Q = _f64(Q)
+    n, d = Q.shape
+    s = (1.0 / np.sqrt(d)) if (scale is None or scale == 0.0) else float(scale)
+    L = n if length is None else max(0, min(int(length), n))
+    O = np.zeros((n, _f64(V).shape[1]))
+    if L == 0:
+        return O
+    Sm = s * np.matmul(Q[:L], _f64(K)[:L].T)
+    O[:L] = np.matmul(softmax_rows(Sm), _f64(V)[:L])
+    return O
+
+
+def dense_forward(Q, K, V, lengths: Optional[Sequence[int]] = None,
+                  scale: Optional[float] = None,
+                  pairs: Optional[Sequence[Tuple[int, int]]] = None) -> np.ndarray:
+    """Dense attention over a [B, H, n, d] batch (optionally only some (b, h) slices)."""
+    Q = _f64(Q)
+    B, H, n, d = Q.shape
+    O = np.zeros((B, H, n, d))
+    todo = [(b, h) for b in range(B) for h in range(H)] if pairs is None else list(pairs)
+    for b, h in todo:
+        L = None if lengths is None else int(lengths[b])
+        O[b, h] = dense_attention(Q[b, h], K[b, h], V[b, h], scale, L)
+    return O
+
+
+def slice_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
+    """Largest per-(b, h) slice value of max|out - ref| / max|ref| (0/0 counts as 0).
+
+    The accuracy metric the tolerances are stated in: elementwise relative error is unbounded
+    where an output crosses zero, so each slice is normalised by its own largest magnitude.
+    """
+    out = _f64(out)
+    ref = _f64(ref)
+    lead = ref.shape[:-2]
+    worst = 0.0
+    for idx in np.ndindex(*lead) if lead else [()]:
+        r = ref[idx]
+        o = out[idx]
+        den = np.abs(r).max() if r.size else 0.0
+        num = np.abs(o - r).max() if r.size else 0.0
+        if den == 0.0:
+            e = 0.0 if num == 0.0 else np.inf
+        else:
+            e = num / den
+        worst = max(worst, float(e))
+    return worst

@@ -1,0 +1,70 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail at least one pin.
+
+Each mutant replaces one oracle function with a plausible wrong version; the listed pin tests are
+then run against the mutated oracle and must raise.  This shows the pins are sharp enough to
+catch a transposed operand, a dropped scale, a wrong softmax axis, a wrong padding reading and a
+wrong sharing map.
+"""
+import numpy as np
+import pytest
+
+from oracle import linformer_oracle as orc
+from tests import test_oracle_pins as pins
+
+
+def _proj_transposed(P, X, length=None):
+    P = np.asarray(P, dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
+    L = X.shape[0] if length is None else int(length)
+    return np.matmul(P.T[:, :L], X[:L])
+
+
+def _scores_unscaled(Q, Kbar, scale):
+    return np.matmul(np.asarray(Q, float), np.asarray(Kbar, float).T)
+
+
+def _softmax_cols(S):
+    S = np.asarray(S, dtype=np.float64)
+    w = np.exp(S - S.max(axis=0, keepdims=True))
+    return w / w.sum(axis=0, keepdims=True)
+
+
+def _proj_ignores_length(P, X, length=None):
+    return np.matmul(np.asarray(P, float), np.asarray(X, float))
+
+
+_orig_heads = orc.head_projections
+
+
+def _headwise_uses_E_for_V(E, F, share, heads):
+    Es, Fs = _orig_heads(E, F, share, heads)
+    return Es, list(Es)
+
+
+def _sign_flip_scores(Q, Kbar, scale):
+    return -float(scale) * np.matmul(np.asarray(Q, float), np.asarray(Kbar, float).T)
+
+
+MUTANTS = [
+    ("project", _proj_transposed, [pins.test_golden_orientation]),
+    ("scores", _scores_unscaled, [pins.test_golden_scale]),
+    ("scores", _sign_flip_scores, [pins.test_golden_orientation, pins.test_golden_scale]),
+    ("softmax_rows", _softmax_cols, [pins.test_golden_orientation,
+                                     pins.test_softmax_rows_sum_to_one]),
+    ("project", _proj_ignores_length, [pins.test_golden_padding,
+                                       pins.test_padding_ignores_positions_past_length]),
+    ("head_projections", _headwise_uses_E_for_V, [pins.test_golden_orientation,
+                                                   pins.test_golden_orientation_sharing_modes]),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(MUTANTS)))
+def test_mutant_is_caught(idx, monkeypatch):
+    name, fn, checks = MUTANTS[idx]
+    monkeypatch.setattr(orc, name, fn)
+    for check in checks:
+        with pytest.raises((AssertionError, ValueError)):
+            if check is pins.test_golden_orientation_sharing_modes:
+                check(orc.SHARE_HEADWISE)
+            else:
+                check()
