@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Throughput of Linformer attention on one MI355X: tokens/s for one non-causal encoder layer at
+B8 H12 n4096 d64 k256 bf16 with unshared per-head E, F and padded lengths in [2048, 4096].
+
+A step is one linformer_forward call (sequence projection, then compressed attention) over the
+whole batch, inputs already resident in device memory.  Input replicas are rotated so that
+consecutive steps do not find their inputs in the 256 MB last-level cache.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Linformer attention tokens/s at n=4096,k=256 bf16; % of MFMA/HBM roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "efficient_transformer_attention_seq_amd", "csrc")
+KERNEL_SOURCES = {"attend": "attend_bf16.hip", "project": "proj_bf16.hip"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    with open(os.path.join(CSRC, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_bytes(kernel: str, workload: str):
+    """HBM bytes per launch from the committed PMC counter summary, if it was taken on the
+    current kernel source (else None)."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(f"{kernel}:{workload}")
+    if not ent or ent.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def algorithmic(wl, kernel: str):
+    """(bytes, flops) the method needs per launch, counted from the definition.
+
+    project: read K and V once, each unique E/F matrix once; write Kbar (hi and lo planes)
+             and Vbar.  flops 2*n*k*d for each of Kbar and Vbar per (b, h).
+    attend : read Q once and Kbar (hi, lo) and Vbar once per (b, h); write O once.
+             flops 2*n*k*d for the scores and 2*n*k*d for the weighted sum per (b, h).
+    """
+    B, H, n, d, k = wl.batch, wl.heads, wl.n, wl.d, wl.k
+    bh = B * H
+    eb = 2  # bf16
+    kv_out = 3 * bh * k * d * eb
+    if kernel == "project":
+        n_mats = wl.e_heads * (2 if wl.separate_f else 1)
+        byts = 2 * bh * n * d * eb + n_mats * k * n * eb + kv_out
+        flops = 4.0 * bh * n * k * d
+    else:
+        byts = 2 * bh * n * d * eb + kv_out
+        flops = 4.0 * bh * n * k * d
+    return byts, flops
+
+
+def cpu_baseline(inp, budget_s: float = 30.0):
+    """The float64 oracle, as it stands, on the host cores: one pass over the workload (or the
+    first batch items that fit the time budget)."""
+    import numpy as np
+    from oracle import linformer_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    wl = inp.wl
+    pairs_all = [(b, h) for b in range(wl.batch) for h in range(wl.heads)]
+    # time one batch item first, then as many as fit the budget
+    t0 = time.perf_counter()
+    orc.forward(inp.Q, inp.K, inp.V, inp.E, inp.F, wl.share, inp.lengths,
+                pairs=pairs_all[:wl.heads])
+    t1 = time.perf_counter() - t0
+    nb = max(1, min(wl.batch, int(budget_s / max(t1, 1e-6))))
+    if nb > 1:
+        t0 = time.perf_counter()
+        orc.forward(inp.Q, inp.K, inp.V, inp.E, inp.F, wl.share, inp.lengths,
+                    pairs=pairs_all[:nb * wl.heads])
+        dt = time.perf_counter() - t0
+    else:
+        nb, dt = 1, t1
+    tokens = nb * wl.n
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    del np
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{nb} of {wl.batch} batch items ({nb * wl.heads} (b,h) slices), "
+                      f"full n={wl.n}, float64 numpy, {dt:.2f} s on {cpu}",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--workload", default="long_b8_h12_n4096_k256_unshared_padded")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--kernel-iters", type=int, default=20)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures a single GPU; --gpus N > 1 is not supported by this build "
+              "(the path is per-GPU; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from efficient_transformer_attention_seq_amd import linformer as L
+    from efficient_transformer_attention_seq_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    L.lib()  # fail loudly if the HIP library is missing
+    wl = synth.WORKLOADS[args.workload]
+    log(f"workload {wl}")
+    t0 = time.time()
+    inp = synth.make_inputs(wl)
+    log(f"inputs drawn in {time.time() - t0:.1f}s; lengths={None if inp.lengths is None else inp.lengths.tolist()}")
+
+    td = torch.bfloat16 if wl.dtype == synth.DT_BF16 else torch.float32
+
+    def dev(x):
+        return torch.from_numpy(x).to(td).cuda()
+
+    p = L.problem(wl.batch, wl.heads, wl.n, wl.d, wl.k, wl.dtype, wl.share, 0.0)
+    reps = []
+    for r in range(args.replicas):
+        reps.append(dict(Q=dev(inp.Q), K=dev(inp.K), V=dev(inp.V), E=dev(inp.E),
+                         F=dev(inp.F) if inp.F is not None else None))
+    lens = (torch.tensor(inp.lengths, dtype=torch.int32, device="cuda")
+            if inp.lengths is not None else None)
+    O = torch.empty(wl.batch, wl.heads, wl.n, wl.d, dtype=td, device="cuda")
+    wsb = L.linformer_workspace_size(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    kb, vb = L.linformer_kv_sizes(p)
+    Kbar = torch.empty(kb, dtype=torch.uint8, device="cuda")
+    Vbar = torch.empty(vb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        r = reps[i % len(reps)]
+        L.linformer_forward(p, r["Q"], r["K"], r["V"], r["E"], r["F"], lens, O, ws, wsb,
+                            stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tokens = wl.batch * wl.n
+    log(f"forward: {ms * 1e3:.1f} us/step ({tokens / (ms / 1e3):.3e} tokens/s), wall {wall:.3f}s")
+
+    # ---- per-kernel timing of the two halves, on the same stream, with rotated replicas
+    def time_half(kind, iters):
+        for i in range(3):
+            run_half(kind, i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(iters):
+            run_half(kind, i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters * 1e3  # us
+
+    def run_half(kind, i):
+        r = reps[i % len(reps)]
+        if kind == "project":
+            L.linformer_project_kv(p, r["K"], r["V"], r["E"], r["F"], lens, Kbar, Vbar, ws,
+                                   wsb, stream=stream)
+        else:
+            L.linformer_attend(p, r["Q"], Kbar, Vbar, lens, O, stream=stream)
+
+    L.linformer_project_kv(p, reps[0]["K"], reps[0]["V"], reps[0]["E"], reps[0]["F"], lens,
+                           Kbar, Vbar, ws, wsb, stream=stream)
+    kern = {}
+    for kind in ("project", "attend"):
+        us = time_half(kind, args.kernel_iters)
+        byts, flops = algorithmic(wl, kind)
+        kern[kind] = dict(us=us, bytes=byts, flops=flops, gbs=byts / (us * 1e-6) / 1e9,
+                          tflops=flops / (us * 1e-6) / 1e12)
+        log(f"{kind}: {us:.1f} us/launch, {kern[kind]['gbs']:.0f} GB/s algorithmic, "
+            f"{kern[kind]['tflops']:.1f} TFLOP/s")
+    dom = max(kern, key=lambda k: kern[k]["us"])
+    kd = kern[dom]
+    traffic = traffic_bytes(dom, wl.name)
+    roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(kd["gbs"] / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "kernel": dom, "avg_us": round(kd["us"], 2),
+                "algorithmic_bytes": kd["bytes"],
+                "mfma_tflops": round(kd["tflops"], 1),
+                "mfma_frac": round(kd["tflops"] / PEAK_BF16_TFLOPS, 4)}
+    step_bytes = kern["project"]["bytes"] + kern["attend"]["bytes"]
+    step_flops = kern["project"]["flops"] + kern["attend"]["flops"]
+    roof_us = max(step_bytes / (PEAK_HBM_GBS * 1e9), step_flops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
+
+    dense = None
+    if not args.no_dense and wl.dtype == synth.DT_BF16 and wl.n <= 16384:
+        Od = torch.empty_like(O)
+        for i in range(2):
+            L.attention_dense_forward(p, reps[i % len(reps)]["Q"], reps[i % len(reps)]["K"],
+                                      reps[i % len(reps)]["V"], lens, Od, stream=stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nd = max(3, args.steps // 4)
+        a.record(stream)
+        for i in range(nd):
+            r = reps[i % len(reps)]
+            L.attention_dense_forward(p, r["Q"], r["K"], r["V"], lens, Od, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        dms = a.elapsed_time(b) / nd
+        dense = {"ms": round(dms, 4), "speedup_vs_dense": round(dms / ms, 2)}
+        log(f"dense O(n^2) attention: {dms * 1e3:.1f} us/step, Linformer speedup {dms / ms:.2f}x")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the host cores ...")
+        cpu = cpu_baseline(inp)
+        log(f"oracle: {cpu['value']:.3e} tokens/s on {cpu['cores']} threads ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == synth.DT_BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "seq_len": wl.n,
+                   "head_dim": wl.d, "k": wl.k, "share": synth.SHARE_NAMES[wl.share],
+                   "padded": wl.padded, "replicas": args.replicas},
+        "roofline": roofline,
+        "step_roofline": {"algorithmic_bytes": step_bytes, "roofline_us": round(roof_us, 2),
+                          "frac": round(roof_us / (ms * 1e3), 4)},
+        "kernels_us": {k: round(v["us"], 2) for k, v in kern.items()},
+        "dense_comparator": dense,
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+        "wall_s": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,363 @@
+// liblinformer C ABI: argument validation, workspace layout and kernel dispatch.
+// The operations are declared (with their citations) in include/linformer.h.
+#include "linformer.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "lf_launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+size_t elem_size(int dtype) { return dtype == LF_BF16 ? 2 : 4; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int env_int(const char* name) {
+    const char* v = std::getenv(name);
+    return v ? std::atoi(v) : 0;
+}
+
+// Tuning overrides (for measurement sweeps only; one code path): LINFORMER_PROJ_SPLIT forces
+// the number of position splits, LINFORMER_PROJ_UPT the units per projection tile,
+// LINFORMER_ATTEND_QTB the queries per attention workgroup.
+bool geometry(const lf_problem* p, lf::ProjGeom* g) {
+    return lf::proj_geometry(p->batch, p->heads, p->n, p->k, p->share,
+                             env_int("LINFORMER_PROJ_SPLIT"), env_int("LINFORMER_PROJ_UPT"), g);
+}
+
+int check_problem(const lf_problem* p) {
+    if (!p) return LF_ERR_NULL;
+    if (p->dtype != LF_F32 && p->dtype != LF_BF16) return LF_ERR_DTYPE;
+    if (p->share < LF_SHARE_NONE || p->share > LF_SHARE_LAYERWISE) return LF_ERR_SHARE;
+    if (p->batch < 1 || p->heads < 1 || p->d != 64) return LF_ERR_SHAPE;
+    if (p->n < 64 || p->n % 64) return LF_ERR_SHAPE;
+    if (p->k < 32 || p->k > 256 || p->k % 32) return LF_ERR_SHAPE;
+    if (!(p->scale >= 0.0f) || !std::isfinite(p->scale)) return LF_ERR_SHAPE;
+    const long long qkv = (long long)p->batch * p->heads * p->n * p->d;
+    const long long ef = (long long)p->heads * p->k * p->n;
+    if (qkv >= (1LL << 31) || ef >= (1LL << 31)) return LF_ERR_SHAPE;
+    return LF_OK;
+}
+
+float eff_scale(const lf_problem* p) {
+    return p->scale > 0.0f ? p->scale : 1.0f / std::sqrt((float)p->d);
+}
+
+size_t qkv_bytes(const lf_problem* p) {
+    return (size_t)p->batch * p->heads * p->n * p->d * elem_size(p->dtype);
+}
+size_t ef_bytes(const lf_problem* p) {
+    const size_t he = p->share == LF_SHARE_NONE ? (size_t)p->heads : 1;
+    return he * p->k * p->n * elem_size(p->dtype);
+}
+size_t kbar_bytes(const lf_problem* p) {
+    const size_t e = (size_t)p->batch * p->heads * p->k * p->d;
+    return p->dtype == LF_BF16 ? 2 * e * 2 : e * 4;
+}
+size_t vbar_bytes(const lf_problem* p) {
+    return (size_t)p->batch * p->heads * p->k * p->d * elem_size(p->dtype);
+}
+size_t part_bytes(const lf_problem* p, const lf::ProjGeom& g) {
+    if (p->dtype != LF_BF16 || g.S <= 1) return 0;
+    return (size_t)g.S * 2 * p->batch * p->heads * p->k * p->d * 4;
+}
+
+struct Range {
+    const void* p;
+    size_t n;
+};
+bool overlap(Range a, Range b) {
+    if (!a.p || !b.p || !a.n || !b.n) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+bool any_overlap(const Range* outs, int nout, const Range* ins, int nin) {
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlap(outs[i], ins[j])) return true;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j])) return true;
+    }
+    return false;
+}
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Resolves F per the sharing rule; returns LF_OK or LF_ERR_SHARE / LF_ERR_NULL.
+int resolve_f(const lf_problem* p, const void* E, const void* F, const void** Fout) {
+    if (p->share == LF_SHARE_HEADWISE) {
+        if (!F) return LF_ERR_NULL;
+        *Fout = F;
+        return LF_OK;
+    }
+    if (p->share == LF_SHARE_KV || p->share == LF_SHARE_LAYERWISE) {
+        if (F && F != E) return LF_ERR_SHARE;
+        *Fout = E;
+        return LF_OK;
+    }
+    *Fout = F ? F : E;
+    return LF_OK;
+}
+
+int check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return LF_ERR_NO_DEVICE;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return LF_ERR_ARCH;
+    int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return LF_ERR_NO_DEVICE;
+        }
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? LF_OK : LF_ERR_ARCH;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? LF_OK : LF_ERR_LAUNCH; }
+
+// Validation shared by project_kv and forward (everything about K, V, E, F, lengths, ws).
+int check_project_args(const lf_problem* p, const void* K, const void* V, const void* E,
+                       const void* F, const int32_t* lengths, const lf::ProjGeom& g, void* ws,
+                       size_t ws_bytes, size_t ws_needed, const void** Fres) {
+    if (!K || !V || !E) return LF_ERR_NULL;
+    int st = resolve_f(p, E, F, Fres);
+    if (st) return st;
+    if (!aligned16(K) || !aligned16(V) || !aligned16(E) || !aligned16(*Fres)) return LF_ERR_ALIGN;
+    if (lengths && ((uintptr_t)lengths & 3u)) return LF_ERR_ALIGN;
+    if (ws_needed > 0) {
+        if (!ws || ws_bytes < ws_needed) return LF_ERR_WORKSPACE;
+        if (!aligned16(ws)) return LF_ERR_ALIGN;
+    }
+    (void)g;
+    return LF_OK;
+}
+
+int do_project(const lf_problem* p, const void* K, const void* V, const void* E, const void* F,
+               const int32_t* lengths, void* Kbar, void* Vbar, void* part,
+               const lf::ProjGeom& g, hipStream_t stream) {
+    if (p->dtype == LF_F32) {
+        lf::F32Args a{};
+        a.K = (const float*)K;
+        a.V = (const float*)V;
+        a.E = (const float*)E;
+        a.F = (const float*)F;
+        a.lengths = lengths;
+        a.Kbar = (float*)Kbar;
+        a.Vbar = (float*)Vbar;
+        a.B = p->batch;
+        a.H = p->heads;
+        a.n = p->n;
+        a.k = p->k;
+        a.share = p->share;
+        a.scale = eff_scale(p);
+        return launch_status(lf::launch_proj_f32(a, stream));
+    }
+    lf::ProjBf16Args a{};
+    a.K = (const uint16_t*)K;
+    a.V = (const uint16_t*)V;
+    a.E = (const uint16_t*)E;
+    a.F = (const uint16_t*)F;
+    a.lengths = lengths;
+    const size_t e = (size_t)p->batch * p->heads * p->k * p->d;
+    a.Khi = (uint16_t*)Kbar;
+    a.Klo = (uint16_t*)Kbar + e;
+    a.Vb = (uint16_t*)Vbar;
+    a.part = (float*)part;
+    a.g = g;
+    return launch_status(lf::launch_proj_bf16(a, stream));
+}
+
+int do_attend(const lf_problem* p, const void* Q, const void* Kbar, const void* Vbar,
+              const int32_t* lengths, void* O, hipStream_t stream) {
+    if (p->dtype == LF_F32) {
+        lf::F32Args a{};
+        a.Q = (const float*)Q;
+        a.Kbar = (float*)Kbar;
+        a.Vbar = (float*)Vbar;
+        a.O = (float*)O;
+        a.lengths = lengths;
+        a.B = p->batch;
+        a.H = p->heads;
+        a.n = p->n;
+        a.k = p->k;
+        a.share = p->share;
+        a.scale = eff_scale(p);
+        return launch_status(lf::launch_attend_f32(a, stream));
+    }
+    lf::AttendBf16Args a{};
+    const size_t e = (size_t)p->batch * p->heads * p->k * p->d;
+    a.Q = (const uint16_t*)Q;
+    a.Khi = (const uint16_t*)Kbar;
+    a.Klo = (const uint16_t*)Kbar + e;
+    a.Vb = (const uint16_t*)Vbar;
+    a.lengths = lengths;
+    a.O = (uint16_t*)O;
+    a.B = p->batch;
+    a.H = p->heads;
+    a.n = p->n;
+    a.k = p->k;
+    int qtb = env_int("LINFORMER_ATTEND_QTB");
+    if (qtb <= 0 || qtb % 32) qtb = 512;
+    a.qtb = qtb;
+    a.QB = (p->n + qtb - 1) / qtb;
+    a.nlogical = p->batch * p->heads * a.QB;
+    a.c = eff_scale(p) * lf::kLog2e;
+    return launch_status(lf::launch_attend_bf16(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* linformer_status_string(int status) {
+    switch (status) {
+        case LF_OK: return "LF_OK";
+        case LF_ERR_NULL: return "LF_ERR_NULL: a required pointer is NULL";
+        case LF_ERR_SHAPE: return "LF_ERR_SHAPE: a dimension or the scale is out of range";
+        case LF_ERR_DTYPE: return "LF_ERR_DTYPE: unknown dtype";
+        case LF_ERR_SHARE: return "LF_ERR_SHARE: bad sharing mode or F must alias E";
+        case LF_ERR_WORKSPACE: return "LF_ERR_WORKSPACE: workspace missing or too small";
+        case LF_ERR_ALIGN: return "LF_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case LF_ERR_ALIAS: return "LF_ERR_ALIAS: an output overlaps another buffer";
+        case LF_ERR_NO_DEVICE: return "LF_ERR_NO_DEVICE: no HIP device available";
+        case LF_ERR_ARCH: return "LF_ERR_ARCH: the current device is not gfx950";
+        case LF_ERR_LAUNCH: return "LF_ERR_LAUNCH: kernel launch failed";
+        default: return "unknown liblinformer status";
+    }
+}
+
+int linformer_kv_sizes(const lf_problem* p, size_t* kb, size_t* vb) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!kb || !vb) return LF_ERR_NULL;
+    *kb = kbar_bytes(p);
+    *vb = vbar_bytes(p);
+    return LF_OK;
+}
+
+int linformer_workspace_size(const lf_problem* p, size_t* bytes) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!bytes) return LF_ERR_NULL;
+    lf::ProjGeom g;
+    if (!geometry(p, &g)) return LF_ERR_SHAPE;
+    *bytes = round_up(kbar_bytes(p), 256) + round_up(vbar_bytes(p), 256) +
+             round_up(part_bytes(p, g), 256);
+    return LF_OK;
+}
+
+int linformer_project_kv(const lf_problem* p, const void* K, const void* V, const void* E,
+                         const void* F, const int32_t* lengths, void* Kbar, void* Vbar,
+                         void* ws, size_t ws_bytes, void* stream) {
+    int st = check_problem(p);
+    if (st) return st;
+    lf::ProjGeom g;
+    if (!geometry(p, &g)) return LF_ERR_SHAPE;
+    const size_t need = part_bytes(p, g);
+    const void* Fr = nullptr;
+    st = check_project_args(p, K, V, E, F, lengths, g, ws, ws_bytes, need, &Fr);
+    if (st) return st;
+    if (!Kbar || !Vbar) return LF_ERR_NULL;
+    if (!aligned16(Kbar) || !aligned16(Vbar)) return LF_ERR_ALIGN;
+    const Range ins[] = {{K, qkv_bytes(p)}, {V, qkv_bytes(p)}, {E, ef_bytes(p)},
+                         {Fr, ef_bytes(p)}, {lengths, lengths ? 4u * p->batch : 0u}};
+    const Range outs[] = {{Kbar, kbar_bytes(p)}, {Vbar, vbar_bytes(p)}, {ws, need}};
+    if (any_overlap(outs, 3, ins, 5)) return LF_ERR_ALIAS;
+    st = check_device();
+    if (st) return st;
+    return do_project(p, K, V, E, Fr, lengths, Kbar, Vbar, ws, g, (hipStream_t)stream);
+}
+
+int linformer_attend(const lf_problem* p, const void* Q, const void* Kbar, const void* Vbar,
+                     const int32_t* lengths, void* O, void* stream) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!Q || !Kbar || !Vbar || !O) return LF_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(Kbar) || !aligned16(Vbar) || !aligned16(O)) return LF_ERR_ALIGN;
+    if (lengths && ((uintptr_t)lengths & 3u)) return LF_ERR_ALIGN;
+    const Range ins[] = {{Q, qkv_bytes(p)}, {Kbar, kbar_bytes(p)}, {Vbar, vbar_bytes(p)},
+                         {lengths, lengths ? 4u * p->batch : 0u}};
+    const Range outs[] = {{O, qkv_bytes(p)}};
+    if (any_overlap(outs, 1, ins, 4)) return LF_ERR_ALIAS;
+    st = check_device();
+    if (st) return st;
+    return do_attend(p, Q, Kbar, Vbar, lengths, O, (hipStream_t)stream);
+}
+
+int linformer_forward(const lf_problem* p, const void* Q, const void* K, const void* V,
+                      const void* E, const void* F, const int32_t* lengths, void* O, void* ws,
+                      size_t ws_bytes, void* stream) {
+    int st = check_problem(p);
+    if (st) return st;
+    lf::ProjGeom g;
+    if (!geometry(p, &g)) return LF_ERR_SHAPE;
+    const size_t kb = round_up(kbar_bytes(p), 256), vb = round_up(vbar_bytes(p), 256);
+    const size_t pb = part_bytes(p, g);
+    const size_t need = kb + vb + round_up(pb, 256);
+    const void* Fr = nullptr;
+    st = check_project_args(p, K, V, E, F, lengths, g, ws, ws_bytes, need, &Fr);
+    if (st) return st;
+    if (!Q || !O) return LF_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(O)) return LF_ERR_ALIGN;
+    const Range ins[] = {{Q, qkv_bytes(p)}, {K, qkv_bytes(p)}, {V, qkv_bytes(p)},
+                         {E, ef_bytes(p)},  {Fr, ef_bytes(p)}, {lengths, lengths ? 4u * p->batch : 0u}};
+    const Range outs[] = {{O, qkv_bytes(p)}, {ws, need}};
+    if (any_overlap(outs, 2, ins, 6)) return LF_ERR_ALIAS;
+    st = check_device();
+    if (st) return st;
+    uint8_t* w = (uint8_t*)ws;
+    void* Kbar = w;
+    void* Vbar = w + kb;
+    void* part = pb ? (void*)(w + kb + vb) : nullptr;
+    hipStream_t s = (hipStream_t)stream;
+    st = do_project(p, K, V, E, Fr, lengths, Kbar, Vbar, part, g, s);
+    if (st) return st;
+    return do_attend(p, Q, Kbar, Vbar, lengths, O, s);
+}
+
+int attention_dense_forward(const lf_problem* p, const void* Q, const void* K, const void* V,
+                            const int32_t* lengths, void* O, void* stream) {
+    if (!p) return LF_ERR_NULL;
+    if (p->dtype != LF_BF16) return LF_ERR_DTYPE;
+    if (p->batch < 1 || p->heads < 1 || p->d != 64 || p->n < 64 || p->n % 64)
+        return LF_ERR_SHAPE;
+    if (!(p->scale >= 0.0f) || !std::isfinite(p->scale)) return LF_ERR_SHAPE;
+    if ((long long)p->batch * p->heads * p->n * p->d >= (1LL << 31)) return LF_ERR_SHAPE;
+    if (!Q || !K || !V || !O) return LF_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return LF_ERR_ALIGN;
+    if (lengths && ((uintptr_t)lengths & 3u)) return LF_ERR_ALIGN;
+    const Range ins[] = {{Q, qkv_bytes(p)}, {K, qkv_bytes(p)}, {V, qkv_bytes(p)},
+                         {lengths, lengths ? 4u * p->batch : 0u}};
+    const Range outs[] = {{O, qkv_bytes(p)}};
+    if (any_overlap(outs, 1, ins, 4)) return LF_ERR_ALIAS;
+    int st = check_device();
+    if (st) return st;
+    lf::DenseBf16Args a{};
+    a.Q = (const uint16_t*)Q;
+    a.K = (const uint16_t*)K;
+    a.V = (const uint16_t*)V;
+    a.lengths = lengths;
+    a.O = (uint16_t*)O;
+    a.B = p->batch;
+    a.H = p->heads;
+    a.n = p->n;
+    a.QB = (p->n + lf::kDenseQTB - 1) / lf::kDenseQTB;
+    a.nlogical = p->batch * p->heads * a.QB;
+    a.c = eff_scale(p) * lf::kLog2e;
+    return launch_status(lf::launch_dense_bf16(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Internal launcher interface between the C-ABI host layer (api.cpp) and the kernel translation
+// units.  Every launcher assumes its arguments were validated by api.cpp and returns the
+// hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lf {
+
+// Projection work is organised in "units": one unit = one (which, b, h) output matrix, with
+// which = 0 for Kbar = A.K and 1 for Vbar = A.V.  Units that multiply the same projection matrix A
+// form a group; a group's units share every load of A.
+//   unshared  : group g = which * H + h, members b            (A = E_h or F_h)
+//   headwise  : group g = which,          members (b, h)       (A = E or F)
+//   key-value / layerwise: one group,     members (which, b, h) (A = E)
+struct ProjGeom {
+    int B, H, n, k, share;
+    int groups;           // number of distinct A matrices in use
+    int members;          // units per group
+    int upt;              // units per workgroup tile
+    int tiles_per_group;  // ceil(members / upt)
+    int S;                // splits of the position axis
+    int steps_per_split;  // 64-position steps in one split
+    int nlogical;         // groups * S * tiles_per_group
+};
+
+struct ProjBf16Args {
+    const uint16_t* K;
+    const uint16_t* V;
+    const uint16_t* E;
+    const uint16_t* F;      // never null here (= E when shared or when unshared F is omitted)
+    const int32_t* lengths;
+    uint16_t* Khi;          // [B, H, k, 64]
+    uint16_t* Klo;          // [B, H, k, 64]
+    uint16_t* Vb;           // [B, H, k, 64]
+    float* part;            // [S, 2, B*H, k, 64] when S > 1
+    ProjGeom g;
+};
+
+struct AttendBf16Args {
+    const uint16_t* Q;
+    const uint16_t* Khi;
+    const uint16_t* Klo;
+    const uint16_t* Vb;
+    const int32_t* lengths;
+    uint16_t* O;
+    int B, H, n, k;
+    int qtb;       // queries per workgroup (multiple of 32)
+    int QB;        // ceil(n / qtb)
+    int nlogical;  // B * H * QB
+    float c;       // scale * log2(e)
+};
+
+struct F32Args {
+    const float* Q;
+    const float* K;
+    const float* V;
+    const float* E;
+    const float* F;
+    const int32_t* lengths;
+    float* Kbar;
+    float* Vbar;
+    float* O;
+    int B, H, n, k, share;
+    float scale;
+};
+
+struct DenseBf16Args {
+    const uint16_t* Q;
+    const uint16_t* K;
+    const uint16_t* V;
+    const int32_t* lengths;
+    uint16_t* O;
+    int B, H, n;
+    int QB;
+    int nlogical;
+    float c;  // scale * log2(e)
+};
+
+// Projection geometry for a problem (deterministic; `split_override` > 0 forces S, `upt_override`
+// > 0 forces the units per tile).  Returns false if the shape is unsupported.
+bool proj_geometry(int B, int H, int n, int k, int share, int split_override, int upt_override,
+                   ProjGeom* out);
+
+hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream);
+hipError_t launch_attend_bf16(const AttendBf16Args& a, hipStream_t stream);
+hipError_t launch_proj_f32(const F32Args& a, hipStream_t stream);
+hipError_t launch_attend_f32(const F32Args& a, hipStream_t stream);
+hipError_t launch_dense_bf16(const DenseBf16Args& a, hipStream_t stream);
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kAttendThreads = 512;
+constexpr int kDenseQTB = 256;  // queries per dense-attention workgroup
+
+}  // namespace lf

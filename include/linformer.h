@@ -1,0 +1,136 @@
+/*
+ * liblinformer -- Linformer low-rank self-attention for one non-causal encoder layer,
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method (Linformer 요약 설명, greeksharifa.github.io, section "Model"; Linformer summary
+ * card, ai-papers.xuzou.cn, section 方法适配 "method"): for every batch item b and head h the keys
+ * and values are projected along the sequence axis by E, F of shape k x n,
+ *     Kbar = E . K,   Vbar = F . V               (k x d each)
+ * and each query attends to the k projected slots,
+ *     O = softmax(scale * Q . Kbar^T) . Vbar     (n x d, softmax over the k slots of a row).
+ *
+ * Tensor layouts (all row-major, contiguous, element type per lf_problem.dtype):
+ *   Q, K, V, O : [batch, heads, n, d]
+ *   E, F       : [H_E, k, n], H_E = heads for LF_SHARE_NONE, 1 for the shared modes
+ *   lengths    : int32 [batch] in device memory, or NULL (every position valid)
+ * n is the fixed, padded maximum length.  With lengths, positions t >= lengths[b] contribute
+ * nothing to Kbar, Vbar (exactly what zero padding would give), the softmax still covers all k
+ * slots, and output rows i >= lengths[b] are written as zero.  Lengths are clamped to [0, n] on
+ * the device.  (Padding: Linformer 요약 설명, section "Model" -- the length-axis projection is
+ * sized for a maximum length, so shorter inputs are padded.)
+ *
+ * Projection sharing (Linformer summary card, section 方法适配; Linformer 요약 설명, section
+ * "Additional Efficiency Techniques"):
+ *   LF_SHARE_NONE      per-head E_h and F_h (E, F hold `heads` matrices; F may equal E)
+ *   LF_SHARE_HEADWISE  one E and one F for all heads of the layer
+ *   LF_SHARE_KV        one matrix for all heads, E = F (F must be NULL or equal to E)
+ *   LF_SHARE_LAYERWISE one matrix for all heads, E = F, and the caller passes the same E to
+ *                      every layer (within one call it computes what LF_SHARE_KV computes)
+ *
+ * Precision:
+ *   LF_F32  : fp32 in, fp32 arithmetic, fp32 out.
+ *   LF_BF16 : bf16 Q, K, V, E, F, O; all sums accumulate in fp32; the softmax runs in fp32.
+ *             Kbar is kept to fp32 accuracy as a pair of bf16 planes (hi = bf16(Kbar),
+ *             lo = bf16(Kbar - hi)); Vbar and the softmax weights are rounded once to bf16
+ *             (round to nearest even) for the matrix cores.
+ *
+ * Shape limits: d == 64; k % 32 == 0 and 32 <= k <= 256; n % 64 == 0 and n >= 64;
+ * batch >= 1, heads >= 1; batch * heads * n * d < 2^31 elements.
+ *
+ * Ownership and threading: the caller owns every buffer (device memory) and keeps it alive until
+ * the stream has finished the call.  The library allocates nothing and keeps no state between
+ * calls except a per-device architecture check; calls are reentrant.  Work is enqueued on
+ * `stream` (a hipStream_t; NULL means the default stream) and the calls return before it runs.
+ *
+ * Errors: every argument is validated on the host before anything is enqueued, so an error
+ * return means no work was queued.  Faults during execution surface at the caller's next
+ * synchronisation.  No C++ exception crosses this interface.
+ */
+#ifndef LINFORMER_H
+#define LINFORMER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum lf_status {
+    LF_OK = 0,
+    LF_ERR_NULL = 1,       /* a required pointer is NULL                                   */
+    LF_ERR_SHAPE = 2,      /* a dimension is outside the limits above                       */
+    LF_ERR_DTYPE = 3,      /* unknown dtype                                                 */
+    LF_ERR_SHARE = 4,      /* unknown sharing mode, or F given where it must alias E        */
+    LF_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than linformer_workspace_size()     */
+    LF_ERR_ALIGN = 6,      /* a tensor pointer is not 16-byte aligned                       */
+    LF_ERR_ALIAS = 7,      /* an output range overlaps an input or another output range     */
+    LF_ERR_NO_DEVICE = 8,  /* no HIP device is available                                    */
+    LF_ERR_ARCH = 9,       /* the current device is not gfx950                              */
+    LF_ERR_LAUNCH = 10     /* a kernel launch was rejected by the runtime                   */
+};
+
+enum lf_dtype { LF_F32 = 0, LF_BF16 = 1 };
+
+enum lf_share {
+    LF_SHARE_NONE = 0,
+    LF_SHARE_HEADWISE = 1,
+    LF_SHARE_KV = 2,
+    LF_SHARE_LAYERWISE = 3
+};
+
+/* Problem descriptor, passed by pointer; read only during the call. */
+typedef struct lf_problem {
+    int32_t batch;   /* B                                                    */
+    int32_t heads;   /* H                                                    */
+    int32_t n;       /* padded maximum sequence length                       */
+    int32_t d;       /* head dimension (64)                                  */
+    int32_t k;       /* projected length                                     */
+    int32_t dtype;   /* enum lf_dtype                                        */
+    int32_t share;   /* enum lf_share                                        */
+    float scale;     /* score scale; 0 means 1/sqrt(d)                       */
+} lf_problem;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* linformer_status_string(int status);
+
+/* Bytes of device workspace linformer_forward() and linformer_project_kv() need for `p`
+ * (it covers Kbar/Vbar staging and the projection's split partial sums).  Host only. */
+int linformer_workspace_size(const lf_problem* p, size_t* bytes);
+
+/* Bytes of the Kbar and Vbar buffers linformer_project_kv() writes and linformer_attend() reads.
+ *   LF_F32 : Kbar fp32 [B, H, k, d];            Vbar fp32 [B, H, k, d]
+ *   LF_BF16: Kbar bf16 [2, B, H, k, d] (hi, lo); Vbar bf16 [B, H, k, d]           Host only. */
+int linformer_kv_sizes(const lf_problem* p, size_t* kbar_bytes, size_t* vbar_bytes);
+
+/* Sequence projection, Kbar = E_h . K_{b,h} and Vbar = F_h . V_{b,h} over the valid positions
+ * (Linformer 요약 설명, section "Model").  K, V, E, F and lengths are read; Kbar, Vbar are
+ * written in the layouts of linformer_kv_sizes(); ws is scratch (its contents on entry do not
+ * matter).  F: per the sharing mode above (NULL allowed for NONE, meaning F = E). */
+int linformer_project_kv(const lf_problem* p, const void* K, const void* V, const void* E,
+                         const void* F, const int32_t* lengths, void* Kbar, void* Vbar,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Compressed attention, O = softmax(scale * Q . Kbar^T) . Vbar per (b, h), rows >= lengths[b]
+ * zero (Linformer 요약 설명, sections "Model" and "Transformer and Self-Attention").  Q, Kbar,
+ * Vbar, lengths are read; O is written. */
+int linformer_attend(const lf_problem* p, const void* Q, const void* Kbar, const void* Vbar,
+                     const int32_t* lengths, void* O, void* stream);
+
+/* The whole layer: linformer_project_kv() into the workspace, then linformer_attend(). */
+int linformer_forward(const lf_problem* p, const void* Q, const void* K, const void* V,
+                      const void* E, const void* F, const int32_t* lengths, void* O, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Standard O(n^2) softmax attention of every (b, h) on the same device, the comparison
+ * baseline for Linformer (Linformer 요약 설명, section "Transformer and Self-Attention"):
+ * O = softmax(scale * Q . K^T) . V.  With lengths, keys at positions >= lengths[b] are left out
+ * of the softmax and rows >= lengths[b] are zero.  p->k, p->share are ignored; bf16 only. */
+int attention_dense_forward(const lf_problem* p, const void* Q, const void* K, const void* V,
+                            const int32_t* lengths, void* O, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINFORMER_H */

@@ -1,0 +1,341 @@
+"""GPU parity: liblinformer (through its C ABI) against the float64 oracle on the same seeded
+inputs.  Tolerances (per (b, h) slice, max|gpu - ref| / max|ref|): 1e-4 for the fp32 path and
+2e-2 for bf16 in / fp32 accumulate, the accuracy bars set for this path.  Intermediate Kbar
+(hi + lo planes) is held to fp32 accuracy (1e-4) and the bf16 Vbar to its rounding (4e-3).
+"""
+import numpy as np
+import pytest
+
+from efficient_transformer_attention_seq_amd import linformer as L
+from efficient_transformer_attention_seq_amd import synth
+from oracle import linformer_oracle as orc
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+BF, F32 = synth.DT_BF16, synth.DT_F32
+NONE, HEAD, KV, LAYER = (synth.SHARE_NONE, synth.SHARE_HEADWISE, synth.SHARE_KV,
+                         synth.SHARE_LAYERWISE)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    torch = G.torch_mod()
+    if torch.cuda.device_count() < 1:
+        pytest.skip("no GPU")
+    G.log(f"device: {torch.cuda.get_device_name(0)}")
+    yield
+
+
+def _ref_forward(inp, scale=None, pairs=None):
+    return orc.forward(inp.Q, inp.K, inp.V, inp.E, inp.F, inp.wl.share, inp.lengths, scale,
+                       pairs=pairs)
+
+
+def _ref_project(inp):
+    _, Kb, Vb = orc.forward(inp.Q, inp.K, inp.V, inp.E, inp.F, inp.wl.share, inp.lengths,
+                            return_intermediates=True)
+    return Kb, Vb
+
+
+def _lengths(rng, B, n):
+    out = [n] + [int(x) for x in rng.integers(1, n, size=B - 1)] if B > 1 else [n - 17]
+    return out
+
+
+# --------------------------------------------------------------------------- projection
+PROJ_CASES = [
+    # B, H, n, k, share
+    (2, 3, 192, 64, NONE),
+    (1, 2, 320, 96, HEAD),
+    (2, 2, 256, 256, KV),
+    (3, 1, 128, 32, LAYER),
+    (1, 3, 512, 128, NONE),
+    (2, 2, 448, 160, HEAD),
+]
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+@pytest.mark.parametrize("case", PROJ_CASES)
+def test_project_parity(case, dtype):
+    B, H, n, k, share = case
+    rng = np.random.default_rng(1000 + n + k)
+    lens = _lengths(rng, B, n)
+    inp = synth.random_inputs(B, H, n, 64, k, dtype, share, seed=n * 7 + k, lengths=lens)
+    G.log(f"project case={case} dtype={dtype} lengths={lens}")
+    kb, vb = G.run_project(inp)
+    rk, rv = _ref_project(inp)
+    ek, ev = orc.slice_rel_err(kb, rk), orc.slice_rel_err(vb, rv)
+    G.log(f"  Kbar err {ek:.3e}  Vbar err {ev:.3e}")
+    assert ek <= (1e-5 if dtype == F32 else 1e-4)
+    assert ev <= (1e-5 if dtype == F32 else 4e-3)
+
+
+@pytest.mark.parametrize("split,upt", [(1, 2), (2, 2), (3, 1), (5, 4), (8, 2)])
+def test_project_split_and_tile_variants(split, upt):
+    """Every split count and tile width computes the same thing (fixed-order split sums)."""
+    rng = np.random.default_rng(77)
+    B, H, n, k = 3, 2, 640, 128
+    lens = [640, 333, 64]
+    inp = synth.random_inputs(B, H, n, 64, k, BF, NONE, seed=5, lengths=lens)
+    G.log(f"project split={split} upt={upt}")
+    with G.env(LINFORMER_PROJ_SPLIT=split, LINFORMER_PROJ_UPT=upt):
+        kb, vb = G.run_project(inp)
+    rk, rv = _ref_project(inp)
+    assert orc.slice_rel_err(kb, rk) <= 1e-4
+    assert orc.slice_rel_err(vb, rv) <= 4e-3
+    del rng
+
+
+def test_kbar_planes_are_hi_lo_split():
+    """Kbar's lo plane is the bf16 rounding of the residual of the hi plane: |lo| <= ulp(hi)/2."""
+    inp = synth.random_inputs(2, 2, 256, 64, 128, BF, KV, seed=9)
+    hi, lo = G.run_project_planes(inp)
+    ulp = np.abs(hi) * 2.0 ** -7
+    assert np.all(np.abs(lo) <= 0.5 * ulp + 1e-30)
+
+
+# ------------------------------------------------------------------------------- attend
+ATT_CASES = [
+    # B, H, n, k, lengths
+    (2, 2, 256, 256, [256, 100]),
+    (1, 3, 192, 128, None),
+    (1, 1, 64, 32, [1]),
+    (2, 1, 320, 96, [0, 319]),
+    (1, 2, 576, 160, [500]),
+    (1, 1, 1088, 224, [1088]),
+]
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+@pytest.mark.parametrize("case", ATT_CASES)
+def test_attend_parity(case, dtype):
+    B, H, n, k, lens = case
+    pr = synth.random_projected(B, H, n, 64, k, dtype, seed=n + k)
+    wl = synth.Workload("attend", B, H, n, 64, k, dtype, NONE)
+    G.log(f"attend case={case} dtype={dtype}")
+    out = G.run_attend(pr, wl, lens)
+    ref = np.zeros_like(out)
+    for b in range(B):
+        for h in range(H):
+            kbar = pr.Khi[b, h].astype(np.float64) + pr.Klo[b, h].astype(np.float64)
+            ref[b, h] = orc.attend(pr.Q[b, h], kbar, pr.Vbar[b, h], None,
+                                   None if lens is None else lens[b])
+    err = orc.slice_rel_err(out, ref)
+    G.log(f"  err {err:.3e}")
+    assert err <= G.TOL[dtype]
+
+
+@pytest.mark.parametrize("qtb", [32, 256, 1024])
+def test_attend_workgroup_sizes(qtb):
+    B, H, n, k = 1, 2, 1024, 256
+    pr = synth.random_projected(B, H, n, 64, k, BF, seed=3)
+    wl = synth.Workload("attend", B, H, n, 64, k, BF, NONE)
+    G.log(f"attend qtb={qtb}")
+    with G.env(LINFORMER_ATTEND_QTB=qtb):
+        out = G.run_attend(pr, wl, [700])
+    ref = np.zeros_like(out)
+    for h in range(H):
+        ref[0, h] = orc.attend(pr.Q[0, h], pr.Khi[0, h].astype(np.float64) + pr.Klo[0, h],
+                               pr.Vbar[0, h], None, 700)
+    assert orc.slice_rel_err(out, ref) <= 2e-2
+
+
+def test_attend_explicit_scale():
+    B, H, n, k = 1, 1, 128, 64
+    pr = synth.random_projected(B, H, n, 64, k, BF, seed=4, kbar_std=1.0)
+    wl = synth.Workload("attend", B, H, n, 64, k, BF, NONE)
+    out = G.run_attend(pr, wl, None, scale=0.3)
+    ref = orc.attend(pr.Q[0, 0], pr.Khi[0, 0].astype(np.float64) + pr.Klo[0, 0],
+                     pr.Vbar[0, 0], 0.3)
+    assert orc.slice_rel_err(out[0, 0][None, None], ref[None, None]) <= 2e-2
+
+
+# ------------------------------------------------------------------------------ forward
+FWD_CASES = [
+    (2, 3, 384, 128, NONE),
+    (2, 2, 256, 256, HEAD),
+    (3, 2, 320, 64, KV),
+    (1, 4, 640, 96, LAYER),
+]
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+@pytest.mark.parametrize("case", FWD_CASES)
+def test_forward_parity_small(case, dtype):
+    B, H, n, k, share = case
+    rng = np.random.default_rng(n + B)
+    lens = _lengths(rng, B, n)
+    inp = synth.random_inputs(B, H, n, 64, k, dtype, share, seed=11 + n, lengths=lens)
+    G.log(f"forward case={case} dtype={dtype} lengths={lens}")
+    out, ok = G.run_forward(inp, guard=True)
+    err = orc.slice_rel_err(out, _ref_forward(inp))
+    G.log(f"  err {err:.3e}")
+    assert ok, "write outside the output tensor"
+    assert err <= G.TOL[dtype]
+
+
+def test_forward_single_head_f32_full():
+    """Single-head fp32 workload: B1 H1 n512 k128, separate E, F, seed 0 (full comparison)."""
+    inp = synth.make_inputs(synth.C1)
+    G.log("forward C1 full")
+    out, ok = G.run_forward(inp, guard=True)
+    err = orc.slice_rel_err(out, _ref_forward(inp))
+    G.log(f"  err {err:.3e}")
+    assert ok and err <= 1e-4
+
+
+def test_forward_roberta_kv_full():
+    """RoBERTa-base shape, one key-value matrix: B32 H12 n512 k256 bf16 (full comparison)."""
+    inp = synth.make_inputs(synth.C2)
+    G.log("forward C2 full")
+    out, ok = G.run_forward(inp, guard=True)
+    err = orc.slice_rel_err(out, _ref_forward(inp))
+    G.log(f"  err {err:.3e}")
+    assert ok and err <= 2e-2
+
+
+def _sampled(inp, pairs, guard=False):
+    out, ok = G.run_forward(inp, guard=guard)
+    ref = _ref_forward(inp, pairs=pairs)
+    idx = tuple(np.array(pairs).T)
+    return orc.slice_rel_err(out[idx], ref[idx]), ok, out
+
+
+def test_forward_long_padded_sampled():
+    """B8 H12 n4096 k256 unshared, padded lengths in [2048, 4096]: the benchmarked launch,
+    checked on sampled (b, h) slices plus zero rows past every length."""
+    inp = synth.make_inputs(synth.C3)
+    G.log(f"forward C3 lengths={inp.lengths.tolist()}")
+    pairs = [(0, 0), (1, 5), (3, 11), (5, 2), (7, 7), (int(np.argmin(inp.lengths)), 4)]
+    err, ok, out = _sampled(inp, pairs, guard=True)
+    G.log(f"  err {err:.3e}")
+    assert ok and err <= 2e-2
+    for b, Lb in enumerate(inp.lengths):
+        assert np.all(out[b, :, Lb:] == 0.0)
+    assert np.all(np.isfinite(out))
+
+
+def test_forward_extreme_length_sampled():
+    """B1 H12 n65536 k128 layerwise E = F: sampled heads."""
+    inp = synth.make_inputs(synth.C4)
+    G.log("forward C4")
+    err, ok, out = _sampled(inp, [(0, 0), (0, 6), (0, 11)])
+    G.log(f"  err {err:.3e}")
+    assert err <= 2e-2 and np.all(np.isfinite(out))
+
+
+def test_forward_stack_layer_sampled():
+    """Attention part of the 12-layer stack: B16 H12 n1024 k256 layerwise E = F."""
+    inp = synth.make_inputs(synth.C5A)
+    G.log("forward C5A")
+    err, ok, _ = _sampled(inp, [(0, 0), (7, 3), (15, 11)])
+    G.log(f"  err {err:.3e}")
+    assert err <= 2e-2
+
+
+# --------------------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("lens", [[0, 0], [1, 64], [64, 63], [33, 0]])
+def test_forward_edge_lengths(lens):
+    inp = synth.random_inputs(2, 2, 64, 64, 32, BF, NONE, seed=21, lengths=lens)
+    G.log(f"edge lengths {lens}")
+    out, ok = G.run_forward(inp, guard=True)
+    ref = _ref_forward(inp)
+    assert ok
+    assert orc.slice_rel_err(out, ref) <= 2e-2
+    for b, Lb in enumerate(lens):
+        assert np.all(out[b, :, Lb:] == 0.0)
+
+
+def test_forward_without_lengths_equals_full_lengths():
+    inp = synth.random_inputs(2, 2, 256, 64, 128, BF, KV, seed=22)
+    a, _ = G.run_forward(inp)
+    inp2 = synth.random_inputs(2, 2, 256, 64, 128, BF, KV, seed=22, lengths=[256, 256])
+    b, _ = G.run_forward(inp2)
+    assert np.array_equal(a, b)
+
+
+def test_forward_is_deterministic():
+    inp = synth.random_inputs(2, 3, 1024, 64, 256, BF, NONE, seed=23, lengths=[1000, 517])
+    a, _ = G.run_forward(inp)
+    b, _ = G.run_forward(inp)
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- pins checked on the GPU
+@pytest.mark.parametrize("n", [64, 128, 256])
+def test_identity_projection_equals_dense(n):
+    """k = n, E = F = I: Linformer is standard softmax attention (both GPU paths, vs oracle)."""
+    rng = np.random.default_rng(n)
+    B, H = 1, 2
+    Q = synth.to_dtype(rng.standard_normal((B, H, n, 64)), BF)
+    K = synth.to_dtype(rng.standard_normal((B, H, n, 64)), BF)
+    V = synth.to_dtype(rng.standard_normal((B, H, n, 64)), BF)
+    E = np.eye(n, dtype=np.float32)[None]
+    wl = synth.Workload("identity", B, H, n, 64, n, BF, KV)
+    inp = synth.Inputs(wl, Q, K, V, E, None, None)
+    out, _ = G.run_forward(inp)
+    dense = G.run_dense(inp)
+    ref = orc.dense_forward(Q, K, V)
+    assert orc.slice_rel_err(out, ref) <= 2e-2
+    assert orc.slice_rel_err(dense, ref) <= 2e-2
+
+
+def test_identical_rows_closed_form():
+    """All rows of E equal: every output row is the mean of the projected values."""
+    rng = np.random.default_rng(5)
+    B, H, n, k = 1, 2, 256, 128
+    Q = synth.to_dtype(rng.standard_normal((B, H, n, 64)), BF)
+    K = synth.to_dtype(rng.standard_normal((B, H, n, 64)), BF)
+    V = synth.to_dtype(rng.standard_normal((B, H, n, 64)), BF)
+    row = synth.to_dtype(rng.standard_normal((1, 1, n)) / np.sqrt(k), BF)
+    E = np.repeat(row, k, axis=1)
+    F = synth.to_dtype(rng.standard_normal((1, k, n)) / np.sqrt(k), BF)
+    wl = synth.Workload("rows", B, H, n, 64, k, BF, HEAD)
+    out, _ = G.run_forward(synth.Inputs(wl, Q, K, V, E, F, None))
+    for h in range(H):
+        want = (F[0].astype(np.float64).sum(axis=0) @ V[0, h].astype(np.float64)) / k
+        got = out[0, h]
+        assert np.max(np.abs(got - want[None, :])) <= 2e-2 * np.max(np.abs(want))
+
+
+# ------------------------------------------------------------------ dense comparator
+@pytest.mark.parametrize("case", [(1, 2, 256, None), (2, 1, 1024, [1024, 333]),
+                                  (1, 1, 64, [1])])
+def test_dense_parity(case):
+    B, H, n, lens = case
+    inp = synth.random_inputs(B, H, n, 64, 32, BF, NONE, seed=n, lengths=lens)
+    G.log(f"dense case={case}")
+    out = G.run_dense(inp)
+    ref = orc.dense_forward(inp.Q, inp.K, inp.V, lens)
+    err = orc.slice_rel_err(out, ref)
+    G.log(f"  err {err:.3e}")
+    assert err <= 2e-2
+
+
+# ------------------------------------------------------------------- error paths on GPU
+def test_error_paths_on_device():
+    torch = G.torch_mod()
+    wl = synth.Workload("err", 1, 1, 128, 64, 64, BF, NONE)
+    p = G.prob(wl)
+    x = torch.zeros(2 * 128 * 64 + 64, dtype=torch.bfloat16, device="cuda")
+    Q = x[:128 * 64]
+    O = torch.zeros(128 * 64, dtype=torch.bfloat16, device="cuda")
+    K = torch.zeros(128 * 64, dtype=torch.bfloat16, device="cuda")
+    E = torch.zeros(64 * 128, dtype=torch.bfloat16, device="cuda")
+    wsb = L.linformer_workspace_size(p)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    # misaligned output
+    assert L.linformer_forward(p, Q, K, K, E, None, None, x[1:].data_ptr(), ws, wsb,
+                               check=False) == 6
+    # output aliases an input
+    assert L.linformer_forward(p, Q, K, K, E, None, None, Q, ws, wsb, check=False) == 7
+    # workspace too small
+    assert L.linformer_forward(p, Q, K, K, E, None, None, O, ws, wsb - 1,
+                               check=False) == 5
+    # key-value sharing with a distinct F
+    p2 = G.prob(wl.with_(share=KV))
+    assert L.linformer_forward(p2, Q, K, K, E, O, None, O, ws, wsb, check=False) == 4
+    # valid call succeeds
+    assert L.linformer_forward(p, Q, K, K, E, None, None, O, ws, wsb, check=False) == 0
+    torch.cuda.synchronize()
