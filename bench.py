@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=20)
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -144,6 +146,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     L.lib()  # fail loudly if the HIP library is missing
+    if args.copy_mb:
+        src = torch.empty(args.copy_mb * 1 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_mb} MiB x3")
+        return
     wl = synth.WORKLOADS[args.workload]
     log(f"workload {wl}")
     t0 = time.time()

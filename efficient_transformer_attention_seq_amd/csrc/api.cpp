@@ -26,11 +26,11 @@ int env_int(const char* name) {
 }
 
 // Tuning overrides (for measurement sweeps only; one code path): LINFORMER_PROJ_SPLIT forces
-// the number of position splits, LINFORMER_PROJ_UPT the units per projection tile,
+// the number of position splits, LINFORMER_PROJ_CFG names the projection tile configuration,
 // LINFORMER_ATTEND_QTB the queries per attention workgroup.
 bool geometry(const lf_problem* p, lf::ProjGeom* g) {
     return lf::proj_geometry(p->batch, p->heads, p->n, p->k, p->share,
-                             env_int("LINFORMER_PROJ_SPLIT"), env_int("LINFORMER_PROJ_UPT"), g);
+                             env_int("LINFORMER_PROJ_SPLIT"), std::getenv("LINFORMER_PROJ_CFG"), g);
 }
 
 int check_problem(const lf_problem* p) {

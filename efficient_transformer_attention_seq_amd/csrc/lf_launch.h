@@ -19,7 +19,11 @@ struct ProjGeom {
     int B, H, n, k, share;
     int groups;           // number of distinct A matrices in use
     int members;          // units per group
+    int cfg;              // tile configuration id
     int upt;              // units per workgroup tile
+    int slot_tiles;       // workgroup tiles along the k slots
+    int stages;           // LDS ring depth
+    int threads;          // threads per workgroup
     int tiles_per_group;  // ceil(members / upt)
     int S;                // splits of the position axis
     int steps_per_split;  // 64-position steps in one split
@@ -79,10 +83,10 @@ struct DenseBf16Args {
     float c;  // scale * log2(e)
 };
 
-// Projection geometry for a problem (deterministic; `split_override` > 0 forces S, `upt_override`
-// > 0 forces the units per tile).  Returns false if the shape is unsupported.
-bool proj_geometry(int B, int H, int n, int k, int share, int split_override, int upt_override,
-                   ProjGeom* out);
+// Projection geometry for a problem (deterministic; `split_override` > 0 forces S,
+// `cfg_override` names a tile configuration).  Returns false if the shape is unsupported.
+bool proj_geometry(int B, int H, int n, int k, int share, int split_override,
+                   const char* cfg_override, ProjGeom* out);
 
 hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream);
 hipError_t launch_attend_bf16(const AttendBf16Args& a, hipStream_t stream);

@@ -4,30 +4,84 @@
 //
 // As a GEMM per group of units sharing one projection matrix A (k x n):
 //   M = k projected slots, N = 64 columns per unit, reduction over the n positions.
-// Workgroup (512 threads, 8 waves) = all k slots x `upt` units x one split of the positions.
-// Wave w computes slot block w % (k/32) (32 slots) for `upw` units.
-//   * A rows (positions contiguous) are the MFMA A operand and go straight from global memory
-//     to registers: each wave owns its 32 rows, nothing is shared.
-//   * K/V rows arrive with the head dimension contiguous but the B operand needs the positions
-//     contiguous, so each 64-position step of K/V is transposed on its way into LDS: a thread
-//     loads two consecutive positions (16 B each), interleaves them into (t, t+1) pairs and
-//     writes 8 dwords.  LDS tile per unit: [64 columns][64 positions], 128 B rows, 16-B chunks
-//     XOR-swizzled by (c ^ c>>3) & 7 so both the pair writes and the 16-B MFMA reads spread over
-//     all banks.  Double-buffered: the next step's global loads are in flight during the MFMAs.
+// Workgroup (512 threads, 8 waves) = all k slots x `UPT` units x one split of the positions.
+// Wave w computes a (32 WM) slot x 64 column tile of one unit.
+//
+// Data movement (HBM-bound, so this is what matters):
+//   * Each 64-position step of the A rows and of the units' K/V rows is copied global -> LDS
+//     by buffer loads that write LDS directly (no register staging), 1 KB per wave instruction,
+//     every instruction covering whole 128-byte rows.  A ring of NS stages keeps NS-1 steps in
+//     flight while the matrix cores work on the oldest one.
+//   * K/V loads use a buffer descriptor whose size is the sequence's valid length, so positions
+//     past the length read as zero in hardware: padding costs no branch and no bytes.
+//   * LDS layouts: A tile [k rows][64 positions], 16-byte chunks XOR-swizzled by
+//     (r ^ r>>3) & 7 so the A-operand reads of consecutive rows hit distinct banks.  K/V tile
+//     [64 positions][64 columns], 32-byte blocks XOR-swizzled by (t & 3); the B operand (positions
+//     contiguous per lane) is read with the transposing ds_read_b64_tr_b16 (each 16-lane group
+//     gets a 4 x 16 block transposed), so no explicit transpose is done anywhere.
+//   The swizzles are realised by choosing which global 16-byte chunk each lane fetches.
 // Splits (S > 1) write fp32 partial sums; a fixup kernel adds them in split order (so results are
 // bitwise reproducible) and casts.  With S == 1 the cast happens here.
 // Output cast: Kbar -> (hi = bf16(x), lo = bf16(x - hi)); Vbar -> bf16(x), round to nearest even.
+#include <cstring>
+
 #include "lf_device.h"
 #include "lf_launch.h"
 
 namespace lf {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kStep = 64;                 // positions per pipeline step
-constexpr int kUnitTileBytes = 64 * kStep * 2;
+constexpr int kStep = 64;               // positions per pipeline stage
+constexpr int kUnitTile = 64 * kStep * 2;  // bytes of one unit's K/V stage tile
+constexpr int kLdsBudget = 150 * 1024;
 
-__device__ __forceinline__ int swz(int c) { return (c ^ (c >> 3)) & 7; }
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int swz_e(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Raw buffer descriptor: base, size in bytes (loads at or past it return zero).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from `rsrc` at byte offset `voff` into LDS at lds_base + 16 * lane.
+// Issued as inline asm so the compiler does not add a conservative vmcnt(0) before every LDS
+// read of the ring; completion is tracked explicitly with wait_vmcnt().
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+    i32x4 rs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rs)
+                 : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void vmcnt_le() {
+    // s_waitcnt: vmcnt N, expcnt and lgkmcnt left at "no wait"
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+#define LF_W(i) case i: vmcnt_le<i>(); break;
+        LF_W(0) LF_W(1) LF_W(2) LF_W(3) LF_W(4) LF_W(5) LF_W(6) LF_W(7) LF_W(8) LF_W(9)
+        LF_W(10) LF_W(11) LF_W(12) LF_W(13) LF_W(14) LF_W(15) LF_W(16) LF_W(17) LF_W(18)
+        LF_W(19) LF_W(20) LF_W(21) LF_W(22) LF_W(23) LF_W(24) LF_W(25) LF_W(26) LF_W(27)
+        LF_W(28) LF_W(29) LF_W(30) LF_W(31)
+#undef LF_W
+        default: vmcnt_le<0>(); break;
+    }
+}
 
 struct Unit {
     int which, b, h;
@@ -63,169 +117,203 @@ __device__ __forceinline__ const uint16_t* group_matrix(const ProjBf16Args& a, i
     return a.E;
 }
 
-template <int UPT, int UPW>
-__global__ __launch_bounds__(kThreads) void proj_bf16_kernel(ProjBf16Args a) {
-    constexpr int WN = UPT / UPW;                  // wave groups along units
-    constexpr int LPT = (UPT * 256 + kThreads - 1) / kThreads;  // pair-chunks per thread
+// Workgroup geometry: NW = SG * UG waves; wave (sg, ug) computes 32*WM slots x WN units (64 columns
+// each); the workgroup tile is KS = 32*WM*SG slots x UPT = WN*UG units.
+template <int WM_, int WN_, int SG_, int UG_>
+struct ProjCfg {
+    static constexpr int WM = WM_, WN = WN_, SG = SG_, UG = UG_;
+    static constexpr int NW = SG * UG;
+    static constexpr int KS = 32 * WM * SG;
+    static constexpr int UPT = WN * UG;
+    static constexpr int XPW = 8 / NW;   // K/V row-block instructions per unit per wave
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
+    constexpr int WM = C::WM, WN = C::WN, SG = C::SG, NW = C::NW, KS = C::KS, UPT = C::UPT;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const ProjGeom& g = a.g;
     const int lid = xcd_remap(blockIdx.x, g.nlogical);
     if (lid < 0) return;
-    const int tile = lid % g.tiles_per_group;
-    const int rest = lid / g.tiles_per_group;
+    // logical order (fastest first): unit tile, slot tile, split, group -- consecutive blocks
+    // share the same A chunk, then the same K/V chunk.
+    const int utile = lid % g.tiles_per_group;
+    int rest = lid / g.tiles_per_group;
+    const int stile = rest % g.slot_tiles;
+    rest /= g.slot_tiles;
     const int s = rest % g.S;
     const int grp = rest / g.S;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-    const int SB = g.k >> 5;
-    const bool computes = wave < SB * WN;
-    const int sb = wave % SB, wn = wave / SB;
-    const int j0 = tile * UPT;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+    const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int sg = wave % SG, ug = wave / SG;
+    const int j0 = utile * UPT;
+    const int r0 = stile * KS;
 
+    // valid positions of the tile: steps past every unit's length are all zero and skipped
+    int maxlen = 0;
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+        const int j = j0 + u;
+        if (j < g.members) maxlen = max(maxlen, clamp_len(a.lengths, unit_of(g, grp, j).b, g.n));
+    }
     const int t_begin = s * g.steps_per_split * kStep;
-    const int t_end = min(g.n, t_begin + g.steps_per_split * kStep);
-    const int nsteps = (t_end - t_begin) / kStep;
+    const int t_end = min(min(g.n, t_begin + g.steps_per_split * kStep), maxlen);
+    const int nsteps = t_end > t_begin ? (t_end - t_begin + kStep - 1) / kStep : 0;
 
-    // ---- loader assignment: pair-chunk pc -> (unit ut, positions 2tp, 2tp+1, columns 8cg..)
-    const uint16_t* lsrc[LPT];
-    int llen[LPT], lrow[LPT], lcg[LPT], lut[LPT];
-    bool lon[LPT];
+    constexpr uint32_t stage_bytes = (uint32_t)KS * 128 + UPT * kUnitTile;
+    const int NS = g.stages;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+
+    // ---- this wave's share of one stage's DMA instructions (1 KB each):
+    //   A rows  : I = 0 .. KS/8-1 (rows 8I .. 8I+7 of the slot tile), wave I % NW issues I;
+    //   K/V     : unit u, positions 8q .. 8q+7 for q = 0..7, wave w issues q = xq0 + NW*qi.
+    constexpr int n_e = KS / 8;
+    const int my_e = (wave < n_e) ? (n_e - wave + NW - 1) / NW : 0;
+    const int my_count = my_e + UPT * C::XPW;
+    const int xq0 = (wave - (n_e % NW) + NW) % NW;
+
+    const uint16_t* A = group_matrix(a, grp);
+    const i32x4 rsrc_a = make_rsrc(A, (uint32_t)g.k * g.n * 2);
+    // per-unit K/V descriptors, bounded by the valid length (indexed only by unrolled loops, so
+    // they stay in scalar registers)
+    i32x4 rsrc_x[UPT];
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-        const int pc = tid + i * kThreads;
-        const int ut = pc >> 8, rem = pc & 255;
-        lut[i] = ut;
-        lrow[i] = (rem >> 3) * 2;
-        lcg[i] = rem & 7;
-        lon[i] = (pc < UPT * 256) && (j0 + ut < g.members);
-        lsrc[i] = nullptr;
-        llen[i] = 0;
-        if (lon[i]) {
-            const Unit u = unit_of(g, grp, j0 + ut);
-            const uint16_t* X = u.which ? a.V : a.K;
-            lsrc[i] = X + ((size_t)(u.b * g.H + u.h) * g.n) * kHeadDim + lcg[i] * 8;
-            llen[i] = clamp_len(a.lengths, u.b, g.n);
+    for (int u = 0; u < UPT; ++u) {
+        const int j = j0 + u;
+        if (j < g.members) {
+            const Unit un = unit_of(g, grp, j);
+            const uint16_t* X =
+                (un.which ? a.V : a.K) + (size_t)(un.b * g.H + un.h) * g.n * kHeadDim;
+            const int L = clamp_len(a.lengths, un.b, g.n);
+            rsrc_x[u] = make_rsrc(X, (uint32_t)L * kHeadDim * 2);
+        } else {
+            rsrc_x[u] = make_rsrc(a.K, 0u);
         }
     }
+    const int lrow = lane >> 3, lpc = lane & 7;
 
-    const uint16_t* arow = group_matrix(a, grp) + (size_t)(sb * 32 + l32) * g.n + hh * 8;
-
-    f32x16 acc[UPW][2];
-#pragma unroll
-    for (int u = 0; u < UPW; ++u)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) acc[u][nt][j] = 0.0f;
-
-    u32x4 xr[LPT][2];
-    bf16x8 ea[4], ean[4];
-
-    auto load_x = [&](int t0) {
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            xr[i][0] = z;
-            xr[i][1] = z;
-            if (lon[i]) {
-                const int t = t0 + lrow[i];
-                if (t < llen[i]) xr[i][0] = *(const u32x4*)(lsrc[i] + (size_t)t * kHeadDim);
-                if (t + 1 < llen[i])
-                    xr[i][1] = *(const u32x4*)(lsrc[i] + (size_t)(t + 1) * kHeadDim);
-            }
+    auto issue = [&](int step, int slot) {
+        const int t0 = t_begin + step * kStep;
+        const uint32_t sb = lds0 + (uint32_t)slot * stage_bytes;
+        for (int I = wave; I < n_e; I += NW) {
+            const int r = I * 8 + lrow;                 // row within the slot tile
+            const int lc = lpc ^ swz_e(r);
+            dma16(rsrc_a, sb + I * 1024,
+                  (uint32_t)((size_t)(r0 + r) * g.n + t0 + lc * 8) * 2);
         }
-    };
-    auto load_a = [&](int t0, bf16x8* dst) {
-        if (computes) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) dst[ks] = *(const bf16x8*)(arow + t0 + ks * 16);
-        }
-    };
-    auto store_x = [&](int buf) {
-        uint8_t* base = smem + buf * (UPT * kUnitTileBytes);
+        for (int qi = 0; qi < C::XPW; ++qi) {
+            const int q = xq0 + NW * qi;
+            const int tl = q * 8 + lrow;
+            const int lc = 2 * ((lpc >> 1) ^ (tl & 3)) + (lpc & 1);
+            const uint32_t xoff = (uint32_t)((t0 + tl) * kHeadDim + lc * 8) * 2;
 #pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            if (i * kThreads + tid >= UPT * 256) continue;
-            const int t = lrow[i];
-            const int q = t >> 3;
-            uint8_t* ub = base + lut[i] * kUnitTileBytes + (t & 7) * 2;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t w0 = xr[i][0][e >> 1], w1 = xr[i][1][e >> 1];
-                const uint32_t v = (e & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u))
-                                           : ((w0 & 0xFFFFu) | (w1 << 16));
-                const int c = lcg[i] * 8 + e;
-                *(uint32_t*)(ub + c * 128 + ((q ^ swz(c)) << 4)) = v;
-            }
+            for (int u = 0; u < UPT; ++u)
+                dma16(rsrc_x[u], sb + (uint32_t)KS * 128 + u * kUnitTile + q * 1024, xoff);
         }
     };
 
-    if (nsteps > 0) {
-        load_x(t_begin);
-        load_a(t_begin, ea);
-        store_x(0);
+    f32x16 acc[WM][WN][2];
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+        for (int wn = 0; wn < WN; ++wn)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) acc[mt][wn][nt][j] = 0.0f;
+
+    // ---- per-lane LDS offsets for the operand reads
+    int a_off[WM];
+    int a_sw[WM];
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt) {
+        const int r = sg * 32 * WM + mt * 32 + l32;
+        a_off[mt] = r * 128;
+        a_sw[mt] = swz_e(r);
     }
-    __syncthreads();
+    const int grp16 = lane >> 4, s16 = lane & 15;
+    const int tq = 8 * (grp16 >> 1) + (s16 >> 2);          // + 16 ks + 4 rd
+    const int cb = grp16 & 1;
+    const int cin = (s16 & 3) * 8;                          // byte offset inside a 32-B block
 
-    for (int step = 0; step < nsteps; ++step) {
-        const bool more = step + 1 < nsteps;
-        if (more) {
-            load_x(t_begin + (step + 1) * kStep);
-            load_a(t_begin + (step + 1) * kStep, ean);
-        }
-        if (computes) {
-            const uint8_t* base = smem + (step & 1) * (UPT * kUnitTileBytes);
+    const int npro = min(NS - 1, nsteps);
+    for (int i = 0; i < npro; ++i) issue(i, i);
+
+    int cslot = 0;           // ring slot of step i
+    int islot = NS - 1;      // ring slot of step i + NS - 1
+    for (int i = 0; i < nsteps; ++i) {
+        const int later = min(NS - 2, nsteps - 1 - i);
+        wait_vmcnt(later * my_count);
+        __syncthreads();
+        if (i + NS - 1 < nsteps) issue(i + NS - 1, islot);
+        islot = (islot + 1 == NS) ? 0 : islot + 1;
+        const int cur = cslot;
+        cslot = (cslot + 1 == NS) ? 0 : cslot + 1;
+        const uint8_t* st = smem + (size_t)cur * stage_bytes;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int q = ks * 2 + hh;
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 av[WM];
 #pragma unroll
-                for (int u = 0; u < UPW; ++u) {
-                    const uint8_t* ub = base + (wn * UPW + u) * kUnitTileBytes;
+            for (int mt = 0; mt < WM; ++mt)
+                av[mt] = *(const bf16x8*)(st + a_off[mt] + (((2 * ks + hh) ^ a_sw[mt]) << 4));
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const int c = nt * 32 + l32;
-                        const bf16x8 bop = *(const bf16x8*)(ub + c * 128 + ((q ^ swz(c)) << 4));
-                        acc[u][nt] = mfma32(ea[ks], bop, acc[u][nt]);
+            for (int wn = 0; wn < WN; ++wn) {
+                const uint8_t* xt = st + KS * 128 + (ug * WN + wn) * kUnitTile;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int cblk = nt * 2 + cb;
+                    s16x4 v[2];
+#pragma unroll
+                    for (int rd = 0; rd < 2; ++rd) {
+                        const int t = ks * 16 + tq + 4 * rd;
+                        const uint8_t* p = xt + t * 128 + ((cblk ^ (t & 3)) << 5) + cin;
+                        v[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4*)(uintptr_t)(
+                                (__attribute__((address_space(3))) const uint8_t*)p));
                     }
+                    const bf16x8 bop = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                    for (int mt = 0; mt < WM; ++mt)
+                        acc[mt][wn][nt] = mfma32(av[mt], bop, acc[mt][wn][nt]);
                 }
             }
         }
-        if (more) {
-            store_x((step + 1) & 1);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) ea[ks] = ean[ks];
-        }
-        __syncthreads();
     }
 
-    if (!computes) return;
     const size_t bhk = (size_t)g.B * g.H * g.k;
 #pragma unroll
-    for (int u = 0; u < UPW; ++u) {
-        const int j = j0 + wn * UPW + u;
+    for (int wn = 0; wn < WN; ++wn) {
+        const int j = j0 + ug * WN + wn;
         if (j >= g.members) continue;
         const Unit un = unit_of(g, grp, j);
         const size_t ubase = ((size_t)(un.b * g.H + un.h) * g.k) * kHeadDim;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int c = nt * 32 + l32;
+        for (int mt = 0; mt < WM; ++mt) {
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int r = sb * 32 + 8 * (jj >> 2) + 4 * hh + (jj & 3);
-                const float x = acc[u][nt][jj];
-                const size_t idx = ubase + (size_t)r * kHeadDim + c;
-                if (g.S == 1) {
-                    if (un.which == 0) {
-                        const uint16_t hi = f32_to_bf16(x);
-                        a.Khi[idx] = hi;
-                        a.Klo[idx] = f32_to_bf16(x - bf16_to_f32(hi));
+            for (int nt = 0; nt < 2; ++nt) {
+                const int c = nt * 32 + l32;
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) {
+                    const int r = r0 + sg * 32 * WM + mt * 32 + 8 * (jj >> 2) + 4 * hh + (jj & 3);
+                    const float x = acc[mt][wn][nt][jj];
+                    const size_t idx = ubase + (size_t)r * kHeadDim + c;
+                    if (g.S == 1) {
+                        if (un.which == 0) {
+                            const uint16_t hi = f32_to_bf16(x);
+                            a.Khi[idx] = hi;
+                            a.Klo[idx] = f32_to_bf16(x - bf16_to_f32(hi));
+                        } else {
+                            a.Vb[idx] = f32_to_bf16(x);
+                        }
                     } else {
-                        a.Vb[idx] = f32_to_bf16(x);
+                        a.part[((size_t)s * 2 + un.which) * bhk * kHeadDim + idx] = x;
                     }
-                } else {
-                    a.part[((size_t)s * 2 + un.which) * bhk * kHeadDim + idx] = x;
                 }
             }
         }
@@ -254,10 +342,31 @@ __global__ __launch_bounds__(256) void proj_fixup_bf16_kernel(const float* part,
     }
 }
 
+// Tile configurations (compile-time geometry).  The names are what LINFORMER_PROJ_CFG selects.
+using Cfg256x128 = ProjCfg<2, 1, 4, 2>;   // 8 waves, 64x64 wave tiles
+using Cfg256x256 = ProjCfg<2, 2, 4, 2>;   // 8 waves, 64x128 wave tiles
+using Cfg128x256w4 = ProjCfg<2, 2, 2, 2>; // 4 waves, 64x128 wave tiles
+using Cfg128x256 = ProjCfg<2, 1, 2, 4>;   // 8 waves, 64x64 wave tiles
+using Cfg64x512 = ProjCfg<2, 1, 1, 8>;    // 8 waves, 64x64 wave tiles
+using Cfg32x512 = ProjCfg<1, 1, 1, 8>;    // 8 waves, 32x64 wave tiles (any k % 32 == 0)
+
+struct CfgInfo {
+    const char* name;
+    int id, ks, upt, nw;
+};
+constexpr CfgInfo kCfgs[] = {
+    {"256x128", 0, Cfg256x128::KS, Cfg256x128::UPT, Cfg256x128::NW},
+    {"256x256", 1, Cfg256x256::KS, Cfg256x256::UPT, Cfg256x256::NW},
+    {"128x256w4", 2, Cfg128x256w4::KS, Cfg128x256w4::UPT, Cfg128x256w4::NW},
+    {"128x256", 3, Cfg128x256::KS, Cfg128x256::UPT, Cfg128x256::NW},
+    {"64x512", 4, Cfg64x512::KS, Cfg64x512::UPT, Cfg64x512::NW},
+    {"32x512", 5, Cfg32x512::KS, Cfg32x512::UPT, Cfg32x512::NW},
+};
+
 }  // namespace
 
-bool proj_geometry(int B, int H, int n, int k, int share, int split_override, int upt_override,
-                   ProjGeom* out) {
+bool proj_geometry(int B, int H, int n, int k, int share, int split_override,
+                   const char* cfg_override, ProjGeom* out) {
     if (B < 1 || H < 1 || n < kStep || n % kStep || k < 32 || k > 256 || k % 32) return false;
     ProjGeom g{};
     g.B = B;
@@ -275,44 +384,76 @@ bool proj_geometry(int B, int H, int n, int k, int share, int split_override, in
         g.groups = 1;
         g.members = 2 * B * H;
     }
-    // units per tile: 2 when all 8 waves already cover the slots (k = 256 or k > 128),
-    // 4 for k <= 128 so that 8 waves stay busy.
-    int upt = (k > 128) ? 2 : 4;
-    if (upt_override == 1 || upt_override == 2 || (upt_override == 4 && k <= 128)) upt = upt_override;
-    g.upt = upt;
-    g.tiles_per_group = (g.members + upt - 1) / upt;
+    int cfg = -1;
+    if (cfg_override && cfg_override[0]) {
+        for (const CfgInfo& c : kCfgs)
+            if (std::strcmp(c.name, cfg_override) == 0 && k % c.ks == 0) cfg = c.id;
+    }
+    if (cfg < 0) {
+        if (k % 128 == 0) cfg = 3;
+        else if (k % 64 == 0) cfg = 4;
+        else cfg = 5;
+    }
+    const CfgInfo& ci = kCfgs[cfg];
+    g.cfg = cfg;
+    g.upt = ci.upt;
+    g.slot_tiles = k / ci.ks;
+    g.tiles_per_group = (g.members + ci.upt - 1) / ci.upt;
+    const int stage = ci.ks * 128 + ci.upt * kUnitTile;
+    int ns = kLdsBudget / stage;
+    if (ns > 5) ns = 5;
+    if (ns < 2) ns = 2;
+    g.stages = ns;
+    g.threads = ci.nw * 64;
     const int steps = n / kStep;
-    const int tiles = g.groups * g.tiles_per_group;
+    const int tiles = g.groups * g.slot_tiles * g.tiles_per_group;
     int S;
     if (split_override > 0) {
         S = split_override;
     } else {
-        // aim for about two workgroups per compute unit (256 CUs) without splitting below
-        // four steps (256 positions) per split.
-        const int target = 512;
-        S = (target + tiles - 1) / tiles;
+        // workgroups resident per compute unit (LDS-limited), 256 compute units: split the
+        // positions so that all tiles x splits fit in one wave of workgroups, keeping at least
+        // 4 steps (256 positions) per split.
+        const int per_cu = (160 * 1024) / (ns * stage);
+        const int slots = 256 * (per_cu > 0 ? per_cu : 1);
+        S = slots / tiles;
         if (S > steps / 4) S = steps / 4;
         if (S < 1) S = 1;
     }
     if (S > steps) S = steps;
     g.steps_per_split = (steps + S - 1) / S;
     g.S = (steps + g.steps_per_split - 1) / g.steps_per_split;
-    g.nlogical = g.groups * g.S * g.tiles_per_group;
+    g.nlogical = g.groups * g.S * g.slot_tiles * g.tiles_per_group;
     *out = g;
     return true;
 }
 
-hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream) {
+namespace {
+template <class C>
+hipError_t launch_cfg(const ProjBf16Args& a, hipStream_t stream) {
     const ProjGeom& g = a.g;
     const int grid = ((g.nlogical + 7) / 8) * 8;
-    const size_t lds = 2 * (size_t)g.upt * kUnitTileBytes;
-    if (g.upt == 1)
-        hipLaunchKernelGGL((proj_bf16_kernel<1, 1>), dim3(grid), dim3(kThreads), lds, stream, a);
-    else if (g.upt == 2)
-        hipLaunchKernelGGL((proj_bf16_kernel<2, 2>), dim3(grid), dim3(kThreads), lds, stream, a);
-    else
-        hipLaunchKernelGGL((proj_bf16_kernel<4, 2>), dim3(grid), dim3(kThreads), lds, stream, a);
-    hipError_t e = hipGetLastError();
+    const size_t lds = (size_t)g.stages * ((size_t)C::KS * 128 + (size_t)C::UPT * kUnitTile);
+    auto kern = proj_bf16_kernel<C>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NW * 64), lds, stream, a);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream) {
+    const ProjGeom& g = a.g;
+    hipError_t e;
+    switch (g.cfg) {
+        case 0: e = launch_cfg<Cfg256x128>(a, stream); break;
+        case 1: e = launch_cfg<Cfg256x256>(a, stream); break;
+        case 2: e = launch_cfg<Cfg128x256w4>(a, stream); break;
+        case 3: e = launch_cfg<Cfg128x256>(a, stream); break;
+        case 4: e = launch_cfg<Cfg64x512>(a, stream); break;
+        default: e = launch_cfg<Cfg32x512>(a, stream); break;
+    }
     if (e != hipSuccess || g.S == 1) return e;
     const size_t half = (size_t)g.B * g.H * g.k * kHeadDim;
     const size_t threads = (2 * half) / 4;
