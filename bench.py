@@ -40,17 +40,21 @@ def source_hash(kernel: str) -> str:
 
 
 def traffic_bytes(kernel: str, workload: str):
-    """HBM bytes per launch from the committed PMC counter summary, if it was taken on the
-    current kernel source (else None)."""
-    path = os.path.join(PROFILES, "traffic.json")
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (copy-calibrated), from
+    profiles/traffic.txt, if they were taken on the current kernel source; else None.
+
+    traffic.txt lines: <kernel> <workload> <source sha256, 16 hex> <fetch bytes> <write bytes>
+    """
+    path = os.path.join(PROFILES, "traffic.txt")
     if not os.path.exists(path):
         return None
+    sha = source_hash(kernel)
     with open(path) as f:
-        data = json.load(f)
-    ent = data.get(f"{kernel}:{workload}")
-    if not ent or ent.get("source_sha256_16") != source_hash(kernel):
-        return None
-    return ent.get("hbm_bytes_per_launch")
+        for line in f:
+            parts = line.split()
+            if len(parts) == 5 and parts[0] == kernel and parts[1] == workload and parts[2] == sha:
+                return int(parts[3]) + int(parts[4])
+    return None
 
 
 def algorithmic(wl, kernel: str):

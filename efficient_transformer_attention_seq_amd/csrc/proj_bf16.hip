@@ -217,15 +217,16 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
         }
     };
 
-    f32x16 acc[WM][WN][2];
+    // acc[wn][ct][mt]: rows = 32 columns (ct) of unit wn, columns = 32 slots (mt)
+    f32x16 acc[WN][2][WM];
 #pragma unroll
-    for (int mt = 0; mt < WM; ++mt)
+    for (int wn = 0; wn < WN; ++wn)
 #pragma unroll
-        for (int wn = 0; wn < WN; ++wn)
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) acc[mt][wn][nt][j] = 0.0f;
+                for (int j = 0; j < 16; ++j) acc[wn][ct][mt][j] = 0.0f;
 
     // ---- per-lane LDS offsets for the operand reads
     int a_off[WM];
@@ -257,16 +258,18 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
         const uint8_t* st = smem + (size_t)cur * stage_bytes;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 av[WM];
+            // B operand: E rows (slots) with 8 consecutive positions per lane
+            bf16x8 ev[WM];
 #pragma unroll
             for (int mt = 0; mt < WM; ++mt)
-                av[mt] = *(const bf16x8*)(st + a_off[mt] + (((2 * ks + hh) ^ a_sw[mt]) << 4));
+                ev[mt] = *(const bf16x8*)(st + a_off[mt] + (((2 * ks + hh) ^ a_sw[mt]) << 4));
 #pragma unroll
             for (int wn = 0; wn < WN; ++wn) {
                 const uint8_t* xt = st + KS * 128 + (ug * WN + wn) * kUnitTile;
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const int cblk = nt * 2 + cb;
+                for (int ct = 0; ct < 2; ++ct) {
+                    // A operand: K/V columns with 8 consecutive positions per lane (transposed read)
+                    const int cblk = ct * 2 + cb;
                     s16x4 v[2];
 #pragma unroll
                     for (int rd = 0; rd < 2; ++rd) {
@@ -276,47 +279,94 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
                             (__attribute__((address_space(3))) s16x4*)(uintptr_t)(
                                 (__attribute__((address_space(3))) const uint8_t*)p));
                     }
-                    const bf16x8 bop = __builtin_bit_cast(
+                    const bf16x8 xop = __builtin_bit_cast(
                         bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                     for (int mt = 0; mt < WM; ++mt)
-                        acc[mt][wn][nt] = mfma32(av[mt], bop, acc[mt][wn][nt]);
+                        acc[wn][ct][mt] = mfma32(xop, ev[mt], acc[wn][ct][mt]);
                 }
             }
         }
     }
 
+    // ---- epilogue: stage each wave's tile through LDS (the ring is free once every wave has
+    // left the loop) so global stores are whole 128-byte rows, 16 bytes per lane.
+    //   lane (l32, hh) holds, for slot (32 mt + l32) of the wave, columns 32 ct + 8 q + 4 hh + (0..3)
+    __syncthreads();
+    constexpr int RW = 32 * WM;                      // slot rows per wave tile
+    const bool split_out = g.S > 1;
+    // per-wave staging region: RW rows x 64 columns, fp32 (row stride 272 B) or two bf16
+    // planes (row stride 136 B each); at most 16 KB + padding per wave
+    constexpr int kRowF = 64 * 4 + 16, kRowH = 64 * 2 + 8;
+    uint8_t* stg = smem + (size_t)wave * (RW * kRowF);
     const size_t bhk = (size_t)g.B * g.H * g.k;
 #pragma unroll
     for (int wn = 0; wn < WN; ++wn) {
         const int j = j0 + ug * WN + wn;
-        if (j >= g.members) continue;
-        const Unit un = unit_of(g, grp, j);
-        const size_t ubase = ((size_t)(un.b * g.H + un.h) * g.k) * kHeadDim;
+        const bool live = j < g.members;
+        const Unit un = live ? unit_of(g, grp, j) : Unit{0, 0, 0};
 #pragma unroll
         for (int mt = 0; mt < WM; ++mt) {
+            const int row = mt * 32 + l32;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int c = nt * 32 + l32;
+            for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
-                for (int jj = 0; jj < 16; ++jj) {
-                    const int r = r0 + sg * 32 * WM + mt * 32 + 8 * (jj >> 2) + 4 * hh + (jj & 3);
-                    const float x = acc[mt][wn][nt][jj];
-                    const size_t idx = ubase + (size_t)r * kHeadDim + c;
-                    if (g.S == 1) {
-                        if (un.which == 0) {
-                            const uint16_t hi = f32_to_bf16(x);
-                            a.Khi[idx] = hi;
-                            a.Klo[idx] = f32_to_bf16(x - bf16_to_f32(hi));
-                        } else {
-                            a.Vb[idx] = f32_to_bf16(x);
-                        }
+                for (int q = 0; q < 4; ++q) {
+                    const int col = ct * 32 + q * 8 + 4 * hh;
+                    const float x0 = acc[wn][ct][mt][4 * q], x1 = acc[wn][ct][mt][4 * q + 1];
+                    const float x2 = acc[wn][ct][mt][4 * q + 2], x3 = acc[wn][ct][mt][4 * q + 3];
+                    if (split_out) {
+                        const f32x4 v = {x0, x1, x2, x3};
+                        *(f32x4*)(stg + row * kRowF + col * 4) = v;
                     } else {
-                        a.part[((size_t)s * 2 + un.which) * bhk * kHeadDim + idx] = x;
+                        const u32x2 hi = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+                        *(u32x2*)(stg + row * kRowH + col * 2) = hi;
+                        if (un.which == 0) {
+                            const float h0 = __uint_as_float(hi[0] << 16);
+                            const float h1 = __uint_as_float(hi[0] & 0xFFFF0000u);
+                            const float h2 = __uint_as_float(hi[1] << 16);
+                            const float h3 = __uint_as_float(hi[1] & 0xFFFF0000u);
+                            const u32x2 lo = {pack_bf16x2(x0 - h0, x1 - h1),
+                                              pack_bf16x2(x2 - h2, x3 - h3)};
+                            *(u32x2*)(stg + RW * kRowH + row * kRowH + col * 2) = lo;
+                        }
                     }
                 }
             }
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
+        __builtin_amdgcn_wave_barrier();
+        if (live) {
+            const int rbase = r0 + sg * RW;     // first slot row of this wave tile
+            const size_t ubase = ((size_t)(un.b * g.H + un.h) * g.k + rbase) * kHeadDim;
+            if (split_out) {
+                float* dst = a.part + ((size_t)s * 2 + un.which) * bhk * kHeadDim + ubase;
+                // RW rows x 256 B: 16 lanes per row
+#pragma unroll
+                for (int it = 0; it < RW / 4; ++it) {
+                    const int row = it * 4 + (lane >> 4), ch = lane & 15;
+                    *(f32x4*)(dst + row * kHeadDim + ch * 4) = *(const f32x4*)(stg + row * kRowF + ch * 16);
+                }
+            } else {
+                uint16_t* dst_hi = (un.which == 0 ? a.Khi : a.Vb) + ubase;
+#pragma unroll
+                for (int it = 0; it < RW / 8; ++it) {
+                    const int row = it * 8 + (lane >> 3), ch = lane & 7;
+                    *(u32x4*)(dst_hi + row * kHeadDim + ch * 8) = *(const u32x4*)(stg + row * kRowH + ch * 16);
+                }
+                if (un.which == 0) {
+                    uint16_t* dst_lo = a.Klo + ubase;
+#pragma unroll
+                    for (int it = 0; it < RW / 8; ++it) {
+                        const int row = it * 8 + (lane >> 3), ch = lane & 7;
+                        *(u32x4*)(dst_lo + row * kHeadDim + ch * 8) =
+                            *(const u32x4*)(stg + RW * kRowH + row * kRowH + ch * 16);
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -433,7 +483,9 @@ template <class C>
 hipError_t launch_cfg(const ProjBf16Args& a, hipStream_t stream) {
     const ProjGeom& g = a.g;
     const int grid = ((g.nlogical + 7) / 8) * 8;
-    const size_t lds = (size_t)g.stages * ((size_t)C::KS * 128 + (size_t)C::UPT * kUnitTile);
+    const size_t ring = (size_t)g.stages * ((size_t)C::KS * 128 + (size_t)C::UPT * kUnitTile);
+    const size_t staging = (size_t)C::NW * (32 * C::WM) * (64 * 4 + 16);   // epilogue staging
+    const size_t lds = ring > staging ? ring : staging;
     auto kern = proj_bf16_kernel<C>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
