@@ -27,7 +27,7 @@ int env_int(const char* name) {
 
 // Tuning overrides (for measurement sweeps only; one code path): LINFORMER_PROJ_SPLIT forces
 // the number of position splits, LINFORMER_PROJ_CFG names the projection tile configuration,
-// LINFORMER_ATTEND_QTB the queries per attention workgroup.
+// LINFORMER_ATTEND_GRID the number of attention workgroups.
 bool geometry(const lf_problem* p, lf::ProjGeom* g) {
     return lf::proj_geometry(p->batch, p->heads, p->n, p->k, p->share,
                              env_int("LINFORMER_PROJ_SPLIT"), std::getenv("LINFORMER_PROJ_CFG"), g);
@@ -128,6 +128,23 @@ int check_device() {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? LF_OK : LF_ERR_LAUNCH; }
 
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device (cached; 256 on MI355X).
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c <= 0) {
+        hipDeviceProp_t prop;
+        c = (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+                ? prop.multiProcessorCount
+                : 256;
+        g_cu_count[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
 // Validation shared by project_kv and forward (everything about K, V, E, F, lengths, ws).
 int check_project_args(const lf_problem* p, const void* K, const void* V, const void* E,
                        const void* F, const int32_t* lengths, const lf::ProjGeom& g, void* ws,
@@ -209,11 +226,16 @@ int do_attend(const lf_problem* p, const void* Q, const void* Kbar, const void* 
     a.H = p->heads;
     a.n = p->n;
     a.k = p->k;
-    int qtb = env_int("LINFORMER_ATTEND_QTB");
-    if (qtb <= 0 || qtb % 32) qtb = 512;
-    a.qtb = qtb;
-    a.QB = (p->n + qtb - 1) / qtb;
-    a.nlogical = p->batch * p->heads * a.QB;
+    // persistent grid: one workgroup per compute unit (LINFORMER_ATTEND_GRID overrides, for tests),
+    // never more than the number of 32-query tiles, a multiple of 8 (one share per XCD)
+    int grid = env_int("LINFORMER_ATTEND_GRID");
+    if (grid <= 0) grid = cu_count();
+    const long long max_tiles = (long long)p->batch * p->heads * (p->n / 32);
+    if ((long long)grid > max_tiles) grid = (int)max_tiles;
+    grid = (grid + 7) / 8 * 8;
+    a.qtb = 32;
+    a.QB = 0;
+    a.nlogical = grid;
     a.c = eff_scale(p) * lf::kLog2e;
     return launch_status(lf::launch_attend_bf16(a, stream));
 }

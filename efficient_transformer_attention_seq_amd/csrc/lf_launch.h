@@ -51,9 +51,9 @@ struct AttendBf16Args {
     const int32_t* lengths;
     uint16_t* O;
     int B, H, n, k;
-    int qtb;       // queries per workgroup (multiple of 32)
-    int QB;        // ceil(n / qtb)
-    int nlogical;  // B * H * QB
+    int qtb;       // queries per tile (32)
+    int QB;        // unused
+    int nlogical;  // persistent grid size (multiple of 8)
     float c;       // scale * log2(e)
 };
 

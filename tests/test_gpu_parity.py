@@ -130,19 +130,25 @@ def test_attend_parity(case, dtype):
     assert err <= G.TOL[dtype]
 
 
-@pytest.mark.parametrize("qtb", [32, 256, 1024])
-def test_attend_workgroup_sizes(qtb):
-    B, H, n, k = 1, 2, 1024, 256
+@pytest.mark.parametrize("grid", [8, 16, 64, 256])
+def test_attend_persistent_grid_sizes(grid):
+    """Work ranges of the persistent attention kernel that start and end inside a head, span
+    several heads, or hold no tiles at all, all give the same result."""
+    B, H, n, k = 3, 2, 1024, 256
+    lens = [700, 1024, 33]
     pr = synth.random_projected(B, H, n, 64, k, BF, seed=3)
     wl = synth.Workload("attend", B, H, n, 64, k, BF, NONE)
-    G.log(f"attend qtb={qtb}")
-    with G.env(LINFORMER_ATTEND_QTB=qtb):
-        out = G.run_attend(pr, wl, [700])
+    G.log(f"attend grid={grid}")
+    with G.env(LINFORMER_ATTEND_GRID=grid):
+        out = G.run_attend(pr, wl, lens)
     ref = np.zeros_like(out)
-    for h in range(H):
-        ref[0, h] = orc.attend(pr.Q[0, h], pr.Khi[0, h].astype(np.float64) + pr.Klo[0, h],
-                               pr.Vbar[0, h], None, 700)
+    for b in range(B):
+        for h in range(H):
+            ref[b, h] = orc.attend(pr.Q[b, h], pr.Khi[b, h].astype(np.float64) + pr.Klo[b, h],
+                                   pr.Vbar[b, h], None, lens[b])
     assert orc.slice_rel_err(out, ref) <= 2e-2
+    for b, Lb in enumerate(lens):
+        assert np.all(out[b, :, Lb:] == 0.0)
 
 
 def test_attend_explicit_scale():
