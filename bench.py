@@ -57,25 +57,32 @@ def traffic_bytes(kernel: str, workload: str):
     return None
 
 
-def algorithmic(wl, kernel: str):
-    """(bytes, flops) the method needs per launch, counted from the definition.
+def algorithmic(wl, kernel: str, lengths=None):
+    """(bytes, flops) the method needs per launch, counted from its definition (bf16 storage).
 
-    project: read K and V once, each unique E/F matrix once; write Kbar (hi and lo planes)
-             and Vbar.  flops 2*n*k*d for each of Kbar and Vbar per (b, h).
-    attend : read Q once and Kbar (hi, lo) and Vbar once per (b, h); write O once.
-             flops 2*n*k*d for the scores and 2*n*k*d for the weighted sum per (b, h).
+    With per-sequence lengths L_b only the valid positions take part: Lsum = sum of L_b over the
+    batch, Lmax = the largest L_b (columns of E, F past it are never needed).
+    project: read K and V at the valid positions and each distinct E/F matrix up to Lmax; write
+             Kbar and Vbar (bf16).  flops 2 L k d for each of Kbar and Vbar per (b, h).
+    attend : read Q at the valid positions, Kbar and Vbar once per (b, h); write all n rows of O
+             (rows past the length are written as zeros).  flops 2 L k d for the scores and
+             2 L k d for the weighted sum per (b, h).
+    The storage format's extra bytes (the fp8 residual plane and scales of Kbar) are not counted.
     """
     B, H, n, d, k = wl.batch, wl.heads, wl.n, wl.d, wl.k
     bh = B * H
     eb = 2  # bf16
-    kv_out = 3 * bh * k * d * eb
+    if lengths is None:
+        lsum, lmax = B * n, n
+    else:
+        lsum, lmax = int(sum(int(x) for x in lengths)), int(max(lengths))
+    kv_out = 2 * bh * k * d * eb
+    flops = 4.0 * H * lsum * k * d
     if kernel == "project":
         n_mats = wl.e_heads * (2 if wl.separate_f else 1)
-        byts = 2 * bh * n * d * eb + n_mats * k * n * eb + kv_out
-        flops = 4.0 * bh * n * k * d
+        byts = 2 * H * lsum * d * eb + n_mats * k * lmax * eb + kv_out
     else:
-        byts = 2 * bh * n * d * eb + kv_out
-        flops = 4.0 * bh * n * k * d
+        byts = H * lsum * d * eb + bh * n * d * eb + kv_out
     return byts, flops
 
 
@@ -234,7 +241,7 @@ def main():
     kern = {}
     for kind in ("project", "attend"):
         us = time_half(kind, args.kernel_iters)
-        byts, flops = algorithmic(wl, kind)
+        byts, flops = algorithmic(wl, kind, inp.lengths)
         kern[kind] = dict(us=us, bytes=byts, flops=flops, gbs=byts / (us * 1e-6) / 1e9,
                           tflops=flops / (us * 1e-6) / 1e12)
         log(f"{kind}: {us:.1f} us/launch, {kern[kind]['gbs']:.0f} GB/s algorithmic, "

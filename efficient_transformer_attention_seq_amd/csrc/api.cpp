@@ -37,7 +37,8 @@ int check_problem(const lf_problem* p) {
     if (!p) return LF_ERR_NULL;
     if (p->dtype != LF_F32 && p->dtype != LF_BF16) return LF_ERR_DTYPE;
     if (p->share < LF_SHARE_NONE || p->share > LF_SHARE_LAYERWISE) return LF_ERR_SHARE;
-    if (p->batch < 1 || p->heads < 1 || p->d != 64) return LF_ERR_SHAPE;
+    if (p->batch < 1 || p->batch > lf::kMaxAttendBatch || p->heads < 1 || p->d != 64)
+        return LF_ERR_SHAPE;
     if (p->n < 64 || p->n % 64) return LF_ERR_SHAPE;
     if (p->k < 32 || p->k > 256 || p->k % 32) return LF_ERR_SHAPE;
     if (!(p->scale >= 0.0f) || !std::isfinite(p->scale)) return LF_ERR_SHAPE;
@@ -59,8 +60,10 @@ size_t ef_bytes(const lf_problem* p) {
     return he * p->k * p->n * elem_size(p->dtype);
 }
 size_t kbar_bytes(const lf_problem* p) {
+    // bf16: hi plane (2 B per element), fp8 lo plane (1 B), two scale bytes per row
     const size_t e = (size_t)p->batch * p->heads * p->k * p->d;
-    return p->dtype == LF_BF16 ? 2 * e * 2 : e * 4;
+    const size_t rows = (size_t)p->batch * p->heads * p->k;
+    return p->dtype == LF_BF16 ? 3 * e + 2 * rows : e * 4;
 }
 size_t vbar_bytes(const lf_problem* p) {
     return (size_t)p->batch * p->heads * p->k * p->d * elem_size(p->dtype);
@@ -190,9 +193,11 @@ int do_project(const lf_problem* p, const void* K, const void* V, const void* E,
     a.lengths = lengths;
     const size_t e = (size_t)p->batch * p->heads * p->k * p->d;
     a.Khi = (uint16_t*)Kbar;
-    a.Klo = (uint16_t*)Kbar + e;
+    a.Klo = (uint8_t*)Kbar + 2 * e;
+    a.Ksc = (uint8_t*)Kbar + 3 * e;
     a.Vb = (uint16_t*)Vbar;
     a.part = (float*)part;
+    a.c = eff_scale(p) * lf::kLog2e;
     a.g = g;
     return launch_status(lf::launch_proj_bf16(a, stream));
 }
@@ -218,7 +223,8 @@ int do_attend(const lf_problem* p, const void* Q, const void* Kbar, const void* 
     const size_t e = (size_t)p->batch * p->heads * p->k * p->d;
     a.Q = (const uint16_t*)Q;
     a.Khi = (const uint16_t*)Kbar;
-    a.Klo = (const uint16_t*)Kbar + e;
+    a.Klo = (const uint8_t*)Kbar + 2 * e;
+    a.Ksc = (const uint8_t*)Kbar + 3 * e;
     a.Vb = (const uint16_t*)Vbar;
     a.lengths = lengths;
     a.O = (uint16_t*)O;
@@ -233,10 +239,7 @@ int do_attend(const lf_problem* p, const void* Q, const void* Kbar, const void* 
     const long long max_tiles = (long long)p->batch * p->heads * (p->n / 32);
     if ((long long)grid > max_tiles) grid = (int)max_tiles;
     grid = (grid + 7) / 8 * 8;
-    a.qtb = 32;
-    a.QB = 0;
     a.nlogical = grid;
-    a.c = eff_scale(p) * lf::kLog2e;
     return launch_status(lf::launch_attend_bf16(a, stream));
 }
 

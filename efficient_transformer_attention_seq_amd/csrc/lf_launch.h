@@ -30,6 +30,19 @@ struct ProjGeom {
     int nlogical;         // groups * S * tiles_per_group
 };
 
+// bf16 Kbar storage (the attention kernel's operand format).  With c = scale * log2(e) and
+// x = c * Kbar[r][d] (fp32):
+//   Khi [B, H, k, 64] bf16 : hi = bf16(x), round to nearest even
+//   Klo [B, H, k, 64] byte : e4m3(lo * 2^s) with lo = x - hi, one power-of-two scale 2^s per row
+//                            and per half d < 32 / d >= 32 ("block"), chosen so that the block's
+//                            largest |lo| * 2^s lies in [128, 256); within a row, byte
+//                            32 h + p holds d = 16 (p / 8) + 8 h + p % 8 (the order in which a
+//                            lane of the 32x32x64 fp8 MFMA holds the 64 products)
+//   Ksc [B, H, k, 2]  byte : 127 - s for blocks 0 and 1 (an E8M0 exponent: the MFMA scales the
+//                            block's products by 2^-s)
+// so x = hi + lo8 * 2^-s to about 2^-13 relative.
+constexpr int kLoBlockHi = 128, kLoBlockTop = 256;
+
 struct ProjBf16Args {
     const uint16_t* K;
     const uint16_t* V;
@@ -37,24 +50,24 @@ struct ProjBf16Args {
     const uint16_t* F;      // never null here (= E when shared or when unshared F is omitted)
     const int32_t* lengths;
     uint16_t* Khi;          // [B, H, k, 64]
-    uint16_t* Klo;          // [B, H, k, 64]
+    uint8_t* Klo;           // [B, H, k, 64]
+    uint8_t* Ksc;           // [B, H, k, 2]
     uint16_t* Vb;           // [B, H, k, 64]
     float* part;            // [S, 2, B*H, k, 64] when S > 1
+    float c;                // scale * log2(e), applied to Kbar before it is stored
     ProjGeom g;
 };
 
 struct AttendBf16Args {
     const uint16_t* Q;
     const uint16_t* Khi;
-    const uint16_t* Klo;
+    const uint8_t* Klo;
+    const uint8_t* Ksc;
     const uint16_t* Vb;
     const int32_t* lengths;
     uint16_t* O;
     int B, H, n, k;
-    int qtb;       // queries per tile (32)
-    int QB;        // unused
     int nlogical;  // persistent grid size (multiple of 8)
-    float c;       // scale * log2(e)
 };
 
 struct F32Args {
@@ -96,6 +109,7 @@ hipError_t launch_dense_bf16(const DenseBf16Args& a, hipStream_t stream);
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kAttendThreads = 512;
+constexpr int kMaxAttendBatch = 4096;   // batch items the bf16 attention kernel tables in LDS
 constexpr int kDenseQTB = 256;  // queries per dense-attention workgroup
 
 }  // namespace lf

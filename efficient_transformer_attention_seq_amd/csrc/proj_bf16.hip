@@ -22,7 +22,8 @@
 //   The swizzles are realised by choosing which global 16-byte chunk each lane fetches.
 // Splits (S > 1) write fp32 partial sums; a fixup kernel adds them in split order (so results are
 // bitwise reproducible) and casts.  With S == 1 the cast happens here.
-// Output cast: Kbar -> (hi = bf16(x), lo = bf16(x - hi)); Vbar -> bf16(x), round to nearest even.
+// Output: Kbar scaled by c = scale * log2(e) and stored as a bf16 plane plus an fp8 residual plane
+// with per-block power-of-two scales (format in lf_launch.h); Vbar -> bf16, round to nearest even.
 #include <cstring>
 
 #include "lf_device.h"
@@ -39,6 +40,33 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int swz_e(int r) { return (r ^ (r >> 3)) & 7; }
+
+// ---- Kbar lo-plane encoding (layout in lf_launch.h)
+// Byte of column d within a lo row.
+__device__ __forceinline__ int lo_pos(int d) { return ((d >> 3) & 1) * 32 + (d >> 4) * 8 + (d & 7); }
+// Block shift s for a block whose largest residual magnitude is m: 2^s m in [128, 256), clamped
+// to the exponent range of the E8M0 scale byte 127 - s (m == 0 gives the smallest scale).
+__device__ __forceinline__ int lo_shift(float m) {
+    const int e = (int)((__float_as_uint(m) >> 23) & 0xFF) - 127;   // floor(log2 m), m normal
+    const int s = 7 - e;
+    return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+// Four residuals -> four e4m3 bytes (round to nearest even) of lo * 2^s.
+__device__ __forceinline__ uint32_t lo_bytes(float l0, float l1, float l2, float l3, int s) {
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(l0, s), ldexpf(l1, s), 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(l2, s), ldexpf(l3, s), w, true);
+}
+// bf16 hi of x and the fp32 residual x - hi.
+__device__ __forceinline__ uint32_t hi_pair(float x0, float x1, float& r0, float& r1) {
+    const uint32_t h = pack_bf16x2(x0, x1);
+    r0 = x0 - __uint_as_float(h << 16);
+    r1 = x1 - __uint_as_float(h & 0xFFFF0000u);
+    return h;
+}
+__device__ __forceinline__ float other_half(float x, bool upper) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(upper ? r[0] : r[1]);
+}
 
 // Raw buffer descriptor: base, size in bytes (loads at or past it return zero).
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
@@ -196,14 +224,21 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
     }
     const int lrow = lane >> 3, lpc = lane & 7;
 
-    auto issue = [&](int step, int slot) {
+    // One step's DMA share of this wave, in four parts so that it can be spread over the four
+    // MFMA sub-steps of the step before (the TA queue then drains while the matrix cores work):
+    // part 0 = the A rows, parts 1..3 = the units u with u % 3 == part - 1.  The per-step count
+    // of instructions (my_count) and their order within a step are what the waits rely on.
+    auto issue_part = [&](int step, int slot, int part) {
         const int t0 = t_begin + step * kStep;
         const uint32_t sb = lds0 + (uint32_t)slot * stage_bytes;
-        for (int I = wave; I < n_e; I += NW) {
-            const int r = I * 8 + lrow;                 // row within the slot tile
-            const int lc = lpc ^ swz_e(r);
-            dma16(rsrc_a, sb + I * 1024,
-                  (uint32_t)((size_t)(r0 + r) * g.n + t0 + lc * 8) * 2);
+        if (part == 0) {
+            for (int I = wave; I < n_e; I += NW) {
+                const int r = I * 8 + lrow;                 // row within the slot tile
+                const int lc = lpc ^ swz_e(r);
+                dma16(rsrc_a, sb + I * 1024,
+                      (uint32_t)((size_t)(r0 + r) * g.n + t0 + lc * 8) * 2);
+            }
+            return;
         }
 #pragma unroll
         for (int qi = 0; qi < C::XPW; ++qi) {
@@ -213,8 +248,13 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
             const uint32_t xoff = (uint32_t)((t0 + tl) * kHeadDim + lc * 8) * 2;
 #pragma unroll
             for (int u = 0; u < UPT; ++u)
-                dma16(rsrc_x[u], sb + (uint32_t)KS * 128 + u * kUnitTile + q * 1024, xoff);
+                if (u % 3 == part - 1)
+                    dma16(rsrc_x[u], sb + (uint32_t)KS * 128 + u * kUnitTile + q * 1024, xoff);
         }
+    };
+    auto issue = [&](int step, int slot) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) issue_part(step, slot, part);
     };
 
     // acc[wn][ct][mt]: rows = 32 columns (ct) of unit wn, columns = 32 slots (mt)
@@ -251,13 +291,15 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
         const int later = min(NS - 2, nsteps - 1 - i);
         wait_vmcnt(later * my_count);
         __syncthreads();
-        if (i + NS - 1 < nsteps) issue(i + NS - 1, islot);
+        const bool refill = i + NS - 1 < nsteps;   // the slot read at step i - 1 is free now
+        const int fill_slot = islot;
         islot = (islot + 1 == NS) ? 0 : islot + 1;
         const int cur = cslot;
         cslot = (cslot + 1 == NS) ? 0 : cslot + 1;
         const uint8_t* st = smem + (size_t)cur * stage_bytes;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+            if (refill) issue_part(i + NS - 1, fill_slot, ks);
             // B operand: E rows (slots) with 8 consecutive positions per lane
             bf16x8 ev[WM];
 #pragma unroll
@@ -290,55 +332,78 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
     }
 
     // ---- epilogue: stage each wave's tile through LDS (the ring is free once every wave has
-    // left the loop) so global stores are whole 128-byte rows, 16 bytes per lane.
+    // left the loop) so global stores are whole rows, 16 bytes per lane.
     //   lane (l32, hh) holds, for slot (32 mt + l32) of the wave, columns 32 ct + 8 q + 4 hh + (0..3)
     __syncthreads();
     constexpr int RW = 32 * WM;                      // slot rows per wave tile
     const bool split_out = g.S > 1;
-    // per-wave staging region: RW rows x 64 columns, fp32 (row stride 272 B) or two bf16
-    // planes (row stride 136 B each); at most 16 KB + padding per wave
-    constexpr int kRowF = 64 * 4 + 16, kRowH = 64 * 2 + 8;
+    // per-wave staging region: RW rows x 64 columns, fp32 (row stride 272 B), or the bf16 plane
+    // (row stride 136 B) followed by the fp8 lo plane (row stride 80 B); at most 17 KB per wave
+    constexpr int kRowF = 64 * 4 + 16, kRowH = 64 * 2 + 8, kRowL = 80;
     uint8_t* stg = smem + (size_t)wave * (RW * kRowF);
+    uint8_t* stg_lo = stg + RW * kRowH;
     const size_t bhk = (size_t)g.B * g.H * g.k;
+    const float c = a.c;
 #pragma unroll
     for (int wn = 0; wn < WN; ++wn) {
         const int j = j0 + ug * WN + wn;
         const bool live = j < g.members;
         const Unit un = live ? unit_of(g, grp, j) : Unit{0, 0, 0};
+        const int rbase = r0 + sg * RW;     // first slot row of this wave tile
+        const size_t urow = (size_t)(un.b * g.H + un.h) * g.k + rbase;   // global Kbar row
 #pragma unroll
         for (int mt = 0; mt < WM; ++mt) {
             const int row = mt * 32 + l32;
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
+                if (split_out) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = ct * 32 + q * 8 + 4 * hh;
-                    const float x0 = acc[wn][ct][mt][4 * q], x1 = acc[wn][ct][mt][4 * q + 1];
-                    const float x2 = acc[wn][ct][mt][4 * q + 2], x3 = acc[wn][ct][mt][4 * q + 3];
-                    if (split_out) {
-                        const f32x4 v = {x0, x1, x2, x3};
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = ct * 32 + q * 8 + 4 * hh;
+                        const f32x4 v = {acc[wn][ct][mt][4 * q], acc[wn][ct][mt][4 * q + 1],
+                                         acc[wn][ct][mt][4 * q + 2], acc[wn][ct][mt][4 * q + 3]};
                         *(f32x4*)(stg + row * kRowF + col * 4) = v;
-                    } else {
-                        const u32x2 hi = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-                        *(u32x2*)(stg + row * kRowH + col * 2) = hi;
-                        if (un.which == 0) {
-                            const float h0 = __uint_as_float(hi[0] << 16);
-                            const float h1 = __uint_as_float(hi[0] & 0xFFFF0000u);
-                            const float h2 = __uint_as_float(hi[1] << 16);
-                            const float h3 = __uint_as_float(hi[1] & 0xFFFF0000u);
-                            const u32x2 lo = {pack_bf16x2(x0 - h0, x1 - h1),
-                                              pack_bf16x2(x2 - h2, x3 - h3)};
-                            *(u32x2*)(stg + RW * kRowH + row * kRowH + col * 2) = lo;
-                        }
                     }
+                } else if (un.which == 1) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = ct * 32 + q * 8 + 4 * hh;
+                        const f32x16& x = acc[wn][ct][mt];
+                        const u32x2 v = {pack_bf16x2(x[4 * q], x[4 * q + 1]),
+                                         pack_bf16x2(x[4 * q + 2], x[4 * q + 3])};
+                        *(u32x2*)(stg + row * kRowH + col * 2) = v;
+                    }
+                } else {
+                    // Kbar: x = c * Kbar, hi = bf16(x), lo = x - hi; block ct of this row is
+                    // split between this lane and lane l ^ 32
+                    float lo[16];
+                    float m = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = ct * 32 + q * 8 + 4 * hh;
+                        const f32x16& x = acc[wn][ct][mt];
+                        const u32x2 hv = {hi_pair(c * x[4 * q], c * x[4 * q + 1], lo[4 * q], lo[4 * q + 1]),
+                                          hi_pair(c * x[4 * q + 2], c * x[4 * q + 3], lo[4 * q + 2], lo[4 * q + 3])};
+                        *(u32x2*)(stg + row * kRowH + col * 2) = hv;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(lo[4 * q + i]));
+                    }
+                    m = fmaxf(m, other_half(m, hh));
+                    const int sh = lo_shift(m);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = ct * 32 + q * 8 + 4 * hh;
+                        *(uint32_t*)(stg_lo + row * kRowL + lo_pos(col)) =
+                            lo_bytes(lo[4 * q], lo[4 * q + 1], lo[4 * q + 2], lo[4 * q + 3], sh);
+                    }
+                    if (live && hh == 0) a.Ksc[(urow + row) * 2 + ct] = (uint8_t)(127 - sh);
                 }
             }
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
         __builtin_amdgcn_wave_barrier();
         if (live) {
-            const int rbase = r0 + sg * RW;     // first slot row of this wave tile
-            const size_t ubase = ((size_t)(un.b * g.H + un.h) * g.k + rbase) * kHeadDim;
+            const size_t ubase = urow * kHeadDim;
             if (split_out) {
                 float* dst = a.part + ((size_t)s * 2 + un.which) * bhk * kHeadDim + ubase;
                 // RW rows x 256 B: 16 lanes per row
@@ -355,12 +420,11 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
                     *(u32x4*)(dst_hi + row * kHeadDim + ch * 8) = *(const u32x4*)(stg + row * kRowH + ch * 16);
                 }
                 if (un.which == 0) {
-                    uint16_t* dst_lo = a.Klo + ubase;
+                    uint8_t* dst_lo = a.Klo + ubase;   // 64 bytes per row
 #pragma unroll
-                    for (int it = 0; it < RW / 8; ++it) {
-                        const int row = it * 8 + (lane >> 3), ch = lane & 7;
-                        *(u32x4*)(dst_lo + row * kHeadDim + ch * 8) =
-                            *(const u32x4*)(stg + RW * kRowH + row * kRowH + ch * 16);
+                    for (int it = 0; it < RW / 16; ++it) {
+                        const int row = it * 16 + (lane >> 2), ch = lane & 3;
+                        *(u32x4*)(dst_lo + row * 64 + ch * 16) = *(const u32x4*)(stg_lo + row * kRowL + ch * 16);
                     }
                 }
             }
@@ -370,22 +434,30 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
     }
 }
 
-// Adds the S fp32 partial sums of every Kbar/Vbar element in split order and casts.
+// Adds the S fp32 partial sums of every Kbar/Vbar element in split order and stores them in the
+// bf16 formats (Kbar: hi plane, fp8 lo plane and block scales, see lf_launch.h).  Thread = 4
+// consecutive columns of one row; the 8 threads of a 32-column block are consecutive lanes.
 __global__ __launch_bounds__(256) void proj_fixup_bf16_kernel(const float* part, int S,
-                                                              size_t half, uint16_t* Khi,
-                                                              uint16_t* Klo, uint16_t* Vb) {
+                                                              size_t half, float c,
+                                                              uint16_t* Khi, uint8_t* Klo,
+                                                              uint8_t* Ksc, uint16_t* Vb) {
     const size_t e4 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-    if (e4 >= 2 * half) return;
+    if (e4 >= 2 * half) return;   // 2 * half is a multiple of 64: whole blocks leave together
     f32x4 acc = *(const f32x4*)(part + e4);
     for (int s = 1; s < S; ++s) acc += *(const f32x4*)(part + (size_t)s * 2 * half + e4);
     if (e4 < half) {
-        const u32x2 hi = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-        const float h0 = __uint_as_float(hi[0] << 16), h1 = __uint_as_float(hi[0] & 0xFFFF0000u);
-        const float h2 = __uint_as_float(hi[1] << 16), h3 = __uint_as_float(hi[1] & 0xFFFF0000u);
-        const u32x2 lo = {pack_bf16x2(acc[0] - h0, acc[1] - h1),
-                          pack_bf16x2(acc[2] - h2, acc[3] - h3)};
+        float r0, r1, r2, r3;
+        const u32x2 hi = {hi_pair(c * acc[0], c * acc[1], r0, r1), hi_pair(c * acc[2], c * acc[3], r2, r3)};
+        float m = fmaxf(fmaxf(fabsf(r0), fabsf(r1)), fmaxf(fabsf(r2), fabsf(r3)));
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 4));
+        const int sh = lo_shift(m);
+        const size_t row = e4 / 64;
+        const int d0 = (int)(e4 % 64);
         *(u32x2*)(Khi + e4) = hi;
-        *(u32x2*)(Klo + e4) = lo;
+        *(uint32_t*)(Klo + row * 64 + lo_pos(d0)) = lo_bytes(r0, r1, r2, r3, sh);
+        if ((d0 & 31) == 0) Ksc[row * 2 + (d0 >> 5)] = (uint8_t)(127 - sh);
     } else {
         const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
         *(u32x2*)(Vb + (e4 - half)) = v;
@@ -399,6 +471,7 @@ using Cfg128x256w4 = ProjCfg<2, 2, 2, 2>; // 4 waves, 64x128 wave tiles
 using Cfg128x256 = ProjCfg<2, 1, 2, 4>;   // 8 waves, 64x64 wave tiles
 using Cfg64x512 = ProjCfg<2, 1, 1, 8>;    // 8 waves, 64x64 wave tiles
 using Cfg32x512 = ProjCfg<1, 1, 1, 8>;    // 8 waves, 32x64 wave tiles (any k % 32 == 0)
+using Cfg256x256w4b = ProjCfg<4, 2, 2, 2>; // 4 waves, 128x128 wave tiles
 
 struct CfgInfo {
     const char* name;
@@ -411,6 +484,7 @@ constexpr CfgInfo kCfgs[] = {
     {"128x256", 3, Cfg128x256::KS, Cfg128x256::UPT, Cfg128x256::NW},
     {"64x512", 4, Cfg64x512::KS, Cfg64x512::UPT, Cfg64x512::NW},
     {"32x512", 5, Cfg32x512::KS, Cfg32x512::UPT, Cfg32x512::NW},
+    {"256x256w4", 6, Cfg256x256w4b::KS, Cfg256x256w4b::UPT, Cfg256x256w4b::NW},
 };
 
 }  // namespace
@@ -504,6 +578,7 @@ hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream) {
         case 2: e = launch_cfg<Cfg128x256w4>(a, stream); break;
         case 3: e = launch_cfg<Cfg128x256>(a, stream); break;
         case 4: e = launch_cfg<Cfg64x512>(a, stream); break;
+        case 6: e = launch_cfg<Cfg256x256w4b>(a, stream); break;
         default: e = launch_cfg<Cfg32x512>(a, stream); break;
     }
     if (e != hipSuccess || g.S == 1) return e;
@@ -511,7 +586,7 @@ hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream) {
     const size_t threads = (2 * half) / 4;
     const int blocks = (int)((threads + 255) / 256);
     hipLaunchKernelGGL(proj_fixup_bf16_kernel, dim3(blocks), dim3(256), 0, stream, a.part, g.S,
-                       half, a.Khi, a.Klo, a.Vb);
+                       half, a.c, a.Khi, a.Klo, a.Ksc, a.Vb);
     return hipGetLastError();
 }
 

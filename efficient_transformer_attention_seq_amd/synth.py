@@ -178,18 +178,17 @@ def random_inputs(batch: int, heads: int, n: int, d: int, k: int, dtype: int, sh
 class Projected:
     """Seeded stand-ins for projected keys/values, to drive the attention half on its own.
 
-    For bf16, Kbar is carried as two bf16 planes (hi, lo) and the value it stands for is
-    hi + lo; Vbar is one bf16 plane.  For fp32 both are plain fp32 with ``Klo`` all zero.
+    Kbar holds the values the stand-in stands for (float32); putting them into the attention
+    kernel's storage format is the caller's business.  Vbar is rounded to the workload dtype.
     """
     Q: np.ndarray       # [B, H, n, d]
-    Khi: np.ndarray     # [B, H, k, d]
-    Klo: np.ndarray     # [B, H, k, d]
+    Kbar: np.ndarray    # [B, H, k, d]
     Vbar: np.ndarray    # [B, H, k, d]
 
 
 def random_projected(batch: int, heads: int, n: int, d: int, k: int, dtype: int, seed: int,
                      kbar_std: float = 4.0, vbar_std: float = 4.0) -> Projected:
-    """Q ~ N(0,1); Kbar ~ N(0, kbar_std^2) split into hi/lo bf16 planes; Vbar ~ N(0, vbar_std^2).
+    """Q ~ N(0,1); Kbar ~ N(0, kbar_std^2); Vbar ~ N(0, vbar_std^2).
 
     The default standard deviation 4 matches sqrt(n/k) at n = 4096, k = 256 (the spread of
     E . K with E ~ N(0, 1/k) and K ~ N(0, 1)).
@@ -198,8 +197,4 @@ def random_projected(batch: int, heads: int, n: int, d: int, k: int, dtype: int,
     Q = to_dtype(rng.standard_normal((batch, heads, n, d)), dtype)
     kb = rng.standard_normal((batch, heads, k, d)) * kbar_std
     vb = rng.standard_normal((batch, heads, k, d)) * vbar_std
-    if dtype == DT_BF16:
-        hi = round_bf16(round_f32(kb))
-        lo = round_bf16(round_f32(kb - hi.astype(np.float64)))
-        return Projected(Q, hi, lo, round_bf16(round_f32(vb)))
-    return Projected(Q, round_f32(kb), np.zeros((batch, heads, k, d), np.float32), round_f32(vb))
+    return Projected(Q, round_f32(kb), to_dtype(vb, dtype))

@@ -30,12 +30,13 @@
  * Precision:
  *   LF_F32  : fp32 in, fp32 arithmetic, fp32 out.
  *   LF_BF16 : bf16 Q, K, V, E, F, O; all sums accumulate in fp32; the softmax runs in fp32.
- *             Kbar is kept to fp32 accuracy as a pair of bf16 planes (hi = bf16(Kbar),
- *             lo = bf16(Kbar - hi)); Vbar and the softmax weights are rounded once to bf16
- *             (round to nearest even) for the matrix cores.
+ *             Kbar is kept to about 2^-13 relative accuracy as a bf16 plane plus an fp8
+ *             (e4m3) residual plane with power-of-two block scales (layout below); Vbar and
+ *             the softmax weights are rounded once to bf16 (round to nearest even) for the
+ *             matrix cores.
  *
  * Shape limits: d == 64; k % 32 == 0 and 32 <= k <= 256; n % 64 == 0 and n >= 64;
- * batch >= 1, heads >= 1; batch * heads * n * d < 2^31 elements.
+ * 1 <= batch <= 4096, heads >= 1; batch * heads * n * d < 2^31 elements.
  *
  * Ownership and threading: the caller owns every buffer (device memory) and keeps it alive until
  * the stream has finished the call.  The library allocates nothing and keeps no state between
@@ -99,8 +100,18 @@ const char* linformer_status_string(int status);
 int linformer_workspace_size(const lf_problem* p, size_t* bytes);
 
 /* Bytes of the Kbar and Vbar buffers linformer_project_kv() writes and linformer_attend() reads.
- *   LF_F32 : Kbar fp32 [B, H, k, d];            Vbar fp32 [B, H, k, d]
- *   LF_BF16: Kbar bf16 [2, B, H, k, d] (hi, lo); Vbar bf16 [B, H, k, d]           Host only. */
+ *   LF_F32 : Kbar fp32 [B, H, k, d]; Vbar fp32 [B, H, k, d].
+ *   LF_BF16: Vbar bf16 [B, H, k, d].  Kbar holds x = c * Kbar with c = scale * log2(e) (the
+ *            attention kernel works in base-2 logits), as three consecutive planes:
+ *              hi  bf16 [B, H, k, 64]: bf16(x), round to nearest even;
+ *              lo  byte [B, H, k, 64]: fp8 e4m3 of (x - hi) * 2^s, where each row has one s for
+ *                  d < 32 and one for d >= 32 (the row's "blocks"), chosen so that the block's
+ *                  largest |x - hi| * 2^s lies in [128, 256); within a row, byte 32 h + p holds
+ *                  d = 16 (p / 8) + 8 h + p % 8 (p = 0..31, h = 0, 1);
+ *              sc  byte [B, H, k, 2] : 127 - s of blocks 0 and 1.
+ *            So x = hi + lo * 2^-s, and linformer_attend() must get the same scale as the
+ *            linformer_project_kv() call that wrote Kbar.  Total 3 B H k d + 2 B H k bytes.
+ *   Host only. */
 int linformer_kv_sizes(const lf_problem* p, size_t* kbar_bytes, size_t* vbar_bytes);
 
 /* Sequence projection, Kbar = E_h . K_{b,h} and Vbar = F_h . V_{b,h} over the valid positions

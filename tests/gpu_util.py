@@ -1,5 +1,8 @@
 """Helpers for the GPU tests: move seeded inputs to the device, call liblinformer through its C
-ABI binding, bring results back as float64.  No arithmetic of the method lives here."""
+ABI binding, bring results back as float64.  No arithmetic of the method lives here; the bf16
+Kbar storage format (documented with linformer_kv_sizes() in include/linformer.h) is encoded and
+decoded here so that tests can feed stand-ins to the attention half and read the projection's
+output."""
 from __future__ import annotations
 
 import contextlib
@@ -12,6 +15,93 @@ from efficient_transformer_attention_seq_amd import linformer as L
 from efficient_transformer_attention_seq_amd import synth
 
 TOL = {synth.DT_F32: 1e-4, synth.DT_BF16: 2e-2}   # max per-slice |out-ref| / max|ref|
+LOG2E = 1.4426950408889634
+
+
+def log2e_scale(wl: synth.Workload, scale: float = 0.0) -> float:
+    """c = scale * log2(e), the factor the bf16 Kbar planes carry (float32, as the library uses)."""
+    s = scale if scale > 0.0 else 1.0 / np.sqrt(np.float32(wl.d))
+    return float(np.float32(np.float32(s) * np.float32(LOG2E)))
+
+
+# ---- bf16 Kbar storage: hi bf16 plane, e4m3 residual plane with per-(row, half) scales
+def _lo_perm() -> np.ndarray:
+    """perm[d] = byte of column d within a residual row (byte 32 h + p holds 16 (p/8) + 8 h + p%8)."""
+    perm = np.zeros(64, np.int64)
+    for h in range(2):
+        for p in range(32):
+            perm[16 * (p // 8) + 8 * h + p % 8] = 32 * h + p
+    return perm
+
+
+LO_PERM = _lo_perm()
+
+
+def e4m3_decode(b: np.ndarray) -> np.ndarray:
+    b = b.astype(np.int64)
+    sgn = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = b & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    return sgn * mag
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Round to nearest even e4m3 (|v| < 448 assumed: the format keeps residuals below 256)."""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -30)))
+    e = np.clip(e, -6, 8)
+    q = np.round(a / 2.0 ** (e - 3))            # numpy rounds half to even
+    # subnormal range (|v| < 2^-6): step 2^-9, code = q directly; normal: code (e + 7) << 3 | q - 8
+    q_sub = np.round(a / 2.0 ** -9)
+    bump = q >= 16                               # rounded up to the next binade
+    e = np.where(bump, e + 1, e)
+    q = np.where(bump, 8, q)
+    code_norm = ((e + 7).astype(np.int64) << 3) | (q.astype(np.int64) - 8)
+    code_sub = q_sub.astype(np.int64)            # 8 means 2^-6, the first normal, also valid
+    use_sub = a < 2.0 ** -6
+    code = np.where(use_sub, code_sub, code_norm)
+    code = np.where(a == 0, 0, code)
+    return (code | np.where(v < 0, 0x80, 0)).astype(np.uint8)
+
+
+def _bf16_round(x32: np.ndarray) -> np.ndarray:
+    u = x32.astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def encode_kbar_bf16(kbar: np.ndarray, c: float) -> np.ndarray:
+    """Kbar [B, H, k, 64] (float) -> the library's bf16 Kbar bytes for factor c."""
+    x = (np.float32(c) * kbar.astype(np.float32)).astype(np.float32)
+    hi = _bf16_round(x)
+    lo = (x - hi).astype(np.float64)
+    rows = x.reshape(-1, 64)
+    lo = lo.reshape(-1, 2, 32)                    # [row, block, 32]
+    m = np.abs(lo).max(axis=2)
+    _, ex = np.frexp(m)                           # m = f 2^ex, f in [0.5, 1): floor(log2 m) = ex - 1
+    s = np.where(m > 0, 7 - (ex - 1), 127)
+    s = np.clip(s, -127, 127)
+    lo8 = e4m3_encode(lo * np.exp2(s)[:, :, None]).reshape(-1, 64)
+    lo_rows = np.zeros_like(lo8)
+    lo_rows[:, LO_PERM] = lo8
+    sc = (127 - s).astype(np.uint8)
+    hi_bytes = (hi.view(np.uint32) >> 16).astype(np.uint16).reshape(-1).view(np.uint8)
+    return np.concatenate([hi_bytes, lo_rows.reshape(-1), sc.reshape(-1)])
+
+
+def decode_kbar_bf16(raw: np.ndarray, shape) -> tuple:
+    """Library bf16 Kbar bytes -> (hi, residual, x = hi + residual) as float64 [B, H, k, 64]."""
+    B, H, k, d = shape
+    e = B * H * k * d
+    hi16 = raw[:2 * e].view(np.uint16).astype(np.uint32) << 16
+    hi = hi16.view(np.float32).astype(np.float64).reshape(-1, 64)
+    lo_rows = raw[2 * e:3 * e].reshape(-1, 64)
+    sc = raw[3 * e:3 * e + 2 * B * H * k].reshape(-1, 2).astype(np.float64)
+    lo = e4m3_decode(lo_rows[:, LO_PERM]).reshape(-1, 2, 32) * np.exp2(sc - 127.0)[:, :, None]
+    lo = lo.reshape(-1, 64)
+    return hi.reshape(shape), lo.reshape(shape), (hi + lo).reshape(shape)
 
 
 def log(msg: str) -> None:
@@ -89,48 +179,40 @@ def run_forward(inp: synth.Inputs, scale: float = 0.0, guard: bool = False):
     return out, ok
 
 
-def run_project(inp: synth.Inputs):
-    """Calls linformer_project_kv; returns (Kbar, Vbar) as float64 [B, H, k, d] (hi + lo)."""
+def _project_raw(inp: synth.Inputs):
     torch = torch_mod()
     wl = inp.wl
     p = prob(wl)
     K, V = dev(inp.K, wl.dtype), dev(inp.V, wl.dtype)
     E = dev(inp.E, wl.dtype)
     F = dev(inp.F, wl.dtype) if inp.F is not None else None
-    lens = lengths_dev(inp.lengths)
-    shp = (wl.batch, wl.heads, wl.k, wl.d)
-    if wl.dtype == synth.DT_BF16:
-        Kbar = empty((2,) + shp, wl.dtype)
-    else:
-        Kbar = empty(shp, wl.dtype)
-    Vbar = empty(shp, wl.dtype)
-    wsb = L.linformer_workspace_size(p)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
-    L.linformer_project_kv(p, K, V, E, F, lens, Kbar, Vbar, ws, wsb)
-    torch.cuda.synchronize()
-    kb = host(Kbar)
-    if wl.dtype == synth.DT_BF16:
-        kb = kb[0] + kb[1]
-    return kb, host(Vbar)
-
-
-def run_project_planes(inp: synth.Inputs):
-    """Like run_project but returns the raw bf16 hi and lo planes separately."""
-    torch = torch_mod()
-    wl = inp.wl
-    p = prob(wl)
-    K, V = dev(inp.K, wl.dtype), dev(inp.V, wl.dtype)
-    E = dev(inp.E, wl.dtype)
-    F = dev(inp.F, wl.dtype) if inp.F is not None else None
-    shp = (wl.batch, wl.heads, wl.k, wl.d)
-    Kbar = empty((2,) + shp, wl.dtype)
-    Vbar = empty(shp, wl.dtype)
+    kbytes, vbytes = L.linformer_kv_sizes(p)
+    Kbar = torch.empty(kbytes, dtype=torch.uint8, device="cuda")
+    Vbar = empty((wl.batch, wl.heads, wl.k, wl.d), wl.dtype)
     wsb = L.linformer_workspace_size(p)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
     L.linformer_project_kv(p, K, V, E, F, lengths_dev(inp.lengths), Kbar, Vbar, ws, wsb)
     torch.cuda.synchronize()
-    kb = host(Kbar)
-    return kb[0], kb[1]
+    return Kbar.cpu().numpy(), host(Vbar)
+
+
+def run_project(inp: synth.Inputs):
+    """Calls linformer_project_kv; returns (Kbar, Vbar) as float64 [B, H, k, d] (for bf16 the
+    decoded planes divided by c, i.e. the Kbar the planes stand for)."""
+    wl = inp.wl
+    raw, vb = _project_raw(inp)
+    shp = (wl.batch, wl.heads, wl.k, wl.d)
+    if wl.dtype == synth.DT_BF16:
+        _, _, x = decode_kbar_bf16(raw, shp)
+        return x / log2e_scale(wl), vb
+    return raw.view(np.float32).astype(np.float64).reshape(shp), vb
+
+
+def run_project_planes(inp: synth.Inputs):
+    """bf16 only: the raw Kbar bytes and their decoding (hi, residual, hi + residual)."""
+    wl = inp.wl
+    raw, _ = _project_raw(inp)
+    return raw, decode_kbar_bf16(raw, (wl.batch, wl.heads, wl.k, wl.d))
 
 
 def run_attend(pr: synth.Projected, wl: synth.Workload, lengths=None, scale: float = 0.0):
@@ -138,9 +220,10 @@ def run_attend(pr: synth.Projected, wl: synth.Workload, lengths=None, scale: flo
     p = prob(wl, scale)
     Q = dev(pr.Q, wl.dtype)
     if wl.dtype == synth.DT_BF16:
-        Kbar = dev(np.stack([pr.Khi, pr.Klo]), wl.dtype)
+        raw = encode_kbar_bf16(pr.Kbar, log2e_scale(wl, scale))
+        Kbar = torch.from_numpy(raw).cuda()
     else:
-        Kbar = dev(pr.Khi, wl.dtype)
+        Kbar = dev(pr.Kbar, wl.dtype)
     Vbar = dev(pr.Vbar, wl.dtype)
     O = empty((wl.batch, wl.heads, wl.n, wl.d), wl.dtype)
     L.linformer_attend(p, Q, Kbar, Vbar, lengths_dev(lengths), O)

@@ -45,7 +45,7 @@ def test_sizes_match_layout():
     B, H, n, k = 8, 12, 4096, 256
     p = L.problem(B, H, n, 64, k, L.LF_BF16, L.LF_SHARE_NONE)
     kb, vb = L.linformer_kv_sizes(p)
-    assert kb == 2 * B * H * k * 64 * 2          # hi and lo bf16 planes
+    assert kb == 3 * B * H * k * 64 + 2 * B * H * k   # bf16 hi, e4m3 residual, block scales
     assert vb == B * H * k * 64 * 2
     ws = L.linformer_workspace_size(p)
     assert ws >= kb + vb
@@ -57,7 +57,8 @@ def test_sizes_match_layout():
 
 @pytest.mark.parametrize("field,value,code", [
     ("d", 32, 2), ("n", 100, 2), ("n", 0, 2), ("k", 48, 2), ("k", 288, 2), ("k", 0, 2),
-    ("batch", 0, 2), ("heads", 0, 2), ("dtype", 5, 3), ("share", 9, 4), ("scale", -1.0, 2),
+    ("batch", 0, 2), ("batch", 4097, 2), ("heads", 0, 2), ("dtype", 5, 3), ("share", 9, 4),
+    ("scale", -1.0, 2),
     ("scale", float("nan"), 2),
 ])
 def test_problem_validation(field, value, code):
