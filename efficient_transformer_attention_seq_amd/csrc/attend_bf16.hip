@@ -173,8 +173,26 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
 
     // ---- lengths -> LDS: clamped length per batch item and the valid-tile prefix over batch items
-    // (one round of loads, then a block-wide scan), so no later step waits on global memory for them
-    {
+    // (one round of loads, then a scan), so no later step waits on global memory for them
+    if (a.B <= 64) {
+        // one wave: lane b holds batch item b, inclusive scan by shuffles
+        if (wave == 0) {
+            const int L = lane < a.B ? clamp_len(a.lengths, lane, a.n) : 0;
+            const int ntb = (L + kTileQ - 1) / kTileQ;
+            int inc = ntb;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int v = __shfl_up(inc, off);
+                if (lane >= off) inc += v;
+            }
+            if (lane < a.B) {
+                s_len[lane] = L;
+                s_cum[lane] = (inc - ntb) * a.H;
+            }
+            if (lane == a.B - 1) s_cum[a.B] = inc * a.H;
+        }
+        __syncthreads();
+    } else {
         const int per = (a.B + kThreads - 1) / kThreads;
         const int b0 = min(a.B, tid * per), b1 = min(a.B, b0 + per);
         int run = 0;

@@ -181,12 +181,17 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
     const int j0 = utile * UPT;
     const int r0 = stile * KS;
 
-    // valid positions of the tile: steps past every unit's length are all zero and skipped
+    // lengths of the tile's units in one round of loads (lane u < UPT fetches unit u's), then
+    // broadcast; steps past every unit's length are all zero and skipped
+    int lane_len = 0;
+    if (lane < UPT && j0 + lane < g.members)
+        lane_len = clamp_len(a.lengths, unit_of(g, grp, j0 + lane).b, g.n);
+    int ulen[UPT];
     int maxlen = 0;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-        const int j = j0 + u;
-        if (j < g.members) maxlen = max(maxlen, clamp_len(a.lengths, unit_of(g, grp, j).b, g.n));
+        ulen[u] = __builtin_amdgcn_readlane(lane_len, u);
+        maxlen = max(maxlen, ulen[u]);
     }
     const int t_begin = s * g.steps_per_split * kStep;
     const int t_end = min(min(g.n, t_begin + g.steps_per_split * kStep), maxlen);
@@ -216,8 +221,7 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
             const Unit un = unit_of(g, grp, j);
             const uint16_t* X =
                 (un.which ? a.V : a.K) + (size_t)(un.b * g.H + un.h) * g.n * kHeadDim;
-            const int L = clamp_len(a.lengths, un.b, g.n);
-            rsrc_x[u] = make_rsrc(X, (uint32_t)L * kHeadDim * 2);
+            rsrc_x[u] = make_rsrc(X, (uint32_t)ulen[u] * kHeadDim * 2);
         } else {
             rsrc_x[u] = make_rsrc(a.K, 0u);
         }
@@ -471,7 +475,6 @@ using Cfg128x256w4 = ProjCfg<2, 2, 2, 2>; // 4 waves, 64x128 wave tiles
 using Cfg128x256 = ProjCfg<2, 1, 2, 4>;   // 8 waves, 64x64 wave tiles
 using Cfg64x512 = ProjCfg<2, 1, 1, 8>;    // 8 waves, 64x64 wave tiles
 using Cfg32x512 = ProjCfg<1, 1, 1, 8>;    // 8 waves, 32x64 wave tiles (any k % 32 == 0)
-using Cfg256x256w4b = ProjCfg<4, 2, 2, 2>; // 4 waves, 128x128 wave tiles
 
 struct CfgInfo {
     const char* name;
@@ -484,7 +487,6 @@ constexpr CfgInfo kCfgs[] = {
     {"128x256", 3, Cfg128x256::KS, Cfg128x256::UPT, Cfg128x256::NW},
     {"64x512", 4, Cfg64x512::KS, Cfg64x512::UPT, Cfg64x512::NW},
     {"32x512", 5, Cfg32x512::KS, Cfg32x512::UPT, Cfg32x512::NW},
-    {"256x256w4", 6, Cfg256x256w4b::KS, Cfg256x256w4b::UPT, Cfg256x256w4b::NW},
 };
 
 }  // namespace
@@ -578,7 +580,6 @@ hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream) {
         case 2: e = launch_cfg<Cfg128x256w4>(a, stream); break;
         case 3: e = launch_cfg<Cfg128x256>(a, stream); break;
         case 4: e = launch_cfg<Cfg64x512>(a, stream); break;
-        case 6: e = launch_cfg<Cfg256x256w4b>(a, stream); break;
         default: e = launch_cfg<Cfg32x512>(a, stream); break;
     }
     if (e != hipSuccess || g.S == 1) return e;

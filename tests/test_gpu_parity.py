@@ -77,8 +77,7 @@ def test_project_parity(case, dtype):
 @pytest.mark.parametrize("k,cfg,split", [
     (256, "256x128", 1), (256, "256x256", 2), (256, "128x256w4", 3), (256, "128x256", 5),
     (256, "64x512", 2), (256, "32x512", 1), (128, "128x256", 8), (128, "128x256w4", 2),
-    (128, "64x512", 3), (96, "32x512", 2), (192, "64x512", 4), (64, "64x512", 1),
-    (256, "256x256w4", 1), (256, "256x256w4", 3)])
+    (128, "64x512", 3), (96, "32x512", 2), (192, "64x512", 4), (64, "64x512", 1)])
 def test_project_tile_configs_and_splits(k, cfg, split):
     """Every tile configuration and split count computes the same thing (fixed-order split
     sums), including tiles whose later steps lie entirely past every length."""
@@ -158,6 +157,26 @@ def test_attend_persistent_grid_sizes(grid):
     G.log(f"attend grid={grid}")
     with G.env(LINFORMER_ATTEND_GRID=grid):
         out = G.run_attend(pr, wl, lens)
+    ref = np.zeros_like(out)
+    for b in range(B):
+        for h in range(H):
+            ref[b, h] = orc.attend(pr.Q[b, h], pr.Kbar[b, h], pr.Vbar[b, h], None, lens[b])
+    assert orc.slice_rel_err(out, ref) <= 2e-2
+    for b, Lb in enumerate(lens):
+        assert np.all(out[b, :, Lb:] == 0.0)
+
+
+def test_attend_many_batch_items():
+    """More than 64 batch items (the length tables are built by the block-wide scan), with empty,
+    one-tile and ragged sequences."""
+    B, H, n, k = 70, 2, 128, 32
+    rng = np.random.default_rng(12)
+    lens = [int(x) for x in rng.integers(0, n + 1, size=B)]
+    lens[0], lens[1], lens[2] = 0, n, 1
+    pr = synth.random_projected(B, H, n, 64, k, BF, seed=13)
+    wl = synth.Workload("attend", B, H, n, 64, k, BF, NONE)
+    G.log(f"attend B={B}")
+    out = G.run_attend(pr, wl, lens)
     ref = np.zeros_like(out)
     for b in range(B):
         for h in range(H):
