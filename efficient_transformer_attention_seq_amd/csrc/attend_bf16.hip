@@ -20,8 +20,9 @@
 // Per wave and tile of 32 queries:
 //   1. S^T (k x 32) = Kbar . Q^T: per 32 slots four v_mfma_f32_32x32x16_bf16 for the hi plane
 //      times Q, then one v_mfma_scale_f32_32x32x64_f8f6f4 for the residual (fp8 lo plane times Q
-//      rounded to e4m3, scaled back by the block scales), so the scores carry Kbar to about
-//      2^-13.  The accumulators start from -mref (see 2), so they hold s - mref directly.
+//      rounded to e4m3, scaled back by the block scales), so the scores carry Kbar to within
+//      2^-12 of each row half's largest value.  The accumulators start from -mref (see 2), so
+//      they hold s - mref directly.
 //   2. Exact softmax per query in one streaming pass over blocks of 64 slots: the scores of a query
 //      sit in lanes l and l + 32, so the block max is an in-register reduction plus one exchange
 //      of the wave halves.  The reference mref starts at 0 and moves to the block max only when
@@ -102,15 +103,17 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t vo
 // Q of this lane (32 values: columns 16 ks + 8 hh + j, j = 0..7, for ks = 0..3) as e4m3 bytes in
 // the same order (byte 8 ks + j), round to nearest even: the B operand of the residual product.
 __device__ __forceinline__ i32x8 q_fp8(const bf16x8 (&qop)[4]) {
+    // v_cvt_scalef32_pk_fp8_bf16 (scale 1) converts a bf16 pair straight into one 16-bit half of
+    // the destination, keeping the other half (op_sel[2] picks the high half).  Inline asm with
+    // the destination tied, so that both halves are written into the same register in order.
     i32x8 r;
+    const float one = 1.0f;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const u32x4 w = __builtin_bit_cast(u32x4, qop[m >> 1]);
-        const uint32_t w0 = w[2 * (m & 1)], w1 = w[2 * (m & 1) + 1];
-        uint32_t v = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(w0 << 16),
-                                                     __uint_as_float(w0 & 0xFFFF0000u), 0, false);
-        v = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(w1 << 16),
-                                            __uint_as_float(w1 & 0xFFFF0000u), (int)v, true);
+        uint32_t v = 0;
+        asm volatile("v_cvt_scalef32_pk_fp8_bf16 %0, %1, %2" : "+v"(v) : "v"(w[2 * (m & 1)]), "v"(one));
+        asm volatile("v_cvt_scalef32_pk_fp8_bf16 %0, %1, %2 op_sel:[0,0,1]" : "+v"(v) : "v"(w[2 * (m & 1) + 1]), "v"(one));
         r[m] = (int)v;
     }
     return r;

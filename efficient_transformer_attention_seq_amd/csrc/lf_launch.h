@@ -40,7 +40,7 @@ struct ProjGeom {
 //                            lane of the 32x32x64 fp8 MFMA holds the 64 products)
 //   Ksc [B, H, k, 2]  byte : 127 - s for blocks 0 and 1 (an E8M0 exponent: the MFMA scales the
 //                            block's products by 2^-s)
-// so x = hi + lo8 * 2^-s to about 2^-13 relative.
+// so x = hi + lo8 * 2^-s to within 2^-12 of the largest |x| of its block.
 constexpr int kLoBlockHi = 128, kLoBlockTop = 256;
 
 struct ProjBf16Args {

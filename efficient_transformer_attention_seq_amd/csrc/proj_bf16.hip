@@ -154,6 +154,13 @@ struct ProjCfg {
     static constexpr int KS = 32 * WM * SG;
     static constexpr int UPT = WN * UG;
     static constexpr int XPW = 8 / NW;   // K/V row-block instructions per unit per wave
+    // ring depth: as many 64-position stages as the LDS budget holds (2..5); the host geometry
+    // uses the same rule
+    static constexpr int STAGE = KS * 128 + UPT * kUnitTile;
+    static constexpr int NS = kLdsBudget / STAGE > 5 ? 5 : (kLdsBudget / STAGE < 2 ? 2 : kLdsBudget / STAGE);
+    // DMA instructions per wave per step, when every wave issues the same number
+    static constexpr bool UNIFORM = (KS / 8) % NW == 0;
+    static constexpr int MYC = (KS / 8) / NW + UPT * XPW;
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
 };
 
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
     const int nsteps = t_end > t_begin ? (t_end - t_begin + kStep - 1) / kStep : 0;
 
     constexpr uint32_t stage_bytes = (uint32_t)KS * 128 + UPT * kUnitTile;
-    const int NS = g.stages;
+    constexpr int NS = C::NS;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
 
     // ---- this wave's share of one stage's DMA instructions (1 KB each):
@@ -292,8 +299,13 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
     int cslot = 0;           // ring slot of step i
     int islot = NS - 1;      // ring slot of step i + NS - 1
     for (int i = 0; i < nsteps; ++i) {
-        const int later = min(NS - 2, nsteps - 1 - i);
-        wait_vmcnt(later * my_count);
+        // stage i has landed once at most `later` younger stages are still in flight
+        if constexpr (C::UNIFORM) {
+            if (i + NS - 2 < nsteps) vmcnt_le<(NS - 2) * C::MYC>();
+            else vmcnt_le<0>();   // the last stages: wait for everything
+        } else {
+            wait_vmcnt(min(NS - 2, nsteps - 1 - i) * my_count);
+        }
         __syncthreads();
         const bool refill = i + NS - 1 < nsteps;   // the slot read at step i - 1 is free now
         const int fill_slot = islot;
@@ -559,7 +571,8 @@ template <class C>
 hipError_t launch_cfg(const ProjBf16Args& a, hipStream_t stream) {
     const ProjGeom& g = a.g;
     const int grid = ((g.nlogical + 7) / 8) * 8;
-    const size_t ring = (size_t)g.stages * ((size_t)C::KS * 128 + (size_t)C::UPT * kUnitTile);
+    if (g.stages != C::NS) return hipErrorInvalidValue;   // host and kernel ring depths agree
+    const size_t ring = (size_t)C::NS * C::STAGE;
     const size_t staging = (size_t)C::NW * (32 * C::WM) * (64 * 4 + 16);   // epilogue staging
     const size_t lds = ring > staging ? ring : staging;
     auto kern = proj_bf16_kernel<C>;

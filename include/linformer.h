@@ -30,8 +30,9 @@
  * Precision:
  *   LF_F32  : fp32 in, fp32 arithmetic, fp32 out.
  *   LF_BF16 : bf16 Q, K, V, E, F, O; all sums accumulate in fp32; the softmax runs in fp32.
- *             Kbar is kept to about 2^-13 relative accuracy as a bf16 plane plus an fp8
- *             (e4m3) residual plane with power-of-two block scales (layout below); Vbar and
+ *             Kbar is kept to within 2^-12 of the largest value of each row half, as a bf16
+ *             plane plus an fp8 (e4m3) residual plane with power-of-two block scales (layout
+ *             below); Vbar and
  *             the softmax weights are rounded once to bf16 (round to nearest even) for the
  *             matrix cores.
  *
