@@ -59,32 +59,27 @@ def traffic_bytes(kernel: str, workload: str):
     return None
 
 
-def algorithmic(wl, kernel: str, lengths=None):
-    """(bytes, flops) the method needs per launch, counted from its definition (bf16 storage).
+def algorithmic(wl, kernel: str):
+    """(bytes, flops) per launch as the method's work is counted in the scope table: over the
+    padded length n (tokens = B n), bf16 storage.
 
-    With per-sequence lengths L_b only the valid positions take part: Lsum = sum of L_b over the
-    batch, Lmax = the largest L_b (columns of E, F past it are never needed).
-    project: read K and V at the valid positions and each distinct E/F matrix up to Lmax; write
-             Kbar and Vbar (bf16).  flops 2 L k d for each of Kbar and Vbar per (b, h).
-    attend : read Q at the valid positions, Kbar and Vbar once per (b, h); write all n rows of O
-             (rows past the length are written as zeros).  flops 2 L k d for the scores and
-             2 L k d for the weighted sum per (b, h).
-    The storage format's extra bytes (the fp8 residual plane and scales of Kbar) are not counted.
+    Per token and head: project reads K and V (2 d 2 B = 256 B) plus its share of each distinct
+    E/F matrix (read once), and does 4 k d flops (Kbar and Vbar); attend reads Q and writes O
+    (256 B) and does 4 k d flops (scores and weighted sum).  Kbar/Vbar (B H k d, bf16) are counted
+    once as the projection's output and once as the attention's input.  The kernels skip the
+    rows past each length, so their real traffic (profiles/traffic.txt) is lower on padded
+    workloads; the storage format's extra Kbar residual bytes are not counted either.
     """
     B, H, n, d, k = wl.batch, wl.heads, wl.n, wl.d, wl.k
     bh = B * H
     eb = 2  # bf16
-    if lengths is None:
-        lsum, lmax = B * n, n
-    else:
-        lsum, lmax = int(sum(int(x) for x in lengths)), int(max(lengths))
-    kv_out = 2 * bh * k * d * eb
-    flops = 4.0 * H * lsum * k * d
+    kv = 2 * bh * k * d * eb
+    flops = 4.0 * bh * n * k * d
     if kernel == "project":
         n_mats = wl.e_heads * (2 if wl.separate_f else 1)
-        byts = 2 * H * lsum * d * eb + n_mats * k * lmax * eb + kv_out
+        byts = 2 * bh * n * d * eb + n_mats * k * n * eb + kv
     else:
-        byts = H * lsum * d * eb + bh * n * d * eb + kv_out
+        byts = 2 * bh * n * d * eb + kv
     return byts, flops
 
 
@@ -143,6 +138,75 @@ def cpu_baseline(inp, min_s: float = 10.0, budget_s: float = 30.0):
             "seconds": dt}
 
 
+def copy_ceiling(torch, mib: int = 512, iters: int = 10) -> float:
+    """Read + write GB/s of a plain device copy of `mib` MiB: the practical HBM ceiling."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) / 1e3 / iters
+    del src, dst
+    return 2 * (mib << 20) / sec / 1e9
+
+
+def run_sweep(L, synth, torch, np):
+    """Forward time against n at B1 H12, k = 128 and 256, layerwise E = F, bf16, no padding, with
+    the O(n^2) comparator up to n = 16384.  Prints one JSON line with the table."""
+    rows = []
+    for k in (128, 256):
+        for n in (512, 1024, 2048, 4096, 8192, 16384, 32768, 65536):
+            inp = synth.random_inputs(1, 12, n, 64, k, synth.DT_BF16, synth.SHARE_LAYERWISE,
+                                      seed=n + k)
+            td = torch.bfloat16
+            dev = lambda x: torch.from_numpy(x).to(td).cuda()
+            Q, K, V, E = dev(inp.Q), dev(inp.K), dev(inp.V), dev(inp.E)
+            p = L.problem(1, 12, n, 64, k, synth.DT_BF16, synth.SHARE_LAYERWISE, 0.0)
+            O = torch.empty(1, 12, n, 64, dtype=td, device="cuda")
+            wsb = L.linformer_workspace_size(p)
+            ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+            def fwd():
+                L.linformer_forward(p, Q, K, V, E, None, None, O, ws, wsb)
+
+            def dense():
+                L.attention_dense_forward(p, Q, K, V, None, O)
+
+            def timed(fn, iters):
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(iters):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    fn()
+                    b.record()
+                    b.synchronize()
+                    ts.append(a.elapsed_time(b) * 1e3)
+                return float(np.median(ts))
+
+            us = timed(fwd, 20)
+            row = {"k": k, "n": n, "linformer_us": round(us, 2),
+                   "tokens_per_s": round(n / (us * 1e-6), 1)}
+            if n <= 16384:
+                dus = timed(dense, 10)
+                row["dense_us"] = round(dus, 2)
+                row["speedup"] = round(dus / us, 2)
+            rows.append(row)
+            log(f"k={k:4d} n={n:6d}: linformer {us:9.1f} us" +
+                (f", dense {row['dense_us']:9.1f} us, {row['speedup']:.2f}x" if "dense_us" in row else ""))
+            del Q, K, V, E, O, ws
+    print(json.dumps({"sweep": rows, "config": {"batch": 1, "heads": 12, "head_dim": 64,
+                                                "share": "layerwise", "dtype": "bf16"}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +217,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=20)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: forward time over n for B1 H12 and "
+                         "k = 128, 256 (layerwise E = F), with the dense comparator up to n = 16384")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device copy of this many MB (counter calibration)")
     args = ap.parse_args()
@@ -180,6 +247,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {args.copy_mb} MiB x3")
+        return
+    if args.sweep:
+        run_sweep(L, synth, torch, np)
         return
     wl = synth.WORKLOADS[args.workload]
     log(f"workload {wl}")
@@ -256,7 +326,7 @@ def main():
     kern = {}
     for kind in ("project", "attend"):
         us = time_half(kind, args.kernel_iters)
-        byts, flops = algorithmic(wl, kind, inp.lengths)
+        byts, flops = algorithmic(wl, kind)
         kern[kind] = dict(us=us, bytes=byts, flops=flops, gbs=byts / (us * 1e-6) / 1e9,
                           tflops=flops / (us * 1e-6) / 1e12)
         log(f"{kind}: {us:.1f} us/launch, {kern[kind]['gbs']:.0f} GB/s algorithmic, "
@@ -275,6 +345,9 @@ def main():
     step_bytes = kern["project"]["bytes"] + kern["attend"]["bytes"]
     step_flops = kern["project"]["flops"] + kern["attend"]["flops"]
     roof_us = max(step_bytes / (PEAK_HBM_GBS * 1e9), step_flops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
+
+    copy_gbs = copy_ceiling(torch)
+    log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
 
     dense = None
     if not args.no_dense and wl.dtype == synth.DT_BF16 and wl.n <= 16384:
@@ -322,6 +395,7 @@ def main():
                           "frac": round(roof_us / (ms * 1e3), 4)},
         "kernels_us": {k: round(v["us"], 2) for k, v in kern.items()},
         "dense_comparator": dense,
+        "copy_ceiling_gbs": round(copy_gbs, 1),
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
         "wall_s": round(wall, 4),

@@ -313,20 +313,20 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
         const int cur = cslot;
         cslot = (cslot + 1 == NS) ? 0 : cslot + 1;
         const uint8_t* st = smem + (size_t)cur * stage_bytes;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (refill) issue_part(i + NS - 1, fill_slot, ks);
-            // B operand: E rows (slots) with 8 consecutive positions per lane
-            bf16x8 ev[WM];
+        // operands of sub-step ks (16 positions): E rows (B operand, 8 consecutive positions per
+        // lane) and K/V columns (A operand, read transposed); two register sets, so the reads
+        // of sub-step ks + 1 are in flight while the MFMAs of sub-step ks run
+        bf16x8 ev[2][WM];
+        bf16x8 xo[2][WN][2];
+        auto load_ops = [&](int ks, bf16x8 (&e)[WM], bf16x8 (&x)[WN][2]) {
 #pragma unroll
             for (int mt = 0; mt < WM; ++mt)
-                ev[mt] = *(const bf16x8*)(st + a_off[mt] + (((2 * ks + hh) ^ a_sw[mt]) << 4));
+                e[mt] = *(const bf16x8*)(st + a_off[mt] + (((2 * ks + hh) ^ a_sw[mt]) << 4));
 #pragma unroll
             for (int wn = 0; wn < WN; ++wn) {
                 const uint8_t* xt = st + KS * 128 + (ug * WN + wn) * kUnitTile;
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
-                    // A operand: K/V columns with 8 consecutive positions per lane (transposed read)
                     const int cblk = ct * 2 + cb;
                     s16x4 v[2];
 #pragma unroll
@@ -337,13 +337,23 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
                             (__attribute__((address_space(3))) s16x4*)(uintptr_t)(
                                 (__attribute__((address_space(3))) const uint8_t*)p));
                     }
-                    const bf16x8 xop = __builtin_bit_cast(
+                    x[wn][ct] = __builtin_bit_cast(
                         bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                    for (int mt = 0; mt < WM; ++mt)
-                        acc[wn][ct][mt] = mfma32(xop, ev[mt], acc[wn][ct][mt]);
                 }
             }
+        };
+        load_ops(0, ev[0], xo[0]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) load_ops(ks + 1, ev[(ks + 1) & 1], xo[(ks + 1) & 1]);
+            if (refill) issue_part(i + NS - 1, fill_slot, ks);
+#pragma unroll
+            for (int wn = 0; wn < WN; ++wn)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int mt = 0; mt < WM; ++mt)
+                        acc[wn][ct][mt] = mfma32(xo[ks & 1][wn][ct], ev[ks & 1][mt], acc[wn][ct][mt]);
         }
     }
 
