@@ -186,6 +186,33 @@ def test_attend_many_batch_items():
         assert np.all(out[b, :, Lb:] == 0.0)
 
 
+@pytest.mark.parametrize("kind", ["all_low", "all_high", "late_jump"])
+def test_attend_extreme_logits(kind):
+    """Logits far outside the reference's starting window: every slot 100+ below it (the first
+    block's weights underflow and the reference must move down), 100+ above it (overflow), and a
+    later block 60 above the first (the partial sums must be rescaled mid-row)."""
+    B, H, n, k = 1, 2, 128, 256
+    rng = np.random.default_rng(21)
+    Q = synth.to_dtype(np.abs(rng.standard_normal((B, H, n, 64))) + 0.5, BF)
+    base = rng.standard_normal((B, H, k, 64))
+    if kind == "all_low":
+        kbar = base - 12.0
+    elif kind == "all_high":
+        kbar = base + 12.0
+    else:
+        kbar = base * 0.5
+        kbar[:, :, 128:192] += 9.0
+    pr = synth.Projected(Q, synth.round_f32(kbar), synth.to_dtype(rng.standard_normal((B, H, k, 64)), BF))
+    wl = synth.Workload("attend", B, H, n, 64, k, BF, NONE)
+    out = G.run_attend(pr, wl, None)
+    ref = np.zeros_like(out)
+    for h in range(H):
+        ref[0, h] = orc.attend(pr.Q[0, h], pr.Kbar[0, h], pr.Vbar[0, h])
+    err = orc.slice_rel_err(out, ref)
+    G.log(f"  extreme logits {kind}: err {err:.3e}")
+    assert np.all(np.isfinite(out)) and err <= 2e-2
+
+
 def test_attend_explicit_scale():
     B, H, n, k = 1, 1, 128, 64
     pr = synth.random_projected(B, H, n, 64, k, BF, seed=4, kbar_std=1.0)
