@@ -460,17 +460,48 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
     }
 }
 
-// Adds the S fp32 partial sums of every Kbar/Vbar element in split order and stores them in the
-// bf16 formats (Kbar: hi plane, fp8 lo plane and block scales, see lf_launch.h).  Thread = 4
-// consecutive columns of one row; the 8 threads of a 32-column block are consecutive lanes.
+// Adds the S fp32 partial sums of every Kbar/Vbar element and stores them in the bf16 formats
+// (Kbar: hi plane, fp8 lo plane and block scales, see lf_launch.h).  NG = 1: a thread adds all S
+// splits of 4 consecutive columns in split order (loads issued 4 ahead).  NG = 4 (many splits): a
+// block covers 64 such chunks and its 4 waves each add a contiguous quarter of the splits in
+// order, then wave 0 adds the quarter sums in order.  Either way the summation order is fixed,
+// so results are bitwise reproducible; the 8 lanes of a 32-column block are consecutive lanes
+// of the finishing wave.
+template <int NG>
 __global__ __launch_bounds__(256) void proj_fixup_bf16_kernel(const float* part, int S,
                                                               size_t half, float c,
                                                               uint16_t* Khi, uint8_t* Klo,
                                                               uint8_t* Ksc, uint16_t* Vb) {
-    const size_t e4 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-    if (e4 >= 2 * half) return;   // 2 * half is a multiple of 64: whole blocks leave together
-    f32x4 acc = *(const f32x4*)(part + e4);
-    for (int s = 1; s < S; ++s) acc += *(const f32x4*)(part + (size_t)s * 2 * half + e4);
+    constexpr int CH = 256 / NG;   // four-column chunks per block
+    __shared__ f32x4 quarter[NG > 1 ? NG : 1][CH];
+    const int ci = threadIdx.x % CH, grp = threadIdx.x / CH;
+    const size_t e4 = ((size_t)blockIdx.x * CH + ci) * 4;
+    const bool live = e4 < 2 * half;   // 2 * half is a multiple of 64: whole blocks leave together
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (live) {
+        const int s0 = S * grp / NG, s1 = S * (grp + 1) / NG;
+        int s = s0;
+        for (; s + 4 <= s1; s += 4) {
+            const f32x4 p0 = *(const f32x4*)(part + (size_t)s * 2 * half + e4);
+            const f32x4 p1 = *(const f32x4*)(part + (size_t)(s + 1) * 2 * half + e4);
+            const f32x4 p2 = *(const f32x4*)(part + (size_t)(s + 2) * 2 * half + e4);
+            const f32x4 p3 = *(const f32x4*)(part + (size_t)(s + 3) * 2 * half + e4);
+            acc += p0;
+            acc += p1;
+            acc += p2;
+            acc += p3;
+        }
+        for (; s < s1; ++s) acc += *(const f32x4*)(part + (size_t)s * 2 * half + e4);
+    }
+    if constexpr (NG > 1) {
+        quarter[grp][ci] = acc;
+        __syncthreads();
+        if (grp != 0) return;
+        acc = quarter[0][ci];
+#pragma unroll
+        for (int q = 1; q < NG; ++q) acc += quarter[q][ci];
+    }
+    if (!live) return;
     if (e4 < half) {
         float r0, r1, r2, r3;
         const u32x2 hi = {hi_pair(c * acc[0], c * acc[1], r0, r1), hi_pair(c * acc[2], c * acc[3], r2, r3)};
@@ -607,10 +638,14 @@ hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream) {
     }
     if (e != hipSuccess || g.S == 1) return e;
     const size_t half = (size_t)g.B * g.H * g.k * kHeadDim;
-    const size_t threads = (2 * half) / 4;
-    const int blocks = (int)((threads + 255) / 256);
-    hipLaunchKernelGGL(proj_fixup_bf16_kernel, dim3(blocks), dim3(256), 0, stream, a.part, g.S,
-                       half, a.c, a.Khi, a.Klo, a.Ksc, a.Vb);
+    const size_t chunks = 2 * half / 4;
+    if (g.S >= 8) {   // many splits: spread each chunk's reduction over 4 waves
+        hipLaunchKernelGGL(proj_fixup_bf16_kernel<4>, dim3((int)((chunks + 63) / 64)), dim3(256), 0,
+                           stream, a.part, g.S, half, a.c, a.Khi, a.Klo, a.Ksc, a.Vb);
+    } else {
+        hipLaunchKernelGGL(proj_fixup_bf16_kernel<1>, dim3((int)((chunks + 255) / 256)), dim3(256), 0,
+                           stream, a.part, g.S, half, a.c, a.Khi, a.Klo, a.Ksc, a.Vb);
+    }
     return hipGetLastError();
 }
 
