@@ -217,3 +217,64 @@ def slice_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
             e = num / den
         worst = max(worst, float(e))
     return worst
+
+
+# ---------------------------------------------------------------------------------------------
+# Encoder attention stack: per layer, the input projection to per-head queries, keys and values,
+# Linformer attention of every head with one layerwise-shared projection, the concatenation of the
+# heads and the output projection; the layer's output is the next layer's input.
+#
+# Linformer 요약 설명, section "Transformer and Self-Attention": with model width d_m, h heads of
+# width d, each head's query, key and value are X W^Q, X W^K, X W^V with W of size d_m x d, and
+# the heads' outputs are concatenated and mapped by an output projection as in ordinary
+# multi-head attention.  Linformer summary card, section 方法适配: layerwise sharing uses a single
+# projection matrix for the whole model (every layer, head, key and value).
+#
+# Weight layout (a reading; the pages fix only the shapes): Wqkv[l] is [3 d_m, d_m] and Wo[l] is
+# [d_m, d_m], applied as y = x . W^T (row f of a weight holds output feature f); rows 0..d_m-1 of
+# Wqkv[l] give the queries, d_m..2 d_m-1 the keys, 2 d_m..3 d_m-1 the values, and feature f of
+# each belongs to head f // d, column f % d.  Concatenation puts head h's column c at feature
+# h d + c.  The stack has no other step (no bias, residual or normalisation): the configuration
+# names only these.
+# ---------------------------------------------------------------------------------------------
+def split_heads(Y: np.ndarray, heads: int) -> np.ndarray:
+    """[B, n, heads * d] -> [B, heads, n, d]: feature f goes to head f // d, column f % d."""
+    Y = _f64(Y)
+    B, n, w = Y.shape
+    return Y.reshape(B, n, heads, w // heads).transpose(0, 2, 1, 3)
+
+
+def concat_heads(O: np.ndarray) -> np.ndarray:
+    """[B, heads, n, d] -> [B, n, heads * d]: head h's column c becomes feature h d + c."""
+    O = _f64(O)
+    B, H, n, d = O.shape
+    return O.transpose(0, 2, 1, 3).reshape(B, n, H * d)
+
+
+def stack_layer(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, E: np.ndarray, heads: int,
+                lengths: Optional[Sequence[int]] = None, scale: Optional[float] = None
+                ) -> np.ndarray:
+    """One layer: X [B, n, d_m] -> concat_h(Linformer attention of head h) . Wo^T."""
+    X = _f64(X)
+    dm = X.shape[2]
+    Y = np.matmul(X, _f64(Wqkv).T)                     # [B, n, 3 d_m]
+    Q = split_heads(Y[:, :, 0:dm], heads)
+    K = split_heads(Y[:, :, dm:2 * dm], heads)
+    V = split_heads(Y[:, :, 2 * dm:3 * dm], heads)
+    O = forward(Q, K, V, E, None, SHARE_LAYERWISE, lengths, scale)
+    return np.matmul(concat_heads(O), _f64(Wo).T)
+
+
+def stack_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, E: np.ndarray, heads: int,
+                  lengths: Optional[Sequence[int]] = None, scale: Optional[float] = None,
+                  return_layers: bool = False):
+    """The whole stack: Wqkv [L, 3 d_m, d_m], Wo [L, d_m, d_m], one E [1, k, n] for every layer.
+
+    Returns the last layer's output [B, n, d_m], or the list of every layer's output.
+    """
+    outs = []
+    Y = _f64(X)
+    for l in range(np.shape(Wqkv)[0]):
+        Y = stack_layer(Y, Wqkv[l], Wo[l], E, heads, lengths, scale)
+        outs.append(Y)
+    return outs if return_layers else Y

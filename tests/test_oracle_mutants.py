@@ -68,3 +68,48 @@ def test_mutant_is_caught(idx, monkeypatch):
                 check(orc.SHARE_HEADWISE)
             else:
                 check()
+
+
+# ---- encoder-stack oracle: planted mistakes in the head split, the concatenation and the layer
+from tests import test_stack_oracle_pins as spins
+
+
+def _split_heads_interleaved(Y, heads):
+    Y = np.asarray(Y, dtype=np.float64)
+    B, n, w = Y.shape
+    return Y.reshape(B, n, w // heads, heads).transpose(0, 3, 1, 2)   # feature f -> head f % H
+
+
+def _concat_heads_transposed(O):
+    O = np.asarray(O, dtype=np.float64)
+    B, H, n, d = O.shape
+    return O.transpose(0, 2, 3, 1).reshape(B, n, H * d)               # column-major over heads
+
+
+_orig_layer = orc.stack_layer
+
+
+def _layer_swaps_k_and_v(X, Wqkv, Wo, E, heads, lengths=None, scale=None):
+    W = np.asarray(Wqkv, dtype=np.float64).copy()
+    dm = W.shape[1]
+    W[dm:2 * dm], W[2 * dm:] = W[2 * dm:].copy(), W[dm:2 * dm].copy()
+    return _orig_layer(X, W, Wo, E, heads, lengths, scale)
+
+
+STACK_MUTANTS = [
+    ("split_heads", _split_heads_interleaved, [spins.test_stack_reduces_to_library_mha,
+                                               spins.test_stack_brute_force_tiny]),
+    ("concat_heads", _concat_heads_transposed, [spins.test_stack_reduces_to_library_mha,
+                                                spins.test_stack_brute_force_tiny]),
+    ("stack_layer", _layer_swaps_k_and_v, [spins.test_stack_reduces_to_library_mha,
+                                           spins.test_stack_brute_force_tiny]),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(STACK_MUTANTS)))
+def test_stack_mutant_is_caught(idx, monkeypatch):
+    name, fn, checks = STACK_MUTANTS[idx]
+    monkeypatch.setattr(orc, name, fn)
+    for check in checks:
+        with pytest.raises((AssertionError, ValueError)):
+            check()
