@@ -207,6 +207,104 @@ def run_sweep(L, synth, torch, np):
                                                 "share": "layerwise", "dtype": "bf16"}}), flush=True)
 
 
+def stack_flops(wl) -> float:
+    """Matrix flops of one pass of the encoder attention stack: per layer the input projection
+    (2 T d_model 3 d_model), Linformer attention (8 n k d per head and batch item: Kbar, Vbar,
+    scores, weighted sum) and the output projection (2 T d_model^2), T = B n tokens."""
+    T, dm = wl.batch * wl.n, wl.d_model
+    per_layer = 2.0 * T * dm * 3 * dm + 2.0 * T * dm * dm + 8.0 * wl.batch * wl.heads * wl.n * wl.k * 64
+    return wl.layers * per_layer
+
+
+def stack_cpu_baseline(si, min_s: float = 10.0):
+    """The float64 oracle of the stack on the host cores: batch items through every layer, one
+    at a time, until at least `min_s` seconds of work."""
+    from oracle import linformer_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    wl = si.wl
+    t0 = time.perf_counter()
+    items = 0
+    while True:
+        b = items % wl.batch
+        orc.stack_forward(si.X[b:b + 1], si.Wqkv, si.Wo, si.E, wl.heads)
+        items += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            break
+    return {"value": items * wl.n / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{items} batch items of {wl.n} tokens (cycling over the {wl.batch}) "
+                      f"through all {wl.layers} layers, float64 numpy, {dt:.2f} s",
+            "seconds": dt}
+
+
+def run_stack_bench(args, L, synth, torch, np):
+    """One step = linformer_stack_forward over the whole batch (every layer)."""
+    wl = synth.STACK_WORKLOADS[args.workload]
+    log(f"workload {wl}")
+    si = synth.make_stack_inputs(wl)
+    s = L.stack(wl.batch, wl.n, wl.d_model, wl.heads, wl.k, wl.layers, False, 0.0)
+    bf = torch.bfloat16
+
+    def dev(x):
+        return torch.from_numpy(x).to(bf).cuda()
+
+    Wq, Wo, E = dev(si.Wqkv), dev(si.Wo), dev(si.E)
+    Xs = [dev(si.X) for _ in range(args.replicas)]
+    Y = torch.empty(wl.batch, wl.n, wl.d_model, dtype=bf, device="cuda")
+    wsb = L.linformer_stack_workspace_size(s)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        L.linformer_stack_forward(s, Xs[i % len(Xs)], Wq, Wo, E, None, Y, ws, wsb, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tokens = wl.batch * wl.n
+    flops = stack_flops(wl)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"stack: {ms * 1e3:.1f} us/step ({tokens / (ms / 1e3):.3e} tokens/s), "
+        f"{tflops:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the host cores ...")
+        cpu = stack_cpu_baseline(si)
+        log(f"oracle: {cpu['value']:.3e} tokens/s ({cpu['sample']})")
+    out = {
+        "metric": "Linformer encoder attention stack tokens/s (12 layers); % of MFMA roofline",
+        "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.n,
+                   "d_model": wl.d_model, "heads": wl.heads, "k": wl.k, "layers": wl.layers,
+                   "share": "layerwise", "replicas": args.replicas},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "whole step (projections, attention)",
+                     "algorithmic_flops": flops},
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+        "wall_s": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +348,9 @@ def main():
         return
     if args.sweep:
         run_sweep(L, synth, torch, np)
+        return
+    if args.workload in synth.STACK_WORKLOADS:
+        run_stack_bench(args, L, synth, torch, np)
         return
     wl = synth.WORKLOADS[args.workload]
     log(f"workload {wl}")

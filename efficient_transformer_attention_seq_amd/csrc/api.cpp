@@ -243,6 +243,69 @@ int do_attend(const lf_problem* p, const void* Q, const void* Kbar, const void* 
     return launch_status(lf::launch_attend_bf16(a, stream));
 }
 
+// ---- encoder attention stack
+int check_stack(const lf_stack* s) {
+    if (!s) return LF_ERR_NULL;
+    if (s->dtype != LF_BF16) return LF_ERR_DTYPE;
+    if (s->layers < 1 || s->heads < 1 || s->d_model != 64 * s->heads) return LF_ERR_SHAPE;
+    if (s->d_model % lf::kLinearTileF) return LF_ERR_SHAPE;
+    if (s->batch < 1 || s->n < 64 || ((long long)s->batch * s->n) % lf::kLinearTileT)
+        return LF_ERR_SHAPE;
+    if (3LL * s->batch * s->n * s->d_model >= (1LL << 30)) return LF_ERR_SHAPE;
+    if (s->keep_layers != 0 && s->keep_layers != 1) return LF_ERR_SHAPE;
+    return LF_OK;
+}
+
+lf_problem layer_problem(const lf_stack* s) {
+    lf_problem p{};
+    p.batch = s->batch;
+    p.heads = s->heads;
+    p.n = s->n;
+    p.d = 64;
+    p.k = s->k;
+    p.dtype = LF_BF16;
+    p.share = LF_SHARE_LAYERWISE;
+    p.scale = s->scale;
+    return p;
+}
+
+struct StackWs {
+    size_t planes, o, ping, layer_ws, total;   // byte offsets / sizes
+    size_t act;                                 // bytes of one [B, n, d_model] activation
+};
+
+// Workspace: the query | key | value planes, the attention output, two activation buffers (only
+// when intermediate layer outputs are not kept in Y), then the single layer's workspace.
+bool stack_ws(const lf_stack* s, const lf_problem& p, const lf::ProjGeom& g, StackWs* w) {
+    w->act = (size_t)s->batch * s->n * s->d_model * 2;
+    w->planes = 0;
+    w->o = round_up(3 * w->act, 256);
+    w->ping = w->o + round_up(w->act, 256);
+    const size_t nping = (s->keep_layers || s->layers == 1) ? 0 : (s->layers == 2 ? 1 : 2);
+    w->layer_ws = w->ping + nping * round_up(w->act, 256);
+    const size_t kb = round_up(kbar_bytes(&p), 256), vb = round_up(vbar_bytes(&p), 256);
+    w->total = w->layer_ws + kb + vb + round_up(part_bytes(&p, g), 256);
+    return true;
+}
+
+int do_linear(const uint16_t* W, const void* X, void* Y, int T, int F, int K, int n, int H,
+              int act_mode, int out_mode, hipStream_t stream) {
+    lf::LinearBf16Args a{};
+    a.W = W;
+    a.X = (const uint16_t*)X;
+    a.Y = (uint16_t*)Y;
+    a.T = T;
+    a.F = F;
+    a.K = K;
+    a.n = n;
+    a.H = H;
+    a.act_mode = act_mode;
+    a.out_mode = out_mode;
+    a.plane = (size_t)T * (F / 3);
+    a.nlogical = (F / lf::kLinearTileF) * (T / lf::kLinearTileT);
+    return launch_status(lf::launch_linear_bf16(a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -383,6 +446,84 @@ int attention_dense_forward(const lf_problem* p, const void* Q, const void* K, c
     a.nlogical = p->batch * p->heads * a.QB;
     a.c = eff_scale(p) * lf::kLog2e;
     return launch_status(lf::launch_dense_bf16(a, (hipStream_t)stream));
+}
+
+int linformer_stack_workspace_size(const lf_stack* s, size_t* bytes) {
+    int st = check_stack(s);
+    if (st) return st;
+    if (!bytes) return LF_ERR_NULL;
+    const lf_problem p = layer_problem(s);
+    st = check_problem(&p);
+    if (st) return st;
+    lf::ProjGeom g;
+    if (!geometry(&p, &g)) return LF_ERR_SHAPE;
+    StackWs w;
+    stack_ws(s, p, g, &w);
+    *bytes = w.total;
+    return LF_OK;
+}
+
+int linformer_stack_forward(const lf_stack* s, const void* X, const void* Wqkv, const void* Wo,
+                            const void* E, const int32_t* lengths, void* Y, void* ws,
+                            size_t ws_bytes, void* stream) {
+    int st = check_stack(s);
+    if (st) return st;
+    const lf_problem p = layer_problem(s);
+    st = check_problem(&p);
+    if (st) return st;
+    lf::ProjGeom g;
+    if (!geometry(&p, &g)) return LF_ERR_SHAPE;
+    StackWs w;
+    stack_ws(s, p, g, &w);
+    if (!X || !Wqkv || !Wo || !E || !Y || !ws) return LF_ERR_NULL;
+    if (ws_bytes < w.total) return LF_ERR_WORKSPACE;
+    if (!aligned16(X) || !aligned16(Wqkv) || !aligned16(Wo) || !aligned16(E) || !aligned16(Y) ||
+        !aligned16(ws))
+        return LF_ERR_ALIGN;
+    if (lengths && ((uintptr_t)lengths & 3u)) return LF_ERR_ALIGN;
+    const size_t L = (size_t)s->layers, dm = (size_t)s->d_model;
+    const size_t ybytes = (s->keep_layers ? L : 1) * w.act;
+    const Range ins[] = {{X, w.act}, {Wqkv, L * 3 * dm * dm * 2}, {Wo, L * dm * dm * 2},
+                         {E, ef_bytes(&p)}, {lengths, lengths ? 4u * s->batch : 0u}};
+    const Range outs[] = {{Y, ybytes}, {ws, w.total}};
+    if (any_overlap(outs, 2, ins, 5)) return LF_ERR_ALIAS;
+    st = check_device();
+    if (st) return st;
+
+    hipStream_t strm = (hipStream_t)stream;
+    uint8_t* base = (uint8_t*)ws;
+    uint8_t* planes = base + w.planes;
+    const size_t plane_bytes = w.act;   // B H n 64 = B n d_model elements
+    void* Qp = planes;
+    void* Kp = planes + plane_bytes;
+    void* Vp = planes + 2 * plane_bytes;
+    void* O = base + w.o;
+    uint8_t* lw = base + w.layer_ws;
+    void* Kbar = lw;
+    void* Vbar = lw + round_up(kbar_bytes(&p), 256);
+    void* part = part_bytes(&p, g) ? (void*)(lw + round_up(kbar_bytes(&p), 256) +
+                                             round_up(vbar_bytes(&p), 256))
+                                   : nullptr;
+    const int T = s->batch * s->n, D = s->d_model;
+    const void* in = X;
+    for (int l = 0; l < s->layers; ++l) {
+        void* out;
+        if (s->keep_layers) out = (uint8_t*)Y + (size_t)l * w.act;
+        else if (l == s->layers - 1) out = Y;
+        else out = base + w.ping + (size_t)(l & 1) * round_up(w.act, 256);
+        const uint16_t* Wl = (const uint16_t*)Wqkv + (size_t)l * 3 * dm * dm;
+        const uint16_t* Wol = (const uint16_t*)Wo + (size_t)l * dm * dm;
+        st = do_linear(Wl, in, planes, T, 3 * D, D, s->n, s->heads, 0, 1, strm);
+        if (st) return st;
+        st = do_project(&p, Kp, Vp, E, E, lengths, Kbar, Vbar, part, g, strm);
+        if (st) return st;
+        st = do_attend(&p, Qp, Kbar, Vbar, lengths, O, strm);
+        if (st) return st;
+        st = do_linear(Wol, O, out, T, D, D, s->n, s->heads, 1, 0, strm);
+        if (st) return st;
+        in = out;
+    }
+    return LF_OK;
 }
 
 }  // extern "C"

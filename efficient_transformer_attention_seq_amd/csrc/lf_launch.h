@@ -84,6 +84,19 @@ struct F32Args {
     float scale;
 };
 
+// Dense projection Y = X . W^T of the encoder attention stack (linear_bf16.hip).
+struct LinearBf16Args {
+    const uint16_t* W;   // [F, K] bf16, row f = output feature f
+    const uint16_t* X;   // activations, per act_mode
+    uint16_t* Y;         // output, per out_mode
+    int T, F, K;         // tokens (multiple of kLinearTileT), features (of kLinearTileF), K % 32 == 0
+    int n, H;            // tokens per batch item and heads (head-planar layouts)
+    int act_mode;        // 0: row-major [T, K]; 1: head-planar [B, H, n, 64] with K = 64 H
+    int out_mode;        // 0: row-major [T, F]; 1: query | key | value planes [3][B, H, n, 64]
+    size_t plane;        // elements of one plane (out_mode 1)
+    int nlogical;        // (F / kLinearTileF) * (T / kLinearTileT)
+};
+
 struct DenseBf16Args {
     const uint16_t* Q;
     const uint16_t* K;
@@ -106,10 +119,12 @@ hipError_t launch_attend_bf16(const AttendBf16Args& a, hipStream_t stream);
 hipError_t launch_proj_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_attend_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_dense_bf16(const DenseBf16Args& a, hipStream_t stream);
+hipError_t launch_linear_bf16(const LinearBf16Args& a, hipStream_t stream);
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kAttendThreads = 512;
 constexpr int kMaxAttendBatch = 4096;   // batch items the bf16 attention kernel tables in LDS
 constexpr int kDenseQTB = 256;  // queries per dense-attention workgroup
+constexpr int kLinearTileF = 192, kLinearTileT = 256;   // dense projection workgroup tile
 
 }  // namespace lf

@@ -23,7 +23,8 @@ LF_SHARE_NONE, LF_SHARE_HEADWISE, LF_SHARE_KV, LF_SHARE_LAYERWISE = 0, 1, 2, 3
 # every symbol include/linformer.h declares
 EXPORTS = ("linformer_status_string", "linformer_workspace_size", "linformer_kv_sizes",
            "linformer_project_kv", "linformer_attend", "linformer_forward",
-           "attention_dense_forward")
+           "attention_dense_forward", "linformer_stack_workspace_size",
+           "linformer_stack_forward")
 
 
 class lf_problem(ctypes.Structure):
@@ -35,6 +36,18 @@ class lf_problem(ctypes.Structure):
 def problem(batch: int, heads: int, n: int, d: int, k: int, dtype: int, share: int,
             scale: float = 0.0) -> lf_problem:
     return lf_problem(batch, heads, n, d, k, dtype, share, scale)
+
+
+class lf_stack(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("k", ctypes.c_int32), ("layers", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("keep_layers", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+def stack(batch: int, n: int, d_model: int, heads: int, k: int, layers: int,
+          keep_layers: bool = False, scale: float = 0.0, dtype: int = LF_BF16) -> lf_stack:
+    return lf_stack(batch, n, d_model, heads, k, layers, dtype, int(bool(keep_layers)), scale)
 
 
 class LinformerError(RuntimeError):
@@ -71,6 +84,11 @@ def lib() -> ctypes.CDLL:
     L.linformer_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attention_dense_forward.restype = ctypes.c_int
     L.attention_dense_forward.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    S = ctypes.POINTER(lf_stack)
+    L.linformer_stack_workspace_size.restype = ctypes.c_int
+    L.linformer_stack_workspace_size.argtypes = [S, ctypes.POINTER(sz)]
+    L.linformer_stack_forward.restype = ctypes.c_int
+    L.linformer_stack_forward.argtypes = [S, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -151,3 +169,19 @@ def attention_dense_forward(p: lf_problem, Q, K, V, lengths, O, stream=None,
     code = lib().attention_dense_forward(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V),
                                          _ptr(lengths), _ptr(O), _stream(stream))
     return _check(code, "attention_dense_forward", check)
+
+
+def linformer_stack_workspace_size(s: lf_stack) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().linformer_stack_workspace_size(ctypes.byref(s), ctypes.byref(out)),
+           "linformer_stack_workspace_size", True)
+    return out.value
+
+
+def linformer_stack_forward(s: lf_stack, X, Wqkv, Wo, E, lengths, Y, ws, ws_bytes=None,
+                            stream=None, check: bool = True) -> int:
+    wsb = ws_bytes if ws_bytes is not None else (
+        0 if ws is None or isinstance(ws, int) else ws.numel() * ws.element_size())
+    code = lib().linformer_stack_forward(ctypes.byref(s), _ptr(X), _ptr(Wqkv), _ptr(Wo), _ptr(E),
+                                         _ptr(lengths), _ptr(Y), _ptr(ws), wsb, _stream(stream))
+    return _check(code, "linformer_stack_forward", check)

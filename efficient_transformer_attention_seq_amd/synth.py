@@ -198,3 +198,60 @@ def random_projected(batch: int, heads: int, n: int, d: int, k: int, dtype: int,
     kb = rng.standard_normal((batch, heads, k, d)) * kbar_std
     vb = rng.standard_normal((batch, heads, k, d)) * vbar_std
     return Projected(Q, round_f32(kb), to_dtype(vb, dtype))
+
+
+# ---------------------------------------------------------------------------------------------
+# Encoder attention stack inputs: the 12-layer RoBERTa-base-shaped stack (d_model 768, 12 heads,
+# n = 1024, k = 256, batch 16, bf16) whose per-layer attention part is the stack-layer workload
+# above.  Draw order: X, then for each layer l = 0 .. L-1 its Wqkv[l] and then its Wo[l], then E.
+# X ~ N(0, 1); weights ~ 0.02 N(0, 1); E ~ N(0, 1/k), one matrix for every layer.
+# ---------------------------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class StackWorkload:
+    name: str
+    batch: int
+    n: int
+    d_model: int
+    heads: int
+    k: int
+    layers: int
+    w_std: float = 0.02
+    padded: bool = False
+    seed: int = 0
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.n
+
+    def with_(self, **kw) -> "StackWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+C5 = StackWorkload("encoder_stack_l12_b16_n1024_d768_k256_layerwise", 16, 1024, 768, 12, 256, 12)
+STACK_WORKLOADS = {C5.name: C5}
+
+
+@dataclasses.dataclass
+class StackInputs:
+    """Host copies (float32 arrays holding bf16 values)."""
+    wl: StackWorkload
+    X: np.ndarray                   # [B, n, d_model]
+    Wqkv: np.ndarray                # [L, 3 d_model, d_model]
+    Wo: np.ndarray                  # [L, d_model, d_model]
+    E: np.ndarray                   # [1, k, n]
+    lengths: Optional[np.ndarray]   # int32 [B] or None
+
+
+def make_stack_inputs(wl: StackWorkload, seed: Optional[int] = None,
+                      lengths: Optional[list] = None) -> StackInputs:
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    dm, L = wl.d_model, wl.layers
+    X = to_dtype(rng.standard_normal((wl.batch, wl.n, dm)), DT_BF16)
+    Wqkv = np.empty((L, 3 * dm, dm), dtype=np.float32)
+    Wo = np.empty((L, dm, dm), dtype=np.float32)
+    for l in range(L):
+        Wqkv[l] = to_dtype(rng.standard_normal((3 * dm, dm)) * wl.w_std, DT_BF16)
+        Wo[l] = to_dtype(rng.standard_normal((dm, dm)) * wl.w_std, DT_BF16)
+    E = to_dtype(rng.standard_normal((1, wl.k, wl.n)) / np.sqrt(wl.k), DT_BF16)
+    lens = None if lengths is None else np.asarray(lengths, dtype=np.int32)
+    return StackInputs(wl, X, Wqkv, Wo, E, lens)

@@ -141,6 +141,47 @@ int linformer_forward(const lf_problem* p, const void* Q, const void* K, const v
 int attention_dense_forward(const lf_problem* p, const void* Q, const void* K, const void* V,
                             const int32_t* lengths, void* O, void* stream);
 
+/* ---- Encoder attention stack.  Each of `layers` layers maps its input X [B, n, d_model] to
+ * every head's queries, keys and values, runs Linformer attention (above) on every head with one
+ * layerwise-shared E, concatenates the heads and applies the output projection; the result is the
+ * next layer's input (Linformer 요약 설명, section "Transformer and Self-Attention": per-head
+ * projections X W^Q, X W^K, X W^V of width d = d_model / heads, heads concatenated and mapped by
+ * an output projection; Linformer summary card, section 方法适配: layerwise sharing, one
+ * projection matrix for the whole model).  No other step (bias, residual, normalisation).
+ *
+ * Layouts (bf16, row-major, contiguous):
+ *   X     [B, n, d_model]
+ *   Wqkv  [layers, 3 d_model, d_model], applied as x . W^T: rows 0 .. d_model-1 give the queries,
+ *         then the keys, then the values; feature f of each is column f % 64 of head f / 64
+ *   Wo    [layers, d_model, d_model], applied as x . W^T to the concatenated heads (head h's
+ *         column c is feature 64 h + c)
+ *   E     [1, k, n], the one projection for every layer, head, key and value
+ *   Y     [B, n, d_model] (keep_layers = 0) or [layers, B, n, d_model] (every layer's output)
+ *   lengths as for the single layer: padded positions contribute nothing and output rows past
+ *   the length are zero in every layer.
+ * Shape limits: d_model = 64 heads, d_model % 192 == 0, (batch * n) % 256 == 0, the single layer's
+ * limits on n, k and batch, and 3 batch n d_model < 2^30.  dtype must be LF_BF16.  Ownership,
+ * threading and errors as above; Y must not overlap any input or the workspace. */
+typedef struct lf_stack {
+    int32_t batch;        /* B                                                       */
+    int32_t n;            /* padded maximum sequence length                          */
+    int32_t d_model;      /* model width = 64 * heads                                */
+    int32_t heads;        /* H                                                       */
+    int32_t k;            /* projected length                                        */
+    int32_t layers;       /* >= 1                                                    */
+    int32_t dtype;        /* LF_BF16                                                 */
+    int32_t keep_layers;  /* 1: Y holds every layer's output                         */
+    float scale;          /* score scale; 0 means 1/sqrt(64)                         */
+} lf_stack;
+
+/* Bytes of device workspace linformer_stack_forward() needs (host only). */
+int linformer_stack_workspace_size(const lf_stack* s, size_t* bytes);
+
+/* The whole stack on `stream`; ws is scratch (its contents on entry do not matter). */
+int linformer_stack_forward(const lf_stack* s, const void* X, const void* Wqkv, const void* Wo,
+                            const void* E, const int32_t* lengths, void* Y, void* ws,
+                            size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

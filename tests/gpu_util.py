@@ -255,3 +255,25 @@ def env(**kw):
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
+
+
+def run_stack(si: synth.StackInputs, keep_layers: bool = True, scale: float = 0.0,
+              guard: bool = False):
+    """Calls linformer_stack_forward; returns Y (float64 numpy: every layer's output when
+    keep_layers, else the last) and, with guard, whether the guard elements survived."""
+    torch = torch_mod()
+    wl = si.wl
+    s = L.stack(wl.batch, wl.n, wl.d_model, wl.heads, wl.k, wl.layers, keep_layers, scale)
+    BF = synth.DT_BF16
+    X, Wq, Wo, E = dev(si.X, BF), dev(si.Wqkv, BF), dev(si.Wo, BF), dev(si.E, BF)
+    lens = lengths_dev(si.lengths)
+    shape = ((wl.layers,) if keep_layers else ()) + (wl.batch, wl.n, wl.d_model)
+    if guard:
+        buf, Y = guarded(shape, BF)
+    else:
+        buf, Y = None, empty(shape, BF)
+    wsb = L.linformer_stack_workspace_size(s)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    L.linformer_stack_forward(s, X, Wq, Wo, E, lens, Y, ws, wsb)
+    torch.cuda.synchronize()
+    return host(Y), (guards_intact(buf) if guard else True)

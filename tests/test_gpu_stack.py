@@ -1,0 +1,109 @@
+"""GPU parity of the encoder attention stack (linformer_stack_forward) against the float64
+oracle: per layer (the oracle's layer applied to the exact bf16 input the GPU layer read) and end
+to end.  Metric: per batch item, max|gpu - ref| / max|ref| over the [n, d_model] output.
+
+Both bars are the bf16 accuracy bar, 2e-2.  Per layer the error comes from that layer's own bf16
+roundings (queries, keys, values, Vbar, weights, attention output, layer output: about 2^-9
+relative each).  End to end it also carries every earlier layer's error through the later
+layers, whose amplification grows with the logit spread (it depends on the weights' scale, not
+on the implementation): the synthetic cases use weights of standard deviation 0.5 / sqrt(d_model),
+the 12-layer workload its own 0.02.
+"""
+import numpy as np
+import pytest
+
+from efficient_transformer_attention_seq_amd import synth
+from oracle import linformer_oracle as orc
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+LAYER_TOL = 2e-2
+
+
+END_TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    torch = G.torch_mod()
+    if torch.cuda.device_count() < 1:
+        pytest.skip("no GPU")
+    yield
+
+
+def _check_layers(si, Y, items=None):
+    """Per-layer parity on the listed batch items (all by default); returns the worst error."""
+    wl = si.wl
+    items = list(range(wl.batch)) if items is None else list(items)
+    lens = None if si.lengths is None else [int(si.lengths[b]) for b in items]
+    worst = 0.0
+    x = si.X[items].astype(np.float64)
+    for l in range(wl.layers):
+        ref = orc.stack_layer(x, si.Wqkv[l], si.Wo[l], si.E, wl.heads, lens)
+        err = orc.slice_rel_err(Y[l][items], ref)
+        G.log(f"  layer {l}: err {err:.3e}")
+        assert err <= LAYER_TOL, (l, err)
+        worst = max(worst, err)
+        x = Y[l][items]
+    return worst
+
+
+def _stack_wl(batch, n, d_model, k, layers, w_std=None, seed=1):
+    heads = d_model // 64
+    ws = (0.5 / np.sqrt(d_model)) if w_std is None else w_std
+    return synth.StackWorkload(f"stack_b{batch}n{n}d{d_model}k{k}l{layers}", batch, n, d_model,
+                               heads, k, layers, w_std=ws, seed=seed)
+
+
+@pytest.mark.parametrize("batch,n,d_model,k,layers", [
+    (2, 256, 384, 64, 2),     # 6 heads, two feature tiles of the output map
+    (1, 512, 768, 128, 1),    # 12 feature tiles (queries | keys | values), 2 token tiles
+    (4, 128, 192, 32, 3),     # token tiles spanning batch items, three layers
+])
+def test_stack_parity(batch, n, d_model, k, layers):
+    wl = _stack_wl(batch, n, d_model, k, layers)
+    G.log(f"stack {wl.name}")
+    si = synth.make_stack_inputs(wl)
+    Y, ok = G.run_stack(si, keep_layers=True, guard=True)
+    assert ok, "stray writes outside Y"
+    assert np.all(np.isfinite(Y))
+    _check_layers(si, Y)
+    ref = orc.stack_forward(si.X, si.Wqkv, si.Wo, si.E, wl.heads)
+    err = orc.slice_rel_err(Y[-1], ref)
+    G.log(f"  end to end: err {err:.3e}")
+    assert err <= END_TOL
+
+
+def test_stack_last_layer_only_matches_kept():
+    wl = _stack_wl(2, 256, 384, 64, 3)
+    si = synth.make_stack_inputs(wl)
+    Yk, _ = G.run_stack(si, keep_layers=True)
+    Y1, ok = G.run_stack(si, keep_layers=False, guard=True)
+    assert ok
+    assert np.array_equal(Y1, Yk[-1])
+
+
+def test_stack_padding():
+    wl = _stack_wl(2, 256, 384, 64, 2, seed=3)
+    si = synth.make_stack_inputs(wl, lengths=[200, 77])
+    Y, ok = G.run_stack(si, keep_layers=True, guard=True)
+    assert ok
+    for l in range(wl.layers):
+        assert np.all(Y[l][0, 200:] == 0.0) and np.all(Y[l][1, 77:] == 0.0)
+    _check_layers(si, Y)
+
+
+def test_stack_full_size_sampled():
+    """The 12-layer d_model 768 stack at batch 16, n 1024, k 256 (the workload the benchmark
+    times), checked per layer and end to end on two batch items."""
+    wl = synth.C5
+    G.log(f"stack {wl.name}")
+    si = synth.make_stack_inputs(wl)
+    Y, _ = G.run_stack(si, keep_layers=True)
+    assert np.all(np.isfinite(Y))
+    items = [0, wl.batch - 1]
+    _check_layers(si, Y, items)
+    ref = orc.stack_forward(si.X[items], si.Wqkv, si.Wo, si.E, wl.heads)
+    err = orc.slice_rel_err(Y[-1][items], ref)
+    G.log(f"  end to end: err {err:.3e}")
+    assert err <= END_TOL
