@@ -9,14 +9,15 @@
 // as the B operand, so both operands are read K-contiguous, 8 bf16 per lane, from LDS and each
 // accumulator lane ends with runs of 4 consecutive features of one token.
 //
-// K streams through LDS in 32-wide stages (one 64-byte row per feature and per token) with
-// direct-to-LDS buffer loads, 1 KB per wave instruction, in a ring of kNS stages so that kNS - 1
-// stages are in flight while the matrix cores work on the oldest.  Within a row the four 16-byte
-// chunks are XOR-swizzled by (r >> 1) & 3, which makes the operand reads of eight consecutive rows
-// hit distinct banks; the swizzle is realised by choosing which global chunk each lane fetches.
+// K streams through LDS in 64-wide stages (one 128-byte row per feature and per token) with
+// direct-to-LDS buffer loads, 1 KB per wave instruction, double-buffered: the loads of stage i + 1
+// are issued, a quarter at a time, between the matrix sub-steps of stage i.  Within a row the
+// eight 16-byte chunks are XOR-swizzled by (r ^ r >> 3) & 7, so the operand reads of consecutive
+// rows hit distinct banks; the swizzle is realised by choosing which global chunk each lane
+// fetches.  The operands of sub-step ks + 1 are read while the MFMAs of sub-step ks run.
 //
 // Activation layouts: row-major [T, K], or head-planar [B, H, n, 64] (the attention output, read
-// as its head concatenation: a 32-wide K stage lies inside one head).  Output layouts: row-major
+// as its head concatenation: a 64-wide K stage is one head).  Output layouts: row-major
 // [T, F], or the head-planar query | key | value planes [3][B, H, n, 64] (F = 3 d_model) that the
 // attention reads.  The epilogue stages each wave's tile through LDS so that global stores are 16
 // bytes per lane over whole row pieces.
@@ -28,20 +29,21 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kBF = kLinearTileF, kBT = kLinearTileT;   // 192 x 256
-constexpr int kBK = 32;                                 // K per stage
-constexpr int kNS = 4;                                  // ring depth
-constexpr int kRowB = kBK * 2;                          // 64-byte LDS rows
-constexpr int kTileW = kBF * kRowB;                     // 12 KB
-constexpr int kTileX = kBT * kRowB;                     // 16 KB
-constexpr int kStage = kTileW + kTileX;                 // 28 KB
-constexpr int kDmaW = kTileW / 1024, kDmaX = kTileX / 1024;   // 12 + 16 instructions per stage
-constexpr int kDma = kDmaW + kDmaX;
+constexpr int kBK = 64;                                 // K per stage
+constexpr int kNS = 2;                                  // stages (double buffer)
+constexpr int kRowB = kBK * 2;                          // 128-byte LDS rows
+constexpr int kTileW = kBF * kRowB;                     // 24 KB
+constexpr int kTileX = kBT * kRowB;                     // 32 KB
+constexpr int kStage = kTileW + kTileX;                 // 56 KB
+constexpr int kDmaW = kTileW / 1024, kDmaX = kTileX / 1024;   // 24 + 32 instructions per stage
+constexpr int kDma = kDmaW + kDmaX;                     // 7 per wave
+static_assert(kDma % 8 == 0, "every wave issues the same number of loads");
 constexpr int kStgRow = 96 * 2 + 16;                    // epilogue staging row (bytes)
 static_assert(8 * 64 * kStgRow <= kNS * kStage, "staging fits in the ring");
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -71,17 +73,6 @@ template <int N>
 __device__ __forceinline__ void vmcnt_le() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    switch (n) {
-        case 0: vmcnt_le<0>(); break;
-        case 3: vmcnt_le<3>(); break;
-        case 4: vmcnt_le<4>(); break;
-        case 6: vmcnt_le<6>(); break;
-        case 8: vmcnt_le<8>(); break;
-        default: vmcnt_le<0>(); break;   // (other counts do not occur; waiting for all is safe)
-    }
-}
-
 __global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearBf16Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kNS * kStage];
     const int lid = xcd_remap(blockIdx.x, a.nlogical);
@@ -96,24 +87,24 @@ __global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearBf16Args a)
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int wf = wave & 1, wt = wave >> 1;
     const uint32_t lds0 = lds_addr(smem);
-    const int nsteps = a.K / kBK;
+    const int nsteps = a.K / kBK;   // K % 64 == 0
 
-    // ---- this wave's DMA instructions of a stage: I = wave + 8 j < kDma; I < kDmaW covers the W
-    // rows 16 I .. 16 I + 15, the others the token rows 16 (I - kDmaW) ..; lane -> row lane / 4,
-    // LDS chunk lane % 4, which holds global chunk (lane % 4) ^ swz(row)
-    const int my_count = (kDma - wave + 7) / 8;   // 4 for waves 0..3, 3 for waves 4..7
+    // ---- this wave's DMA instructions of a stage: I = wave + 8 j (j < 7); I < kDmaW covers the W
+    // rows 8 I .. 8 I + 7, the others the token rows 8 (I - kDmaW) ..; lane -> row lane / 8, LDS
+    // chunk lane % 8, which holds global chunk (lane % 8) ^ swz(row)
+    constexpr int kPer = kDma / 8;
     const i32x4 rw = make_rsrc(a.W, (uint32_t)((size_t)a.F * a.K * 2));
     const i32x4 rx = make_rsrc(a.X, (uint32_t)((size_t)a.T * a.K * 2));
-    uint32_t base_off[4];   // per instruction: byte offset of this lane's row at k = 0
+    uint32_t base_off[kPer];   // per instruction: byte offset of this lane's 16 bytes at k = 0
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kPer; ++j) {
         const int I = wave + 8 * j;
-        const int r = (I < kDmaW ? I : I - kDmaW) * 16 + (lane >> 2);
-        const int gch = (lane & 3) ^ swz(r);
-        uint32_t off = 0;
+        const int r = (I < kDmaW ? I : I - kDmaW) * 8 + (lane >> 3);
+        const int gch = (lane & 7) ^ swz(r);
+        uint32_t off;
         if (I < kDmaW) {
             off = (uint32_t)(((size_t)(f0 + r) * a.K) * 2);
-        } else if (I < kDma) {
+        } else {
             const int t = t0 + r;
             if (a.act_mode == 0) {
                 off = (uint32_t)(((size_t)t * a.K) * 2);
@@ -124,19 +115,20 @@ __global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearBf16Args a)
         }
         base_off[j] = off + (uint32_t)(gch * 16);
     }
-    auto issue = [&](int step, int slot) {
+    // part p (0..3) of stage `step`'s loads: instructions j with j % 4 == p
+    auto issue_part = [&](int step, int slot, int part) {
         const int k0 = step * kBK;
         // byte offset of column k0 within a row: row-major adds k0; head-planar moves to head
-        // k0 / 64 (n rows of 64 further per head) and column k0 % 64
-        const uint32_t xk = a.act_mode == 0
-                                ? (uint32_t)(k0 * 2)
-                                : (uint32_t)((((size_t)(k0 >> 6) * a.n) * 64 + (k0 & 63)) * 2);
+        // k0 / 64, n rows of 64 further per head
+        const uint32_t xk = a.act_mode == 0 ? (uint32_t)(k0 * 2)
+                                            : (uint32_t)(((size_t)(k0 >> 6) * a.n) * 64 * 2);
         const uint32_t sb = lds0 + (uint32_t)slot * kStage;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kPer; ++j) {
+            if (j % 4 != part) continue;
             const int I = wave + 8 * j;
             if (I < kDmaW) dma16(rw, sb + I * 1024, base_off[j] + (uint32_t)(k0 * 2));
-            else if (I < kDma) dma16(rx, sb + kTileW + (I - kDmaW) * 1024, base_off[j] + xk);
+            else dma16(rx, sb + kTileW + (I - kDmaW) * 1024, base_off[j] + xk);
         }
     };
 
@@ -148,36 +140,49 @@ __global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearBf16Args a)
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[mf][mt][j] = 0.0f;
 
-    // per-lane LDS read offsets (row part and swizzle) of the operand rows
-    int w_row[3], x_row[2];
+    // per-lane LDS read offsets of the operand rows: row * 128 and the row's swizzle
+    int w_off[3], w_sw[3], x_off[2], x_sw[2];
 #pragma unroll
-    for (int mf = 0; mf < 3; ++mf) w_row[mf] = wf * 96 + mf * 32 + l32;
+    for (int mf = 0; mf < 3; ++mf) {
+        const int r = wf * 96 + mf * 32 + l32;
+        w_off[mf] = r * kRowB;
+        w_sw[mf] = swz(r);
+    }
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) x_row[mt] = wt * 64 + mt * 32 + l32;
+    for (int mt = 0; mt < 2; ++mt) {
+        const int r = wt * 64 + mt * 32 + l32;
+        x_off[mt] = kTileW + r * kRowB;
+        x_sw[mt] = swz(r);
+    }
 
-    const int npro = min(kNS - 1, nsteps);
-    for (int s = 0; s < npro; ++s) issue(s, s);
+#pragma unroll
+    for (int part = 0; part < 4; ++part) issue_part(0, 0, part);
 
     for (int i = 0; i < nsteps; ++i) {
-        wait_vmcnt(min(kNS - 2, nsteps - 1 - i) * my_count);   // this wave's loads of stage i
-        __syncthreads();                                        // everyone's; slot i-1 is free
-        if (i + kNS - 1 < nsteps) issue(i + kNS - 1, (i + kNS - 1) % kNS);
-        const uint8_t* st = smem + (size_t)(i % kNS) * kStage;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        vmcnt_le<0>();     // this wave's loads of stage i (the only ones in flight)
+        __syncthreads();   // everyone's; the other slot (stage i - 1) is free
+        const bool more = i + 1 < nsteps;
+        const uint8_t* st = smem + (size_t)(i & 1) * kStage;
+        bf16x8 wv[2][3], xv[2][2];
+        auto load_ops = [&](int ks, bf16x8 (&w)[3], bf16x8 (&x)[2]) {
             const int c = 2 * ks + hh;
-            bf16x8 wv[3], xv[2];
 #pragma unroll
             for (int mf = 0; mf < 3; ++mf)
-                wv[mf] = *(const bf16x8*)(st + w_row[mf] * kRowB + ((c ^ swz(w_row[mf])) << 4));
+                w[mf] = *(const bf16x8*)(st + w_off[mf] + ((c ^ w_sw[mf]) << 4));
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
-                xv[mt] = *(const bf16x8*)(st + kTileW + x_row[mt] * kRowB +
-                                          ((c ^ swz(x_row[mt])) << 4));
+                x[mt] = *(const bf16x8*)(st + x_off[mt] + ((c ^ x_sw[mt]) << 4));
+        };
+        load_ops(0, wv[0], xv[0]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) load_ops(ks + 1, wv[(ks + 1) & 1], xv[(ks + 1) & 1]);
+            if (more) issue_part(i + 1, (i + 1) & 1, ks);
 #pragma unroll
             for (int mf = 0; mf < 3; ++mf)
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) acc[mf][mt] = mfma32(wv[mf], xv[mt], acc[mf][mt]);
+                for (int mt = 0; mt < 2; ++mt)
+                    acc[mf][mt] = mfma32(wv[ks & 1][mf], xv[ks & 1][mt], acc[mf][mt]);
         }
     }
 

@@ -128,3 +128,42 @@ def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         L.lib()
+
+
+# ---- encoder attention stack
+def _stack(**kw):
+    s = L.stack(2, 256, 384, 6, 64, 2)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def test_stack_workspace_and_validation():
+    out = ctypes.c_size_t(0)
+    s = _stack()
+    assert L.lib().linformer_stack_workspace_size(ctypes.byref(s), ctypes.byref(out)) == 0
+    act = 2 * 256 * 384 * 2
+    assert out.value >= 4 * act    # query/key/value planes and the attention output at least
+    for field, value, code in [("d_model", 320, 2), ("heads", 5, 2), ("layers", 0, 2),
+                               ("n", 100, 2), ("batch", 0, 2), ("k", 48, 2), ("dtype", 0, 3),
+                               ("keep_layers", 2, 2), ("scale", -1.0, 2)]:
+        bad = _stack(**{field: value})
+        assert L.lib().linformer_stack_workspace_size(ctypes.byref(bad), ctypes.byref(out)) == code, field
+    # batch * n must fill whole 256-token tiles; d_model whole 192-feature tiles
+    assert L.lib().linformer_stack_workspace_size(
+        ctypes.byref(L.stack(1, 192, 384, 6, 64, 1)), ctypes.byref(out)) == 2
+    assert L.lib().linformer_stack_workspace_size(
+        ctypes.byref(L.stack(2, 256, 256, 4, 64, 1)), ctypes.byref(out)) == 2
+
+
+def test_stack_argument_errors_before_any_device_work():
+    s = _stack()
+    big = 1 << 32
+    f = lambda *a: L.linformer_stack_forward(s, *a, check=False)
+    assert f(None, fake(1), fake(2), fake(3), None, fake(4), fake(5), big) == 1
+    assert f(fake(0), fake(1), fake(2), fake(3), None, None, fake(5), big) == 1
+    assert f(fake(0) + 2, fake(1), fake(2), fake(3), None, fake(4), fake(5), big) == 6
+    need = L.linformer_stack_workspace_size(s)
+    assert f(fake(0), fake(1), fake(2), fake(3), None, fake(4), fake(5), need - 1) == 5
+    assert f(fake(0), fake(1), fake(2), fake(3), None, fake(0) + 64, fake(5), big) == 7
+    assert f(fake(0), fake(1), fake(2), fake(3), None, fake(4), fake(4) + 256, big) == 7
