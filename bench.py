@@ -254,6 +254,8 @@ def run_stack_bench(args, L, synth, torch, np):
         return torch.from_numpy(x).to(bf).cuda()
 
     Wq, Wo, E = dev(si.Wqkv), dev(si.Wo), dev(si.E)
+    if args.replicas <= 0:   # the activations are the only per-step input; weights stay resident
+        args.replicas = max(2, -(-(1 << 30) // si.X.size // 2))
     Xs = [dev(si.X) for _ in range(args.replicas)]
     Y = torch.empty(wl.batch, wl.n, wl.d_model, dtype=bf, device="cuda")
     wsb = L.linformer_stack_workspace_size(s)
@@ -305,12 +307,83 @@ def run_stack_bench(args, L, synth, torch, np):
     print(json.dumps(out), flush=True)
 
 
+def run_memory(L, synth, torch, np):
+    """Device memory of one Linformer layer against standard attention, per batch item, and the
+    largest batch that fits on this GPU (B H=12, d=64, bf16, layerwise E = F).
+
+    Linformer: Q, K, V, O plus the library's workspace (Kbar, Vbar, split partial sums), whose
+    per-item size is the slope of linformer_workspace_size over the batch, plus E once.  Standard
+    attention as the pages' baseline computes it keeps the n x n context matrix: fp32 scores and
+    bf16 probabilities per head (6 n^2 bytes per head) besides Q, K, V, O.  The in-repo dense
+    comparator streams keys and keeps no n x n matrix, so its footprint is Q, K, V, O only.  The
+    Linformer figure is also measured: the peak allocation of a forward call at a fixed batch."""
+    H, d = 12, 64
+    free, total = torch.cuda.mem_get_info()
+    budget = free - (1 << 30)   # leave 1 GiB for the runtime
+    rows = []
+    for n in (512, 4096, 65536):
+        for k in (128, 256):
+            # the workspace per item at the largest batch one call takes (the position split,
+            # and with it the partial sums, shrinks as the batch grows)
+            bmax = min(4096, ((1 << 31) - 1) // (H * n * d))
+            pb = L.problem(bmax, H, n, d, k, synth.DT_BF16, synth.SHARE_LAYERWISE, 0.0)
+            qkvo = 4 * H * n * d * 2
+            lin_item = qkvo + L.linformer_workspace_size(pb) / bmax
+            lin_fixed = k * n * 2
+            std_item = qkvo + 6 * H * n * n
+            flash_item = qkvo
+            row = {"n": n, "k": k, "linformer_bytes_per_item": int(lin_item),
+                   "standard_bytes_per_item": std_item, "streamed_dense_bytes_per_item": flash_item,
+                   "linformer_max_batch": int((budget - lin_fixed) // lin_item),
+                   "standard_max_batch": int(budget // std_item),
+                   "streamed_dense_max_batch": int(budget // flash_item),
+                   "bytes_per_item_ratio_vs_standard": round(std_item / lin_item, 2),
+                   "max_batch_per_call": bmax}
+            row["max_batch_ratio_vs_standard"] = (
+                round(row["linformer_max_batch"] / row["standard_max_batch"], 2)
+                if row["standard_max_batch"] > 0 else None)
+            rows.append(row)
+            log(f"n={n:6d} k={k}: Linformer {lin_item / 2**20:9.2f} MiB/item "
+                f"(max batch {row['linformer_max_batch']}), standard {std_item / 2**20:10.2f} MiB/item "
+                f"(max batch {row['standard_max_batch']}), bytes ratio "
+                f"{row['bytes_per_item_ratio_vs_standard']}")
+    # measured peak of one forward call (n = 4096, k = 256, batch 16)
+    B, n, k = 16, 4096, 256
+    p = L.problem(B, H, n, d, k, synth.DT_BF16, synth.SHARE_LAYERWISE, 0.0)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    Q = torch.randn(B, H, n, d, device="cuda").to(torch.bfloat16)
+    K = torch.randn(B, H, n, d, device="cuda").to(torch.bfloat16)
+    V = torch.randn(B, H, n, d, device="cuda").to(torch.bfloat16)
+    E = (torch.randn(1, k, n, device="cuda") / 16).to(torch.bfloat16)
+    O = torch.empty_like(Q)
+    wsb = L.linformer_workspace_size(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    torch.cuda.reset_peak_memory_stats()
+    L.linformer_forward(p, Q, K, V, E, None, None, O, ws, wsb)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    expect = B * (4 * H * n * d * 2) + k * n * 2 + wsb
+    log(f"measured peak of a forward call at B={B} n={n} k={k}: {peak / 2**20:.1f} MiB "
+        f"(Q, K, V, O, E and workspace: {expect / 2**20:.1f} MiB)")
+    print(json.dumps({"memory": rows, "free_bytes": free, "total_bytes": total,
+                      "budget_bytes": budget,
+                      "measured": {"batch": B, "n": n, "k": k, "peak_bytes": int(peak),
+                                   "expected_bytes": int(expect)},
+                      "config": {"heads": H, "head_dim": d, "share": "layerwise",
+                                 "dtype": "bf16"}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="input replicas rotated over the steps; 0 = enough for >= 1 GiB of "
+                         "inputs, so the 256 MB last-level cache cannot serve them")
     ap.add_argument("--workload", default="long_b8_h12_n4096_k256_unshared_padded")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -318,6 +391,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: forward time over n for B1 H12 and "
                          "k = 128, 256 (layerwise E = F), with the dense comparator up to n = 16384")
+    ap.add_argument("--memory", action="store_true",
+                    help="instead of the bench line: device memory per batch item and the largest "
+                         "batch that fits, Linformer against standard attention")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device copy of this many MB (counter calibration)")
     args = ap.parse_args()
@@ -349,6 +425,9 @@ def main():
     if args.sweep:
         run_sweep(L, synth, torch, np)
         return
+    if args.memory:
+        run_memory(L, synth, torch, np)
+        return
     if args.workload in synth.STACK_WORKLOADS:
         run_stack_bench(args, L, synth, torch, np)
         return
@@ -364,6 +443,12 @@ def main():
         return torch.from_numpy(x).to(td).cuda()
 
     p = L.problem(wl.batch, wl.heads, wl.n, wl.d, wl.k, wl.dtype, wl.share, 0.0)
+    if args.replicas <= 0:
+        esz = 2 if wl.dtype == synth.DT_BF16 else 4
+        per = (3 * wl.batch * wl.heads * wl.n * wl.d +
+               wl.e_heads * wl.k * wl.n * (2 if wl.separate_f else 1)) * esz
+        args.replicas = max(2, -(-(1 << 30) // per))
+    log(f"{args.replicas} input replicas")
     reps = []
     for r in range(args.replicas):
         reps.append(dict(Q=dev(inp.Q), K=dev(inp.K), V=dev(inp.V), E=dev(inp.E),
@@ -447,6 +532,23 @@ def main():
     step_flops = kern["project"]["flops"] + kern["attend"]["flops"]
     roof_us = max(step_bytes / (PEAK_HBM_GBS * 1e9), step_flops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
 
+    # the same roofline over the valid work only (rows past each length do no work: the
+    # projection skips them and the attention only zero-fills them)
+    valid = None
+    if inp.lengths is not None:
+        Ls = [int(x) for x in inp.lengths]
+        n_mats = wl.e_heads * (2 if wl.separate_f else 1)
+        eb = 2 if wl.dtype == synth.DT_BF16 else 4
+        vtok = sum(Ls)
+        vbytes = (4 * wl.heads * wl.d * eb * vtok + n_mats * wl.k * wl.n * eb +
+                  2 * 2 * wl.batch * wl.heads * wl.k * wl.d * eb)
+        vflops = 8.0 * wl.heads * wl.k * wl.d * vtok
+        vroof = max(vbytes / (PEAK_HBM_GBS * 1e9), vflops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
+        valid = {"tokens": vtok, "tokens_per_s": round(vtok / (ms / 1e3), 1),
+                 "algorithmic_bytes": vbytes, "flops": vflops, "roofline_us": round(vroof, 2),
+                 "frac": round(vroof / (ms * 1e3), 4)}
+        log(f"valid work: {vtok} tokens, roofline {vroof:.1f} us, frac {vroof / (ms * 1e3):.3f}")
+
     copy_gbs = copy_ceiling(torch)
     log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
 
@@ -494,6 +596,7 @@ def main():
         "roofline": roofline,
         "step_roofline": {"algorithmic_bytes": step_bytes, "roofline_us": round(roof_us, 2),
                           "frac": round(roof_us / (ms * 1e3), 4)},
+        "valid_work_roofline": valid,
         "kernels_us": {k: round(v["us"], 2) for k, v in kern.items()},
         "dense_comparator": dense,
         "copy_ceiling_gbs": round(copy_gbs, 1),

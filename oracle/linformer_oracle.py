@@ -278,3 +278,36 @@ def stack_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, E: np.ndarray
         Y = stack_layer(Y, Wqkv[l], Wo[l], E, heads, lengths, scale)
         outs.append(Y)
     return outs if return_layers else Y
+
+
+# ---------------------------------------------------------------------------------------------
+# Convolution / pooling compression (Linformer 요약 설명, section "Additional Efficiency
+# Techniques": besides shared linear projections, the sequence can be compressed by pooling or a
+# convolution).  Reading: a 1-D convolution along the sequence with window s = n / k and stride
+# s, so projected row r combines positions r s .. r s + s - 1 with weights w[0 .. s-1]; mean
+# pooling is w = 1/s.  As a projection this is the banded E with E[r][r s + j] = w[j] and zeros
+# elsewhere, so the method's definition applies unchanged: the oracle builds that E and calls
+# the same projection and attention.
+# ---------------------------------------------------------------------------------------------
+def conv_projection_matrix(w: np.ndarray, n: int) -> np.ndarray:
+    """The k x n banded E of a stride-s, window-s convolution with weights w (s = len(w))."""
+    w = _f64(w)
+    s = w.shape[0]
+    if n % s:
+        raise ValueError("the window must divide n")
+    k = n // s
+    E = np.zeros((k, n))
+    for r in range(k):
+        E[r, r * s:(r + 1) * s] = w
+    return E
+
+
+def conv_forward(Q, K, V, wE, wF, share: int, lengths=None, scale=None, pairs=None,
+                 return_intermediates: bool = False):
+    """Linformer attention with convolution compression: wE, wF are [H_E, s] window weights
+    (H_E per the sharing mode, as for E and F); F = None as in ``forward``."""
+    n = np.shape(Q)[2]
+    E = np.stack([conv_projection_matrix(w, n) for w in _f64(wE)])
+    F = None if wF is None else np.stack([conv_projection_matrix(w, n) for w in _f64(wF)])
+    return forward(Q, K, V, E, F, share, lengths, scale, pairs=pairs,
+                   return_intermediates=return_intermediates)
