@@ -59,7 +59,7 @@ def traffic_bytes(kernel: str, workload: str):
     return None
 
 
-def algorithmic(wl, kernel: str):
+def algorithmic(wl, kernel: str, conv: bool = False):
     """(bytes, flops) per launch as the method's work is counted in the scope table: over the
     padded length n (tokens = B n), bf16 storage.
 
@@ -76,8 +76,11 @@ def algorithmic(wl, kernel: str):
     kv = 2 * bh * k * d * eb
     flops = 4.0 * bh * n * k * d
     if kernel == "project":
+        if conv:   # one multiply-add per key / value element
+            flops = 4.0 * bh * n * d
         n_mats = wl.e_heads * (2 if wl.separate_f else 1)
-        byts = 2 * bh * n * d * eb + n_mats * k * n * eb + kv
+        # the convolution compression reads window weights (negligible) instead of E and F
+        byts = 2 * bh * n * d * eb + (0 if conv else n_mats * k * n * eb) + kv
     else:
         byts = 2 * bh * n * d * eb + kv
     return byts, flops
@@ -391,6 +394,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: forward time over n for B1 H12 and "
                          "k = 128, 256 (layerwise E = F), with the dense comparator up to n = 16384")
+    ap.add_argument("--proj", choices=("dense", "conv"), default="dense",
+                    help="sequence compression: the dense projection E, F (default) or the "
+                         "window-s stride-s convolution (no E read)")
     ap.add_argument("--memory", action="store_true",
                     help="instead of the bench line: device memory per batch item and the largest "
                          "batch that fits, Linformer against standard attention")
@@ -455,6 +461,14 @@ def main():
                          F=dev(inp.F) if inp.F is not None else None))
     lens = (torch.tensor(inp.lengths, dtype=torch.int32, device="cuda")
             if inp.lengths is not None else None)
+    conv = args.proj == "conv"
+    if conv:   # window weights replace E and F (per head, as E and F are for this workload)
+        s_win = wl.n // wl.k
+        wE = synth.conv_weights(wl.e_heads, s_win, seed=11)
+        wF = synth.conv_weights(wl.e_heads, s_win, seed=12) if wl.separate_f else None
+        for r in reps:
+            r["E"] = dev(wE)
+            r["F"] = dev(wF) if wF is not None else None
     O = torch.empty(wl.batch, wl.heads, wl.n, wl.d, dtype=td, device="cuda")
     wsb = L.linformer_workspace_size(p)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
@@ -465,8 +479,12 @@ def main():
 
     def step(i):
         r = reps[i % len(reps)]
-        L.linformer_forward(p, r["Q"], r["K"], r["V"], r["E"], r["F"], lens, O, ws, wsb,
-                            stream=stream)
+        if conv:
+            L.linformer_forward_conv(p, r["Q"], r["K"], r["V"], r["E"], r["F"], lens, O, ws, wsb,
+                                     stream=stream)
+        else:
+            L.linformer_forward(p, r["Q"], r["K"], r["V"], r["E"], r["F"], lens, O, ws, wsb,
+                                stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -501,18 +519,20 @@ def main():
 
     def run_half(kind, i):
         r = reps[i % len(reps)]
-        if kind == "project":
+        if kind == "project" and conv:
+            L.linformer_project_kv_conv(p, r["K"], r["V"], r["E"], r["F"], lens, Kbar, Vbar,
+                                        stream=stream)
+        elif kind == "project":
             L.linformer_project_kv(p, r["K"], r["V"], r["E"], r["F"], lens, Kbar, Vbar, ws,
                                    wsb, stream=stream)
         else:
             L.linformer_attend(p, r["Q"], Kbar, Vbar, lens, O, stream=stream)
 
-    L.linformer_project_kv(p, reps[0]["K"], reps[0]["V"], reps[0]["E"], reps[0]["F"], lens,
-                           Kbar, Vbar, ws, wsb, stream=stream)
+    run_half("project", 0)
     kern = {}
     for kind in ("project", "attend"):
         us = time_half(kind, args.kernel_iters)
-        byts, flops = algorithmic(wl, kind)
+        byts, flops = algorithmic(wl, kind, conv)
         kern[kind] = dict(us=us, bytes=byts, flops=flops, gbs=byts / (us * 1e-6) / 1e9,
                           tflops=flops / (us * 1e-6) / 1e12)
         log(f"{kind}: {us:.1f} us/launch, {kern[kind]['gbs']:.0f} GB/s algorithmic, "
@@ -540,7 +560,7 @@ def main():
         n_mats = wl.e_heads * (2 if wl.separate_f else 1)
         eb = 2 if wl.dtype == synth.DT_BF16 else 4
         vtok = sum(Ls)
-        vbytes = (4 * wl.heads * wl.d * eb * vtok + n_mats * wl.k * wl.n * eb +
+        vbytes = (4 * wl.heads * wl.d * eb * vtok + (0 if conv else n_mats * wl.k * wl.n * eb) +
                   2 * 2 * wl.batch * wl.heads * wl.k * wl.d * eb)
         vflops = 8.0 * wl.heads * wl.k * wl.d * vtok
         vroof = max(vbytes / (PEAK_HBM_GBS * 1e9), vflops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
@@ -553,7 +573,7 @@ def main():
     log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
 
     dense = None
-    if not args.no_dense and wl.dtype == synth.DT_BF16 and wl.n <= 16384:
+    if not args.no_dense and not conv and wl.dtype == synth.DT_BF16 and wl.n <= 16384:
         Od = torch.empty_like(O)
         for i in range(2):
             L.attention_dense_forward(p, reps[i % len(reps)]["Q"], reps[i % len(reps)]["K"],
@@ -572,7 +592,7 @@ def main():
         log(f"dense O(n^2) attention: {dms * 1e3:.1f} us/step, Linformer speedup {dms / ms:.2f}x")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not conv:
         log("timing the float64 oracle on the host cores ...")
         cpu = cpu_baseline(inp)
         log(f"oracle: {cpu['value']:.3e} tokens/s on {cpu['cores']} threads ({cpu['sample']})")
@@ -592,7 +612,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "seq_len": wl.n,
                    "head_dim": wl.d, "k": wl.k, "share": synth.SHARE_NAMES[wl.share],
-                   "padded": wl.padded, "replicas": args.replicas},
+                   "padded": wl.padded, "replicas": args.replicas,
+                   "compression": "conv (window n/k, per-head weights)" if conv else "dense E, F"},
         "roofline": roofline,
         "step_roofline": {"algorithmic_bytes": step_bytes, "roofline_us": round(roof_us, 2),
                           "frac": round(roof_us / (ms * 1e3), 4)},

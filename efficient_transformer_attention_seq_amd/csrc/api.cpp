@@ -243,6 +243,50 @@ int do_attend(const lf_problem* p, const void* Q, const void* Kbar, const void* 
     return launch_status(lf::launch_attend_bf16(a, stream));
 }
 
+// ---- convolution / pooling compression
+int check_conv(const lf_problem* p, const void* K, const void* V, const void* wE, const void* wF,
+               const int32_t* lengths, const void** wFres) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (p->dtype != LF_BF16) return LF_ERR_DTYPE;
+    if (p->n % p->k) return LF_ERR_SHAPE;
+    if (!K || !V || !wE) return LF_ERR_NULL;
+    st = resolve_f(p, wE, wF, wFres);
+    if (st) return st;
+    if (!aligned16(K) || !aligned16(V)) return LF_ERR_ALIGN;
+    if (((uintptr_t)wE & 1u) || ((uintptr_t)*wFres & 1u)) return LF_ERR_ALIGN;
+    if (lengths && ((uintptr_t)lengths & 3u)) return LF_ERR_ALIGN;
+    return LF_OK;
+}
+
+size_t conv_w_bytes(const lf_problem* p) {
+    const size_t he = p->share == LF_SHARE_NONE ? (size_t)p->heads : 1;
+    return he * (size_t)(p->n / p->k) * 2;
+}
+
+int do_conv(const lf_problem* p, const void* K, const void* V, const void* wE, const void* wF,
+            const int32_t* lengths, void* Kbar, void* Vbar, hipStream_t stream) {
+    lf::ConvBf16Args a{};
+    a.K = (const uint16_t*)K;
+    a.V = (const uint16_t*)V;
+    a.wE = (const uint16_t*)wE;
+    a.wF = (const uint16_t*)wF;
+    a.lengths = lengths;
+    const size_t e = (size_t)p->batch * p->heads * p->k * p->d;
+    a.Khi = (uint16_t*)Kbar;
+    a.Klo = (uint8_t*)Kbar + 2 * e;
+    a.Ksc = (uint8_t*)Kbar + 3 * e;
+    a.Vb = (uint16_t*)Vbar;
+    a.B = p->batch;
+    a.H = p->heads;
+    a.n = p->n;
+    a.k = p->k;
+    a.s = p->n / p->k;
+    a.e_heads = p->share == LF_SHARE_NONE ? p->heads : 1;
+    a.c = eff_scale(p) * lf::kLog2e;
+    return launch_status(lf::launch_conv_bf16(a, stream));
+}
+
 // ---- encoder attention stack
 int check_stack(const lf_stack* s) {
     if (!s) return LF_ERR_NULL;
@@ -524,6 +568,47 @@ int linformer_stack_forward(const lf_stack* s, const void* X, const void* Wqkv, 
         in = out;
     }
     return LF_OK;
+}
+
+int linformer_project_kv_conv(const lf_problem* p, const void* K, const void* V, const void* wE,
+                              const void* wF, const int32_t* lengths, void* Kbar, void* Vbar,
+                              void* stream) {
+    const void* wFr = nullptr;
+    int st = check_conv(p, K, V, wE, wF, lengths, &wFr);
+    if (st) return st;
+    if (!Kbar || !Vbar) return LF_ERR_NULL;
+    if (!aligned16(Kbar) || !aligned16(Vbar)) return LF_ERR_ALIGN;
+    const Range ins[] = {{K, qkv_bytes(p)}, {V, qkv_bytes(p)}, {wE, conv_w_bytes(p)},
+                         {wFr, conv_w_bytes(p)}, {lengths, lengths ? 4u * p->batch : 0u}};
+    const Range outs[] = {{Kbar, kbar_bytes(p)}, {Vbar, vbar_bytes(p)}};
+    if (any_overlap(outs, 2, ins, 5)) return LF_ERR_ALIAS;
+    st = check_device();
+    if (st) return st;
+    return do_conv(p, K, V, wE, wFr, lengths, Kbar, Vbar, (hipStream_t)stream);
+}
+
+int linformer_forward_conv(const lf_problem* p, const void* Q, const void* K, const void* V,
+                           const void* wE, const void* wF, const int32_t* lengths, void* O,
+                           void* ws, size_t ws_bytes, void* stream) {
+    const void* wFr = nullptr;
+    int st = check_conv(p, K, V, wE, wF, lengths, &wFr);
+    if (st) return st;
+    const size_t kb = round_up(kbar_bytes(p), 256), vb = round_up(vbar_bytes(p), 256);
+    if (!Q || !O || !ws) return LF_ERR_NULL;
+    if (ws_bytes < kb + vb) return LF_ERR_WORKSPACE;
+    if (!aligned16(Q) || !aligned16(O) || !aligned16(ws)) return LF_ERR_ALIGN;
+    const Range ins[] = {{Q, qkv_bytes(p)}, {K, qkv_bytes(p)}, {V, qkv_bytes(p)},
+                         {wE, conv_w_bytes(p)}, {wFr, conv_w_bytes(p)},
+                         {lengths, lengths ? 4u * p->batch : 0u}};
+    const Range outs[] = {{O, qkv_bytes(p)}, {ws, kb + vb}};
+    if (any_overlap(outs, 2, ins, 6)) return LF_ERR_ALIAS;
+    st = check_device();
+    if (st) return st;
+    uint8_t* w = (uint8_t*)ws;
+    hipStream_t strm = (hipStream_t)stream;
+    st = do_conv(p, K, V, wE, wFr, lengths, w, w + kb, strm);
+    if (st) return st;
+    return do_attend(p, Q, w, w + kb, lengths, O, strm);
 }
 
 }  // extern "C"

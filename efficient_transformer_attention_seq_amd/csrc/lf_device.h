@@ -54,6 +54,29 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
     return __builtin_bit_cast(bf16x8, u);
 }
 
+// ---- Kbar lo-plane encoding (layout in lf_launch.h)
+// Byte of column d within a lo row.
+__device__ __forceinline__ int lo_pos(int d) { return ((d >> 3) & 1) * 32 + (d >> 4) * 8 + (d & 7); }
+// Block shift s for a block whose largest residual magnitude is m: 2^s m in [128, 256), clamped
+// to the exponent range of the E8M0 scale byte 127 - s (m == 0 gives the smallest scale).
+__device__ __forceinline__ int lo_shift(float m) {
+    const int e = (int)((__float_as_uint(m) >> 23) & 0xFF) - 127;   // floor(log2 m), m normal
+    const int s = 7 - e;
+    return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+// Four residuals -> four e4m3 bytes (round to nearest even) of lo * 2^s.
+__device__ __forceinline__ uint32_t lo_bytes(float l0, float l1, float l2, float l3, int s) {
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(l0, s), ldexpf(l1, s), 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(l2, s), ldexpf(l3, s), w, true);
+}
+// bf16 hi of x and the fp32 residual x - hi.
+__device__ __forceinline__ uint32_t hi_pair(float x0, float x1, float& r0, float& r1) {
+    const uint32_t h = pack_bf16x2(x0, x1);
+    r0 = x0 - __uint_as_float(h << 16);
+    r1 = x1 - __uint_as_float(h & 0xFFFF0000u);
+    return h;
+}
+
 __device__ __forceinline__ int clamp_len(const int32_t* lengths, int b, int n) {
     if (lengths == nullptr) return n;
     int L = lengths[b];

@@ -84,6 +84,22 @@ struct F32Args {
     float scale;
 };
 
+// Convolution / pooling compression (conv_bf16.hip): window weights instead of a dense E.
+struct ConvBf16Args {
+    const uint16_t* K;
+    const uint16_t* V;
+    const uint16_t* wE;     // [e_heads, s] window weights for the keys
+    const uint16_t* wF;     // [e_heads, s] for the values (= wE when shared)
+    const int32_t* lengths;
+    uint16_t* Khi;          // Kbar planes as for the dense projection
+    uint8_t* Klo;
+    uint8_t* Ksc;
+    uint16_t* Vb;
+    int B, H, n, k, s;      // s = n / k
+    int e_heads;            // H (per-head weights) or 1
+    float c;                // scale * log2(e)
+};
+
 // Dense projection Y = X . W^T of the encoder attention stack (linear_bf16.hip).
 struct LinearBf16Args {
     const uint16_t* W;   // [F, K] bf16, row f = output feature f
@@ -120,6 +136,7 @@ hipError_t launch_proj_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_attend_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_dense_bf16(const DenseBf16Args& a, hipStream_t stream);
 hipError_t launch_linear_bf16(const LinearBf16Args& a, hipStream_t stream);
+hipError_t launch_conv_bf16(const ConvBf16Args& a, hipStream_t stream);
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kAttendThreads = 512;

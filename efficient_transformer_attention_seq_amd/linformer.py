@@ -24,7 +24,7 @@ LF_SHARE_NONE, LF_SHARE_HEADWISE, LF_SHARE_KV, LF_SHARE_LAYERWISE = 0, 1, 2, 3
 EXPORTS = ("linformer_status_string", "linformer_workspace_size", "linformer_kv_sizes",
            "linformer_project_kv", "linformer_attend", "linformer_forward",
            "attention_dense_forward", "linformer_stack_workspace_size",
-           "linformer_stack_forward")
+           "linformer_stack_forward", "linformer_project_kv_conv", "linformer_forward_conv")
 
 
 class lf_problem(ctypes.Structure):
@@ -84,6 +84,10 @@ def lib() -> ctypes.CDLL:
     L.linformer_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attention_dense_forward.restype = ctypes.c_int
     L.attention_dense_forward.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.linformer_project_kv_conv.restype = ctypes.c_int
+    L.linformer_project_kv_conv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.linformer_forward_conv.restype = ctypes.c_int
+    L.linformer_forward_conv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     S = ctypes.POINTER(lf_stack)
     L.linformer_stack_workspace_size.restype = ctypes.c_int
     L.linformer_stack_workspace_size.argtypes = [S, ctypes.POINTER(sz)]
@@ -185,3 +189,20 @@ def linformer_stack_forward(s: lf_stack, X, Wqkv, Wo, E, lengths, Y, ws, ws_byte
     code = lib().linformer_stack_forward(ctypes.byref(s), _ptr(X), _ptr(Wqkv), _ptr(Wo), _ptr(E),
                                          _ptr(lengths), _ptr(Y), _ptr(ws), wsb, _stream(stream))
     return _check(code, "linformer_stack_forward", check)
+
+
+def linformer_project_kv_conv(p: lf_problem, K, V, wE, wF, lengths, Kbar, Vbar, stream=None,
+                              check: bool = True) -> int:
+    code = lib().linformer_project_kv_conv(ctypes.byref(p), _ptr(K), _ptr(V), _ptr(wE), _ptr(wF),
+                                           _ptr(lengths), _ptr(Kbar), _ptr(Vbar), _stream(stream))
+    return _check(code, "linformer_project_kv_conv", check)
+
+
+def linformer_forward_conv(p: lf_problem, Q, K, V, wE, wF, lengths, O, ws, ws_bytes=None,
+                           stream=None, check: bool = True) -> int:
+    wsb = ws_bytes if ws_bytes is not None else (
+        0 if ws is None or isinstance(ws, int) else ws.numel() * ws.element_size())
+    code = lib().linformer_forward_conv(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(wE),
+                                        _ptr(wF), _ptr(lengths), _ptr(O), _ptr(ws), wsb,
+                                        _stream(stream))
+    return _check(code, "linformer_forward_conv", check)

@@ -255,3 +255,11 @@ def make_stack_inputs(wl: StackWorkload, seed: Optional[int] = None,
     E = to_dtype(rng.standard_normal((1, wl.k, wl.n)) / np.sqrt(wl.k), DT_BF16)
     lens = None if lengths is None else np.asarray(lengths, dtype=np.int32)
     return StackInputs(wl, X, Wqkv, Wo, E, lens)
+
+
+def conv_weights(e_heads: int, s: int, seed: int, dtype: int = DT_BF16) -> np.ndarray:
+    """Window weights [e_heads, s] of the convolution compression, N(0, 1/s) (so a window of
+    N(0, 1) keys projects to unit variance, as a dense E ~ N(0, 1/k) over n = k s positions
+    does), from their own seeded stream."""
+    rng = np.random.default_rng(seed)
+    return to_dtype(rng.standard_normal((e_heads, s)) / np.sqrt(s), dtype)

@@ -141,6 +141,24 @@ int linformer_forward(const lf_problem* p, const void* Q, const void* K, const v
 int attention_dense_forward(const lf_problem* p, const void* Q, const void* K, const void* V,
                             const int32_t* lengths, void* O, void* stream);
 
+/* ---- Convolution / pooling compression (Linformer 요약 설명, section "Additional Efficiency
+ * Techniques": the sequence may be compressed by pooling or a convolution instead of a learned
+ * dense projection).  With window s = n / k and stride s the projected rows are
+ *     Kbar[r] = sum_{j < s} wE[j] K[r s + j],   Vbar[r] = sum_{j < s} wF[j] V[r s + j]
+ * over the valid positions, which is the projection by the banded E with E[r][r s + j] = wE[j]
+ * (mean pooling: w = 1/s).  wE, wF: bf16 [H_E, s] with H_E and the sharing rules of E and F
+ * above.  Requires n % k == 0 and LF_BF16; Kbar and Vbar in the layouts of linformer_kv_sizes();
+ * no workspace (ws may be NULL for the projection; linformer_forward_conv needs
+ * linformer_workspace_size() bytes).  Attention is linformer_attend() unchanged. */
+int linformer_project_kv_conv(const lf_problem* p, const void* K, const void* V, const void* wE,
+                              const void* wF, const int32_t* lengths, void* Kbar, void* Vbar,
+                              void* stream);
+
+/* linformer_project_kv_conv() into the workspace, then linformer_attend(). */
+int linformer_forward_conv(const lf_problem* p, const void* Q, const void* K, const void* V,
+                           const void* wE, const void* wF, const int32_t* lengths, void* O,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* ---- Encoder attention stack.  Each of `layers` layers maps its input X [B, n, d_model] to
  * every head's queries, keys and values, runs Linformer attention (above) on every head with one
  * layerwise-shared E, concatenates the heads and applies the output projection; the result is the

@@ -277,3 +277,32 @@ def run_stack(si: synth.StackInputs, keep_layers: bool = True, scale: float = 0.
     L.linformer_stack_forward(s, X, Wq, Wo, E, lens, Y, ws, wsb)
     torch.cuda.synchronize()
     return host(Y), (guards_intact(buf) if guard else True)
+
+
+def run_conv(inp: synth.Inputs, wE: np.ndarray, wF, scale: float = 0.0, guard: bool = False):
+    """linformer_project_kv_conv then linformer_forward_conv on the same inputs; returns
+    (Kbar as decoded true values, Vbar, O, guards intact)."""
+    torch = torch_mod()
+    wl = inp.wl
+    p = prob(wl, scale)
+    BF = synth.DT_BF16
+    K, V, Q = dev(inp.K, BF), dev(inp.V, BF), dev(inp.Q, BF)
+    dE = dev(wE, BF)
+    dF = dev(wF, BF) if wF is not None else None
+    lens = lengths_dev(inp.lengths)
+    kb, vb = L.linformer_kv_sizes(p)
+    Kbar = torch.empty(kb, dtype=torch.uint8, device="cuda")
+    Vbar = torch.empty(vb // 2, dtype=torch.bfloat16, device="cuda")
+    L.linformer_project_kv_conv(p, K, V, dE, dF, lens, Kbar, Vbar)
+    wsb = L.linformer_workspace_size(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    if guard:
+        buf, O = guarded((wl.batch, wl.heads, wl.n, wl.d), BF)
+    else:
+        buf, O = None, empty((wl.batch, wl.heads, wl.n, wl.d), BF)
+    L.linformer_forward_conv(p, Q, K, V, dE, dF, lens, O, ws, wsb)
+    torch.cuda.synchronize()
+    shape = (wl.batch, wl.heads, wl.k, wl.d)
+    _, _, x = decode_kbar_bf16(Kbar.cpu().numpy(), shape)
+    c = log2e_scale(wl, scale)
+    return x / c, host(Vbar).reshape(shape), host(O), (guards_intact(buf) if guard else True)
