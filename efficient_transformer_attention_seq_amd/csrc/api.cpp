@@ -293,8 +293,7 @@ int check_stack(const lf_stack* s) {
     if (s->dtype != LF_BF16) return LF_ERR_DTYPE;
     if (s->layers < 1 || s->heads < 1 || s->d_model != 64 * s->heads) return LF_ERR_SHAPE;
     if (s->d_model % lf::kLinearTileF) return LF_ERR_SHAPE;
-    if (s->batch < 1 || s->n < 64 || ((long long)s->batch * s->n) % lf::kLinearTileT)
-        return LF_ERR_SHAPE;
+    if (s->batch < 1 || s->n < 64) return LF_ERR_SHAPE;
     if (3LL * s->batch * s->n * s->d_model >= (1LL << 30)) return LF_ERR_SHAPE;
     if (s->keep_layers != 0 && s->keep_layers != 1) return LF_ERR_SHAPE;
     return LF_OK;
@@ -313,40 +312,44 @@ lf_problem layer_problem(const lf_stack* s) {
     return p;
 }
 
-struct StackWs {
-    size_t planes, o, ping, layer_ws, total;   // byte offsets / sizes
-    size_t act;                                 // bytes of one [B, n, d_model] activation
-};
-
-// Workspace: the query | key | value planes, the attention output, two activation buffers (only
-// when intermediate layer outputs are not kept in Y), then the single layer's workspace.
-bool stack_ws(const lf_stack* s, const lf_problem& p, const lf::ProjGeom& g, StackWs* w) {
-    w->act = (size_t)s->batch * s->n * s->d_model * 2;
-    w->planes = 0;
-    w->o = round_up(3 * w->act, 256);
-    w->ping = w->o + round_up(w->act, 256);
-    const size_t nping = (s->keep_layers || s->layers == 1) ? 0 : (s->layers == 2 ? 1 : 2);
-    w->layer_ws = w->ping + nping * round_up(w->act, 256);
-    const size_t kb = round_up(kbar_bytes(&p), 256), vb = round_up(vbar_bytes(&p), 256);
-    w->total = w->layer_ws + kb + vb + round_up(part_bytes(&p, g), 256);
+// Projection of a layer input X [B, n, d_model] (row-major) by the one E: unit (b, h) = columns
+// 64 h .. 64 h + 63 of X_b, output Xbar = E . X_b as bf16 [B, H, k, 64].
+bool stack_geometry(const lf_stack* s, lf::ProjGeom* g) {
+    if (!lf::proj_geometry(s->batch, s->heads, s->n, s->k, lf::kProjSingle,
+                           env_int("LINFORMER_PROJ_SPLIT"), std::getenv("LINFORMER_PROJ_CFG"), g))
+        return false;
+    g->xb = (long long)s->n * s->d_model;
+    g->xh = 64;
+    g->xrow = s->d_model;
     return true;
 }
 
-int do_linear(const uint16_t* W, const void* X, void* Y, int T, int F, int K, int n, int H,
-              int act_mode, int out_mode, hipStream_t stream) {
-    lf::LinearBf16Args a{};
-    a.W = W;
-    a.X = (const uint16_t*)X;
-    a.Y = (uint16_t*)Y;
-    a.T = T;
-    a.F = F;
-    a.K = K;
-    a.n = n;
-    a.H = H;
-    a.act_mode = act_mode;
-    a.out_mode = out_mode;
-    a.plane = (size_t)T * (F / 3);
-    a.nlogical = (F / lf::kLinearTileF) * (T / lf::kLinearTileT);
+struct StackWs {
+    size_t act;                                        // bytes of one [B, n, d_model] activation
+    size_t q, o, xbar, kbar, vbar, part, ping, total;  // byte offsets
+};
+
+// Workspace: queries, attention output, Xbar, Kbar, Vbar, the projection's split partials, and
+// two activation buffers (only when intermediate layer outputs are not kept in Y).
+void stack_ws(const lf_stack* s, const lf_problem& p, const lf::ProjGeom& g, StackWs* w) {
+    w->act = (size_t)s->batch * s->n * s->d_model * 2;
+    const size_t xbar = (size_t)s->batch * s->k * s->d_model * 2;
+    const size_t part = g.S > 1 ? (size_t)g.S * 2 * s->batch * s->heads * s->k * 64 * 4 : 0;
+    w->q = 0;
+    w->o = w->q + round_up(w->act, 256);
+    w->xbar = w->o + round_up(w->act, 256);
+    w->kbar = w->xbar + round_up(xbar, 256);
+    w->vbar = w->kbar + round_up(kbar_bytes(&p), 256);
+    w->part = w->vbar + round_up(vbar_bytes(&p), 256);
+    w->ping = w->part + round_up(part, 256);
+    const size_t nping = (s->keep_layers || s->layers == 1) ? 0 : (s->layers == 2 ? 1 : 2);
+    w->total = w->ping + nping * round_up(w->act, 256);
+}
+
+int do_linear(const lf::LinearBf16Args& base, hipStream_t stream) {
+    lf::LinearBf16Args a = base;
+    const int ttiles = (a.T + lf::kLinearTileT - 1) / lf::kLinearTileT;
+    a.nlogical = (a.F / lf::kLinearTileF) * ttiles;
     return launch_status(lf::launch_linear_bf16(a, stream));
 }
 
@@ -500,13 +503,17 @@ int linformer_stack_workspace_size(const lf_stack* s, size_t* bytes) {
     st = check_problem(&p);
     if (st) return st;
     lf::ProjGeom g;
-    if (!geometry(&p, &g)) return LF_ERR_SHAPE;
+    if (!stack_geometry(s, &g)) return LF_ERR_SHAPE;
     StackWs w;
     stack_ws(s, p, g, &w);
     *bytes = w.total;
     return LF_OK;
 }
 
+// Per layer, with one E for the keys and the values of every head (layerwise sharing), the
+// projected keys are E . (X W_K^T) = (E . X) W_K^T, and likewise for the values: the layer
+// projects its input once along the sequence (Xbar = E . X, k x d_model per batch item) and maps
+// Xbar by W_K and W_V, so the n-long keys and values are never formed.  The queries are X W_Q^T.
 int linformer_stack_forward(const lf_stack* s, const void* X, const void* Wqkv, const void* Wo,
                             const void* E, const int32_t* lengths, void* Y, void* ws,
                             size_t ws_bytes, void* stream) {
@@ -516,7 +523,7 @@ int linformer_stack_forward(const lf_stack* s, const void* X, const void* Wqkv, 
     st = check_problem(&p);
     if (st) return st;
     lf::ProjGeom g;
-    if (!geometry(&p, &g)) return LF_ERR_SHAPE;
+    if (!stack_geometry(s, &g)) return LF_ERR_SHAPE;
     StackWs w;
     stack_ws(s, p, g, &w);
     if (!X || !Wqkv || !Wo || !E || !Y || !ws) return LF_ERR_NULL;
@@ -536,19 +543,14 @@ int linformer_stack_forward(const lf_stack* s, const void* X, const void* Wqkv, 
 
     hipStream_t strm = (hipStream_t)stream;
     uint8_t* base = (uint8_t*)ws;
-    uint8_t* planes = base + w.planes;
-    const size_t plane_bytes = w.act;   // B H n 64 = B n d_model elements
-    void* Qp = planes;
-    void* Kp = planes + plane_bytes;
-    void* Vp = planes + 2 * plane_bytes;
-    void* O = base + w.o;
-    uint8_t* lw = base + w.layer_ws;
-    void* Kbar = lw;
-    void* Vbar = lw + round_up(kbar_bytes(&p), 256);
-    void* part = part_bytes(&p, g) ? (void*)(lw + round_up(kbar_bytes(&p), 256) +
-                                             round_up(vbar_bytes(&p), 256))
-                                   : nullptr;
+    uint16_t* Qp = (uint16_t*)(base + w.q);
+    uint16_t* O = (uint16_t*)(base + w.o);
+    uint16_t* Xbar = (uint16_t*)(base + w.xbar);
+    uint8_t* Kbar = base + w.kbar;
+    uint16_t* Vbar = (uint16_t*)(base + w.vbar);
+    const size_t e = (size_t)s->batch * s->heads * s->k * 64;
     const int T = s->batch * s->n, D = s->d_model;
+    const float c = eff_scale(&p) * lf::kLog2e;
     const void* in = X;
     for (int l = 0; l < s->layers; ++l) {
         void* out;
@@ -557,13 +559,70 @@ int linformer_stack_forward(const lf_stack* s, const void* X, const void* Wqkv, 
         else out = base + w.ping + (size_t)(l & 1) * round_up(w.act, 256);
         const uint16_t* Wl = (const uint16_t*)Wqkv + (size_t)l * 3 * dm * dm;
         const uint16_t* Wol = (const uint16_t*)Wo + (size_t)l * dm * dm;
-        st = do_linear(Wl, in, planes, T, 3 * D, D, s->n, s->heads, 0, 1, strm);
+        // queries: X W_Q^T into the head-planar plane the attention reads
+        lf::LinearBf16Args q{};
+        q.W = Wl;
+        q.X = (const uint16_t*)in;
+        q.Y = Qp;
+        q.T = T;
+        q.F = D;
+        q.K = D;
+        q.n = s->n;
+        q.H = s->heads;
+        q.act_mode = 0;
+        q.out_mode = 1;
+        q.dm = D;
+        q.plane = (size_t)T * D;
+        st = do_linear(q, strm);
         if (st) return st;
-        st = do_project(&p, Kp, Vp, E, E, lengths, Kbar, Vbar, part, g, strm);
+        // Xbar = E . X over the valid positions
+        lf::ProjBf16Args pa{};
+        pa.K = (const uint16_t*)in;
+        pa.V = (const uint16_t*)in;
+        pa.E = (const uint16_t*)E;
+        pa.F = (const uint16_t*)E;
+        pa.lengths = lengths;
+        pa.Vb = Xbar;
+        pa.part = g.S > 1 ? (float*)(base + w.part) : nullptr;
+        pa.c = 1.0f;
+        pa.g = g;
+        st = launch_status(lf::launch_proj_bf16(pa, strm));
+        if (st) return st;
+        // Kbar | Vbar = Xbar [W_K; W_V]^T, Kbar straight into the attention's format
+        lf::LinearBf16Args kv{};
+        kv.W = Wl + dm * dm;
+        kv.X = Xbar;
+        kv.Y = (uint16_t*)Kbar;
+        kv.Klo = Kbar + 2 * e;
+        kv.Ksc = Kbar + 3 * e;
+        kv.Yv = Vbar;
+        kv.c = c;
+        kv.T = s->batch * s->k;
+        kv.F = 2 * D;
+        kv.K = D;
+        kv.n = s->k;
+        kv.H = s->heads;
+        kv.act_mode = 1;
+        kv.out_mode = 2;
+        kv.dm = D;
+        st = do_linear(kv, strm);
         if (st) return st;
         st = do_attend(&p, Qp, Kbar, Vbar, lengths, O, strm);
         if (st) return st;
-        st = do_linear(Wol, O, out, T, D, D, s->n, s->heads, 1, 0, strm);
+        // output projection of the concatenated heads
+        lf::LinearBf16Args o{};
+        o.W = Wol;
+        o.X = O;
+        o.Y = (uint16_t*)out;
+        o.T = T;
+        o.F = D;
+        o.K = D;
+        o.n = s->n;
+        o.H = s->heads;
+        o.act_mode = 1;
+        o.out_mode = 0;
+        o.dm = D;
+        st = do_linear(o, strm);
         if (st) return st;
         in = out;
     }

@@ -15,8 +15,15 @@ namespace lf {
 //   unshared  : group g = which * H + h, members b            (A = E_h or F_h)
 //   headwise  : group g = which,          members (b, h)       (A = E or F)
 //   key-value / layerwise: one group,     members (which, b, h) (A = E)
+//   single (kProjSingle, internal): one group, members (b, h), which = 1 only: Vbar = E . V with
+//             bf16 output (used by the encoder stack to project its layer input once)
+// Unit (which, b, h) reads rows t = 0 .. n-1 of K or V at element offset b xb + h xh + t xrow
+// (64 contiguous elements per row): [B, H, n, 64] is xb = H n 64, xh = n 64, xrow = 64.
+constexpr int kProjSingle = 4;
 struct ProjGeom {
     int B, H, n, k, share;
+    long long xb, xh;     // unit strides of K and V (elements)
+    int xrow;             // row stride of K and V (elements, >= 64)
     int groups;           // number of distinct A matrices in use
     int members;          // units per group
     int cfg;              // tile configuration id
@@ -108,8 +115,16 @@ struct LinearBf16Args {
     int T, F, K;         // tokens (multiple of kLinearTileT), features (of kLinearTileF), K % 32 == 0
     int n, H;            // tokens per batch item and heads (head-planar layouts)
     int act_mode;        // 0: row-major [T, K]; 1: head-planar [B, H, n, 64] with K = 64 H
-    int out_mode;        // 0: row-major [T, F]; 1: query | key | value planes [3][B, H, n, 64]
+    int out_mode;        // 0: row-major [T, F]; 1: head-planar planes [F / dm][B, H, n, 64];
+                         // 2: Kbar (features < dm, stored as the attention's Kbar planes, scaled
+                         //    by c) then Vbar (features >= dm, bf16 [B, H, n, 64]); here the
+                         //    "tokens" are projected slots, n = k
+    int dm;              // plane width in features (64 H) for out_modes 1 and 2
     size_t plane;        // elements of one plane (out_mode 1)
+    uint8_t* Klo;        // out_mode 2: Kbar residual plane and block scales; Y is the Kbar hi
+    uint8_t* Ksc;        //   plane and Yv the Vbar plane
+    uint16_t* Yv;
+    float c;             // out_mode 2: scale * log2(e)
     int nlogical;        // (F / kLinearTileF) * (T / kLinearTileT)
 };
 

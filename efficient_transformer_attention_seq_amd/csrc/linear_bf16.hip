@@ -17,7 +17,8 @@
 // fetches.  The operands of sub-step ks + 1 are read while the MFMAs of sub-step ks run.
 //
 // Activation layouts: row-major [T, K], or head-planar [B, H, n, 64] (the attention output, read
-// as its head concatenation: a 64-wide K stage is one head).  Output layouts: row-major
+// as its head concatenation: a 64-wide K stage is one head).  T need not fill the last token
+// tile: rows past T read as zero through the buffer descriptors and are not stored.  Output layouts: row-major
 // [T, F], or the head-planar query | key | value planes [3][B, H, n, 64] (F = 3 d_model) that the
 // attention reads.  The epilogue stages each wave's tile through LDS so that global stores are 16
 // bytes per lane over whole row pieces.
@@ -186,6 +187,59 @@ __global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearBf16Args a)
         }
     }
 
+    if (a.out_mode == 2) {
+        // ---- projected keys and values straight from the accumulators: lane (l32, hh) holds,
+        // for slot row 32 mt + l32 of the wave tile, features 32 mf + 8 g + 4 hh + (0..3); the 32
+        // features of block mf are one row half of one head, shared with lane l32 + 32 (hh = 1)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int t = t0 + wt * 64 + mt * 32 + l32;
+            const int b = t / a.n, r = t - b * a.n;
+#pragma unroll
+            for (int mf = 0; mf < 3; ++mf) {
+                const int fb = f0 + wf * 96 + mf * 32;   // first feature of the block
+                const f32x16& x = acc[mf][mt];
+                if (fb >= a.dm) {   // values: bf16
+                    if (t >= a.T) continue;   // (a last token tile past T)
+                    const int fh = fb - a.dm;
+                    uint16_t* dst = a.Yv + (((size_t)b * a.H + (fh >> 6)) * a.n + r) * 64 + (fh & 63);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const u32x2 v = {pack_bf16x2(x[4 * g], x[4 * g + 1]),
+                                         pack_bf16x2(x[4 * g + 2], x[4 * g + 3])};
+                        *(u32x2*)(dst + 8 * g + 4 * hh) = v;
+                    }
+                } else {            // keys: c Kbar as hi plane + fp8 residual with a block scale
+                    float lo[16];
+                    u32x2 hv[4];
+                    float m = 0.0f;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        hv[g][0] = hi_pair(a.c * x[4 * g], a.c * x[4 * g + 1], lo[4 * g], lo[4 * g + 1]);
+                        hv[g][1] = hi_pair(a.c * x[4 * g + 2], a.c * x[4 * g + 3], lo[4 * g + 2], lo[4 * g + 3]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(lo[4 * g + i]));
+                    }
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+                    m = fmaxf(m, __uint_as_float(hh ? sw[0] : sw[1]));
+                    const int sh = lo_shift(m);
+                    const size_t row = ((size_t)b * a.H + (fb >> 6)) * a.n + r;
+                    const int d0 = fb & 63;   // 0 or 32: the row half
+                    if (t >= a.T) continue;   // after the exchange, which every lane joins
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int d = d0 + 8 * g + 4 * hh;
+                        *(u32x2*)(a.Y + row * 64 + d) = hv[g];
+                        *(uint32_t*)(a.Klo + row * 64 + lo_pos(d)) =
+                            lo_bytes(lo[4 * g], lo[4 * g + 1], lo[4 * g + 2], lo[4 * g + 3], sh);
+                    }
+                    if (hh == 0) a.Ksc[row * 2 + (d0 >> 5)] = (uint8_t)(127 - sh);
+                }
+            }
+        }
+        return;
+    }
+
     // ---- epilogue: lane (l32, hh) holds, for token 32 mt + l32 of the wave tile, features
     // 32 mf + 8 g + 4 hh + (0..3); stage as [64 tokens][96 features] bf16, then store rows
     __syncthreads();   // every wave is done with the ring
@@ -202,13 +256,14 @@ __global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearBf16Args a)
                 *(u32x2*)(stg + (32 * mt + l32) * kStgRow + (32 * mf + 8 * g + 4 * hh) * 2) = v;
             }
     __syncthreads();
-    const int dm = a.F / 3;   // (output mode 1 only)
+    const int dm = a.dm;   // (output mode 1 only)
 #pragma unroll
     for (int j = 0; j < 12; ++j) {
         const int idx = j * 64 + lane;        // 64 tokens x 12 chunks of 8 features
         const int tr = idx / 12, q = idx - tr * 12;
         const u32x4 v = *(const u32x4*)(stg + tr * kStgRow + q * 16);
         const int t = t0 + wt * 64 + tr;
+        if (t >= a.T) continue;   // (a last token tile past T)
         const int f = f0 + wf * 96 + q * 8;
         size_t dst;
         if (a.out_mode == 0) {

@@ -103,6 +103,10 @@ __device__ __forceinline__ Unit unit_of(const ProjGeom& g, int grp, int j) {
         u.which = grp;
         u.b = j / g.H;
         u.h = j % g.H;
+    } else if (g.share == kProjSingle) {   // one matrix, member = (b, h), values only
+        u.which = 1;
+        u.b = j / g.H;
+        u.h = j % g.H;
     } else {                          // key-value / layerwise: member = (which, b, h)
         const int bh = g.B * g.H;
         u.which = j / bh;
@@ -204,9 +208,9 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
         const int j = j0 + u;
         if (j < g.members) {
             const Unit un = unit_of(g, grp, j);
-            const uint16_t* X =
-                (un.which ? a.V : a.K) + (size_t)(un.b * g.H + un.h) * g.n * kHeadDim;
-            rsrc_x[u] = make_rsrc(X, (uint32_t)ulen[u] * kHeadDim * 2);
+            const uint16_t* X = (un.which ? a.V : a.K) + un.b * g.xb + un.h * g.xh;
+            // rows past the length lie at or beyond the descriptor's size, so they read as zero
+            rsrc_x[u] = make_rsrc(X, ulen[u] > 0 ? (uint32_t)(((size_t)(ulen[u] - 1) * g.xrow + kHeadDim) * 2) : 0u);
         } else {
             rsrc_x[u] = make_rsrc(a.K, 0u);
         }
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
             const int q = xq0 + NW * qi;
             const int tl = q * 8 + lrow;
             const int lc = 2 * ((lpc >> 1) ^ (tl & 3)) + (lpc & 1);
-            const uint32_t xoff = (uint32_t)((t0 + tl) * kHeadDim + lc * 8) * 2;
+            const uint32_t xoff = (uint32_t)(((size_t)(t0 + tl) * g.xrow + lc * 8) * 2);
 #pragma unroll
             for (int u = 0; u < UPT; ++u)
                 if (u % 3 == part - 1)
@@ -447,13 +451,13 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
 // of the finishing wave.
 template <int NG>
 __global__ __launch_bounds__(256) void proj_fixup_bf16_kernel(const float* part, int S,
-                                                              size_t half, float c,
+                                                              size_t half, size_t e0, float c,
                                                               uint16_t* Khi, uint8_t* Klo,
                                                               uint8_t* Ksc, uint16_t* Vb) {
     constexpr int CH = 256 / NG;   // four-column chunks per block
     __shared__ f32x4 quarter[NG > 1 ? NG : 1][CH];
     const int ci = threadIdx.x % CH, grp = threadIdx.x / CH;
-    const size_t e4 = ((size_t)blockIdx.x * CH + ci) * 4;
+    const size_t e4 = e0 + ((size_t)blockIdx.x * CH + ci) * 4;   // e0: first element (0 or half)
     const bool live = e4 < 2 * half;   // 2 * half is a multiple of 64: whole blocks leave together
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     if (live) {
@@ -531,11 +535,17 @@ bool proj_geometry(int B, int H, int n, int k, int share, int split_override,
     g.n = n;
     g.k = k;
     g.share = share;
+    g.xb = (long long)H * n * kHeadDim;   // [B, H, n, 64] unless the caller sets other strides
+    g.xh = (long long)n * kHeadDim;
+    g.xrow = kHeadDim;
     if (share == 0) {
         g.groups = 2 * H;
         g.members = B;
     } else if (share == 1) {
         g.groups = 2;
+        g.members = B * H;
+    } else if (share == kProjSingle) {
+        g.groups = 1;
         g.members = B * H;
     } else {
         g.groups = 1;
@@ -616,13 +626,15 @@ hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream) {
     }
     if (e != hipSuccess || g.S == 1) return e;
     const size_t half = (size_t)g.B * g.H * g.k * kHeadDim;
-    const size_t chunks = 2 * half / 4;
+    // the single-matrix mode has only the values half
+    const size_t e0 = g.share == kProjSingle ? half : 0;
+    const size_t chunks = (2 * half - e0) / 4;
     if (g.S >= 8) {   // many splits: spread each chunk's reduction over 4 waves
         hipLaunchKernelGGL(proj_fixup_bf16_kernel<4>, dim3((int)((chunks + 63) / 64)), dim3(256), 0,
-                           stream, a.part, g.S, half, a.c, a.Khi, a.Klo, a.Ksc, a.Vb);
+                           stream, a.part, g.S, half, e0, a.c, a.Khi, a.Klo, a.Ksc, a.Vb);
     } else {
         hipLaunchKernelGGL(proj_fixup_bf16_kernel<1>, dim3((int)((chunks + 255) / 256)), dim3(256), 0,
-                           stream, a.part, g.S, half, a.c, a.Khi, a.Klo, a.Ksc, a.Vb);
+                           stream, a.part, g.S, half, e0, a.c, a.Khi, a.Klo, a.Ksc, a.Vb);
     }
     return hipGetLastError();
 }

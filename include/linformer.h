@@ -177,9 +177,12 @@ int linformer_forward_conv(const lf_problem* p, const void* Q, const void* K, co
  *   Y     [B, n, d_model] (keep_layers = 0) or [layers, B, n, d_model] (every layer's output)
  *   lengths as for the single layer: padded positions contribute nothing and output rows past
  *   the length are zero in every layer.
- * Shape limits: d_model = 64 heads, d_model % 192 == 0, (batch * n) % 256 == 0, the single layer's
- * limits on n, k and batch, and 3 batch n d_model < 2^30.  dtype must be LF_BF16.  Ownership,
- * threading and errors as above; Y must not overlap any input or the workspace. */
+ * Shape limits: d_model = 64 heads, d_model % 192 == 0, the single layer's limits on n, k and
+ * batch, and 3 batch n d_model < 2^30.  dtype must be LF_BF16.  Ownership, threading and errors
+ * as above; Y must not overlap any input or the workspace.
+ * With one E for the keys and the values, E . (X W_K^T) = (E . X) W_K^T: each layer projects its
+ * input once along the sequence and maps the k projected rows by W_K and W_V (the same result up
+ * to rounding, with the n-long keys and values never formed). */
 typedef struct lf_stack {
     int32_t batch;        /* B                                                       */
     int32_t n;            /* padded maximum sequence length                          */

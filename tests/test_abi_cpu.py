@@ -143,15 +143,15 @@ def test_stack_workspace_and_validation():
     s = _stack()
     assert L.lib().linformer_stack_workspace_size(ctypes.byref(s), ctypes.byref(out)) == 0
     act = 2 * 256 * 384 * 2
-    assert out.value >= 4 * act    # query/key/value planes and the attention output at least
+    assert out.value >= 2 * act    # the query plane and the attention output at least
     for field, value, code in [("d_model", 320, 2), ("heads", 5, 2), ("layers", 0, 2),
                                ("n", 100, 2), ("batch", 0, 2), ("k", 48, 2), ("dtype", 0, 3),
                                ("keep_layers", 2, 2), ("scale", -1.0, 2)]:
         bad = _stack(**{field: value})
         assert L.lib().linformer_stack_workspace_size(ctypes.byref(bad), ctypes.byref(out)) == code, field
-    # batch * n must fill whole 256-token tiles; d_model whole 192-feature tiles
+    # any batch * n (a last token tile may be partial); d_model whole 192-feature tiles
     assert L.lib().linformer_stack_workspace_size(
-        ctypes.byref(L.stack(1, 192, 384, 6, 64, 1)), ctypes.byref(out)) == 2
+        ctypes.byref(L.stack(1, 192, 384, 6, 64, 1)), ctypes.byref(out)) == 0
     assert L.lib().linformer_stack_workspace_size(
         ctypes.byref(L.stack(2, 256, 256, 4, 64, 1)), ctypes.byref(out)) == 2
 
