@@ -311,3 +311,57 @@ def conv_forward(Q, K, V, wE, wF, share: int, lengths=None, scale=None, pairs=No
     F = None if wF is None else np.stack([conv_projection_matrix(w, n) for w in _f64(wF)])
     return forward(Q, K, V, E, F, share, lengths, scale, pairs=pairs,
                    return_intermediates=return_intermediates)
+
+
+# ---------------------------------------------------------------------------------------------
+# Backward pass for learned projections (Linformer card, 方法适配: E and F are learned, so training
+# needs the gradients of the layer with respect to Q, K, V, E and F).  For a loss whose gradient
+# with respect to O is dO, per (b, h) with valid length L (rows i >= L of O are fixed at zero, so
+# dO there has no effect):
+#   Kbar = E[:, :L] K[:L],  Vbar = F[:, :L] V[:L],  P = softmax(s Q Kbar^T),  O = P Vbar
+#   dVbar = P^T dO          dP = dO Vbar^T          dS = P o (dP - rowsum(P o dP))
+#   dQ = s dS Kbar          dKbar = s dS^T Q
+#   dE[:, :L] += dKbar K[:L]^T,   dK[:L] = E[:, :L]^T dKbar
+#   dF[:, :L] += dVbar V[:L]^T,   dV[:L] = F[:, :L]^T dVbar
+# (the softmax Jacobian written out: d s_r = P_r (dP_r - sum_q P_q dP_q)).  Shared matrices
+# collect the gradients of every head (and of both K and V when E = F) that uses them.
+# ---------------------------------------------------------------------------------------------
+def backward(Q, K, V, E, F, share: int, dO, lengths: Optional[Sequence[int]] = None,
+             scale: Optional[float] = None):
+    """Returns dQ, dK, dV ([B, H, n, d]), dE ([H_E, k, n]) and dF (same shape, or None when F
+    aliases E, in which case dE holds both contributions)."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    B, H, n, d = Q.shape
+    s = (1.0 / np.sqrt(d)) if (scale is None or scale == 0.0) else float(scale)
+    Es, Fs = head_projections(E, F, share, H)
+    E = _f64(E)
+    separate = share in (SHARE_NONE, SHARE_HEADWISE) and F is not None
+    dE = np.zeros_like(E)
+    dF = np.zeros_like(E) if separate else None
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+
+    def e_index(h):
+        return h if share == SHARE_NONE else 0
+
+    for b in range(B):
+        L = n if lengths is None else max(0, min(int(lengths[b]), n))
+        for h in range(H):
+            Eh, Fh = Es[h], Fs[h]
+            Kb = project(Eh, K[b, h], L)
+            Vb = project(Fh, V[b, h], L)
+            P = attention_weights(Q[b, h], Kb, s)
+            g = dO[b, h].copy()
+            g[L:] = 0.0
+            dVb = np.matmul(P.T, g)
+            dP = np.matmul(g, Vb.T)
+            dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+            dQ[b, h] = s * np.matmul(dS, Kb)
+            dKb = s * np.matmul(dS.T, Q[b, h])
+            dK[b, h, :L] = np.matmul(Eh[:, :L].T, dKb)
+            dV[b, h, :L] = np.matmul(Fh[:, :L].T, dVb)
+            dE[e_index(h), :, :L] += np.matmul(dKb, K[b, h, :L].T)
+            if separate:
+                dF[e_index(h), :, :L] += np.matmul(dVb, V[b, h, :L].T)
+            else:
+                dE[e_index(h), :, :L] += np.matmul(dVb, V[b, h, :L].T)
+    return dQ, dK, dV, dE, dF
