@@ -379,6 +379,61 @@ def run_memory(L, synth, torch, np):
                                  "dtype": "bf16"}}), flush=True)
 
 
+PEAK_F32_VALU_TFLOPS = 157.3   # MI355X fp32 vector: 256 CUs x 4 SIMD x 64 lanes x 2 flop x 2.4 GHz
+
+
+def run_backward(args, L, synth, torch, np):
+    """linformer_backward on a workload's inputs with a random upstream gradient: gradients of Q,
+    K, V, E, F (fp32 arithmetic on the vector units).  Algorithmic work per (b, h): 22 n k d flops
+    (Kbar, Vbar recomputed: 4; scores, dP, dQ: 6; dVbar, dKbar: 4; dE, dF: 4; dK, dV: 4)."""
+    wl = synth.WORKLOADS[args.workload]
+    inp = synth.make_inputs(wl)
+    td = torch.bfloat16 if wl.dtype == synth.DT_BF16 else torch.float32
+    dev = lambda x: torch.from_numpy(x).to(td).cuda()
+    p = L.problem(wl.batch, wl.heads, wl.n, wl.d, wl.k, wl.dtype, wl.share, 0.0)
+    Q, K, V, E = dev(inp.Q), dev(inp.K), dev(inp.V), dev(inp.E)
+    F = dev(inp.F) if inp.F is not None else None
+    lens = (torch.tensor(inp.lengths, dtype=torch.int32, device="cuda")
+            if inp.lengths is not None else None)
+    dO = dev(np.random.default_rng(1).standard_normal((wl.batch, wl.heads, wl.n, wl.d)).astype(np.float32))
+    f32 = lambda shape: torch.empty(shape, dtype=torch.float32, device="cuda")
+    shp = (wl.batch, wl.heads, wl.n, wl.d)
+    dQ, dK, dV, dE = f32(shp), f32(shp), f32(shp), f32(tuple(inp.E.shape))
+    dF = f32(tuple(inp.F.shape)) if inp.F is not None else None
+    wsb = L.linformer_backward_workspace_size(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        L.linformer_backward(p, Q, K, V, E, F, lens, dO, dQ, dK, dV, dE, dF, ws, wsb,
+                             stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    flops = 22.0 * wl.batch * wl.heads * wl.n * wl.k * wl.d
+    tf = flops / (ms * 1e-3) / 1e12
+    tokens = wl.batch * wl.n
+    log(f"backward: {ms * 1e3:.1f} us/step ({tokens / (ms / 1e3):.3e} tokens/s), {tf:.1f} TFLOP/s fp32")
+    print(json.dumps({
+        "metric": "Linformer backward (dQ, dK, dV, dE, dF) tokens/s", "value": round(tokens / (ms / 1e3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "inputs": "bf16" if wl.dtype == synth.DT_BF16 else "f32"},
+        "roofline": {"bound": "alu", "achieved": round(tf, 1), "peak": PEAK_F32_VALU_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_F32_VALU_TFLOPS, 4), "traffic": None,
+                     "kernel": "whole backward step", "algorithmic_flops": flops},
+        "device": torch.cuda.get_device_name(0)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -397,6 +452,8 @@ def main():
     ap.add_argument("--proj", choices=("dense", "conv"), default="dense",
                     help="sequence compression: the dense projection E, F (default) or the "
                          "window-s stride-s convolution (no E read)")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the bench line: time the backward pass on the workload")
     ap.add_argument("--memory", action="store_true",
                     help="instead of the bench line: device memory per batch item and the largest "
                          "batch that fits, Linformer against standard attention")
@@ -433,6 +490,9 @@ def main():
         return
     if args.memory:
         run_memory(L, synth, torch, np)
+        return
+    if args.backward:
+        run_backward(args, L, synth, torch, np)
         return
     if args.workload in synth.STACK_WORKLOADS:
         run_stack_bench(args, L, synth, torch, np)

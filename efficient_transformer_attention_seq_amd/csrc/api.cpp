@@ -287,6 +287,45 @@ int do_conv(const lf_problem* p, const void* K, const void* V, const void* wE, c
     return launch_status(lf::launch_conv_bf16(a, stream));
 }
 
+// ---- backward pass
+struct BwWs {
+    size_t q, k, v, g, e, f, kb, vb, p, ds, dkb, dvb, total;   // byte offsets
+};
+
+void bw_ws(const lf_problem* p, bool separate, BwWs* w) {
+    const size_t act = (size_t)p->batch * p->heads * p->n * 64 * 4;
+    const size_t mat = (size_t)(p->share == LF_SHARE_NONE ? p->heads : 1) * p->k * p->n * 4;
+    const size_t kv = (size_t)p->batch * p->heads * p->k * 64 * 4;
+    const size_t pk = (size_t)p->batch * p->heads * p->n * p->k * 4;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t at = o; o += round_up(bytes, 256); return at; };
+    w->q = take(act);
+    w->k = take(act);
+    w->v = take(act);
+    w->g = take(act);
+    w->e = take(mat);
+    w->f = separate ? take(mat) : w->e;
+    w->kb = take(kv);
+    w->vb = take(kv);
+    w->p = take(pk);
+    w->ds = take(pk);
+    w->dkb = take(kv);
+    w->dvb = take(kv);
+    w->total = o;
+}
+
+bool bw_separate(const lf_problem* p, const void* E, const void* F) {
+    return (p->share == LF_SHARE_NONE || p->share == LF_SHARE_HEADWISE) && F && F != E;
+}
+
+lf::BwGemm gemm0() {
+    lf::BwGemm g{};
+    g.Z = 1;
+    g.zdiv = 1;
+    g.alpha = 1.0f;
+    return g;
+}
+
 // ---- encoder attention stack
 int check_stack(const lf_stack* s) {
     if (!s) return LF_ERR_NULL;
@@ -668,6 +707,138 @@ int linformer_forward_conv(const lf_problem* p, const void* Q, const void* K, co
     st = do_conv(p, K, V, wE, wFr, lengths, w, w + kb, strm);
     if (st) return st;
     return do_attend(p, Q, w, w + kb, lengths, O, strm);
+}
+
+int linformer_backward_workspace_size(const lf_problem* p, size_t* bytes) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!bytes) return LF_ERR_NULL;
+    BwWs w;
+    bw_ws(p, p->share == LF_SHARE_NONE || p->share == LF_SHARE_HEADWISE, &w);   // the larger
+    *bytes = w.total;
+    return LF_OK;
+}
+
+int linformer_backward(const lf_problem* p, const void* Q, const void* K, const void* V,
+                       const void* E, const void* F, const int32_t* lengths, const void* dO,
+                       float* dQ, float* dK, float* dV, float* dE, float* dF, void* ws,
+                       size_t ws_bytes, void* stream) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!Q || !K || !V || !E || !dO || !dQ || !dK || !dV || !dE || !ws) return LF_ERR_NULL;
+    const void* Fr = nullptr;
+    st = resolve_f(p, E, F, &Fr);
+    if (st) return st;
+    const bool separate = bw_separate(p, E, F);
+    if (separate != (dF != nullptr)) return separate ? LF_ERR_NULL : LF_ERR_SHARE;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(E) || !aligned16(Fr) ||
+        !aligned16(dO) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(dE) ||
+        (dF && !aligned16(dF)) || !aligned16(ws))
+        return LF_ERR_ALIGN;
+    if (lengths && ((uintptr_t)lengths & 3u)) return LF_ERR_ALIGN;
+    BwWs w;
+    bw_ws(p, separate, &w);
+    size_t need = 0;
+    linformer_backward_workspace_size(p, &need);
+    if (ws_bytes < need) return LF_ERR_WORKSPACE;
+    const size_t g4 = (size_t)p->batch * p->heads * p->n * 64 * 4;
+    const size_t m4 = (size_t)(p->share == LF_SHARE_NONE ? p->heads : 1) * p->k * p->n * 4;
+    const Range ins[] = {{Q, qkv_bytes(p)}, {K, qkv_bytes(p)}, {V, qkv_bytes(p)},
+                         {E, ef_bytes(p)}, {Fr, ef_bytes(p)}, {dO, qkv_bytes(p)},
+                         {lengths, lengths ? 4u * p->batch : 0u}};
+    const Range outs[] = {{dQ, g4}, {dK, g4}, {dV, g4}, {dE, m4}, {dF, dF ? m4 : 0}, {ws, need}};
+    if (any_overlap(outs, 6, ins, 7)) return LF_ERR_ALIAS;
+    st = check_device();
+    if (st) return st;
+
+    hipStream_t strm = (hipStream_t)stream;
+    uint8_t* b = (uint8_t*)ws;
+    float *Qf = (float*)(b + w.q), *Kf = (float*)(b + w.k), *Vf = (float*)(b + w.v);
+    float *Gf = (float*)(b + w.g), *Ef = (float*)(b + w.e), *Ff = (float*)(b + w.f);
+    float *Kb = (float*)(b + w.kb), *Vb = (float*)(b + w.vb), *P = (float*)(b + w.p);
+    float *dS = (float*)(b + w.ds), *dKb = (float*)(b + w.dkb), *dVb = (float*)(b + w.dvb);
+    const int bf = p->dtype == LF_BF16 ? 1 : 0;
+    const int B = p->batch, H = p->heads, n = p->n, k = p->k;
+    const size_t cnt = (size_t)B * H * n * 64;
+    const size_t mcnt = (size_t)(p->share == LF_SHARE_NONE ? H : 1) * k * n;
+    const float s = eff_scale(p);
+    const bool unshared = p->share == LF_SHARE_NONE;
+    hipError_t e = lf::launch_bw_convert(Q, bf, Qf, cnt, lengths, H, n, 0, strm);
+    if (e == hipSuccess) e = lf::launch_bw_convert(K, bf, Kf, cnt, lengths, H, n, 1, strm);
+    if (e == hipSuccess) e = lf::launch_bw_convert(V, bf, Vf, cnt, lengths, H, n, 1, strm);
+    if (e == hipSuccess) e = lf::launch_bw_convert(dO, bf, Gf, cnt, lengths, H, n, 1, strm);
+    if (e == hipSuccess) e = lf::launch_bw_convert(E, bf, Ef, mcnt, nullptr, 1, 1, 0, strm);
+    if (e == hipSuccess && separate) e = lf::launch_bw_convert(Fr, bf, Ff, mcnt, nullptr, 1, 1, 0, strm);
+    if (e != hipSuccess) return LF_ERR_LAUNCH;
+    const long long hn64 = (long long)n * 64, hk64 = (long long)k * 64, kn = (long long)k * n;
+    // Kbar = E_h K, Vbar = F_h V: z = (b, h), M = k, N = 64, reduction over n
+    auto project = [&](const float* A, const float* X, float* out) {
+        lf::BwGemm g = gemm0();
+        g.A = A; g.B = X; g.C = out;
+        g.M = k; g.N = 64; g.K = n; g.Z = B * H; g.zdiv = H; g.kblk = n;
+        g.a_z2 = unshared ? kn : 0; g.a_i = n; g.a_kc = 1;
+        g.b_z1 = H * hn64; g.b_z2 = hn64; g.b_kc = 64; g.b_j = 1;
+        g.c_z1 = H * hk64; g.c_z2 = hk64; g.c_i = 64; g.c_j = 1;
+        return lf::launch_bw_gemm(g, strm);
+    };
+    e = project(Ef, Kf, Kb);
+    if (e == hipSuccess) e = project(Ff, Vf, Vb);
+    if (e != hipSuccess) return LF_ERR_LAUNCH;
+    lf::BwAttendArgs at{};
+    at.Q = Qf; at.dO = Gf; at.Kb = Kb; at.Vb = Vb; at.P = P; at.dS = dS; at.dQ = dQ;
+    at.B = B; at.H = H; at.n = n; at.k = k; at.scale = s;
+    if (lf::launch_bw_attend(at, strm) != hipSuccess) return LF_ERR_LAUNCH;
+    // dVbar = P^T dO, dKbar = s dS^T Q: z = (b, h), M = k, N = 64, reduction over the n queries
+    auto reduce_q = [&](const float* A, const float* X, float* out, float alpha) {
+        lf::BwGemm g = gemm0();
+        g.A = A; g.B = X; g.C = out; g.alpha = alpha;
+        g.M = k; g.N = 64; g.K = n; g.Z = B * H; g.zdiv = H; g.kblk = n;
+        g.a_z1 = H * (long long)n * k; g.a_z2 = (long long)n * k; g.a_i = 1; g.a_kc = k;
+        g.b_z1 = H * hn64; g.b_z2 = hn64; g.b_kc = 64; g.b_j = 1;
+        g.c_z1 = H * hk64; g.c_z2 = hk64; g.c_i = 64; g.c_j = 1;
+        return lf::launch_bw_gemm(g, strm);
+    };
+    e = reduce_q(P, Gf, dVb, 1.0f);
+    if (e == hipSuccess) e = reduce_q(dS, Qf, dKb, s);
+    if (e != hipSuccess) return LF_ERR_LAUNCH;
+    // dE (+)= dXbar X^T: M = k, N = n, reduction over (b, c) (unshared: z = h) or over (b, h, c)
+    auto grad_mat = [&](const float* dXb, const float* X, float* out, float beta) {
+        lf::BwGemm g = gemm0();
+        g.A = dXb; g.B = X; g.C = out; g.beta = beta;
+        g.M = k; g.N = n; g.kblk = 64;
+        if (unshared) {
+            g.Z = H; g.K = B * 64;
+            g.a_z1 = hk64; g.a_kb = H * hk64;
+            g.b_z1 = hn64; g.b_kb = H * hn64;
+            g.c_z1 = kn;
+        } else {
+            g.Z = 1; g.K = B * H * 64;
+            g.a_kb = hk64;
+            g.b_kb = hn64;
+        }
+        g.a_i = 64; g.a_kc = 1;
+        g.b_kc = 1; g.b_j = 64;
+        g.c_i = n; g.c_j = 1;
+        return lf::launch_bw_gemm(g, strm);
+    };
+    e = grad_mat(dKb, Kf, dE, 0.0f);
+    if (e == hipSuccess) e = separate ? grad_mat(dVb, Vf, dF, 0.0f) : grad_mat(dVb, Vf, dE, 1.0f);
+    if (e != hipSuccess) return LF_ERR_LAUNCH;
+    // dK = E_h^T dKbar, dV = F_h^T dVbar: z = (b, h), M = n, N = 64, reduction over k
+    auto back = [&](const float* A, const float* dXb, float* out) {
+        lf::BwGemm g = gemm0();
+        g.A = A; g.B = dXb; g.C = out;
+        g.M = n; g.N = 64; g.K = k; g.Z = B * H; g.zdiv = H; g.kblk = k;
+        g.a_z2 = unshared ? kn : 0; g.a_i = 1; g.a_kc = n;
+        g.b_z1 = H * hk64; g.b_z2 = hk64; g.b_kc = 64; g.b_j = 1;
+        g.c_z1 = H * hn64; g.c_z2 = hn64; g.c_i = 64; g.c_j = 1;
+        return lf::launch_bw_gemm(g, strm);
+    };
+    e = back(Ef, dKb, dK);
+    if (e == hipSuccess) e = back(Ff, dVb, dV);
+    if (e == hipSuccess) e = lf::launch_bw_mask_rows(dK, cnt, lengths, H, n, strm);
+    if (e == hipSuccess) e = lf::launch_bw_mask_rows(dV, cnt, lengths, H, n, strm);
+    return launch_status(e);
 }
 
 }  // extern "C"

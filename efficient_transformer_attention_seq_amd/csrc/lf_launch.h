@@ -107,6 +107,35 @@ struct ConvBf16Args {
     float c;                // scale * log2(e)
 };
 
+// Backward pass (backward_f32.hip).  Strided batched fp32 GEMM:
+//   C(z, i, j) = alpha sum_{kk < K} A(z, i, kk) B(z, kk, j) + beta C(z, i, j)
+// with z1 = z / zdiv, z2 = z % zdiv, kb = kk / kblk, kc = kk % kblk and
+//   A(z, i, kk) at A + z1 a_z1 + z2 a_z2 + i a_i + kb a_kb + kc a_kc
+//   B(z, kk, j) at B + z1 b_z1 + z2 b_z2 + kb b_kb + kc b_kc + j b_j
+//   C(z, i, j)  at C + z1 c_z1 + z2 c_z2 + i c_i + j c_j
+struct BwGemm {
+    const float* A;
+    const float* B;
+    float* C;
+    int M, N, K, Z, zdiv, kblk;
+    long long a_z1, a_z2, a_i, a_kb, a_kc;
+    long long b_z1, b_z2, b_kb, b_kc, b_j;
+    long long c_z1, c_z2, c_i, c_j;
+    float alpha, beta;
+};
+
+struct BwAttendArgs {
+    const float* Q;    // [B, H, n, 64]
+    const float* dO;   // [B, H, n, 64], rows past the lengths zero
+    const float* Kb;   // [B, H, k, 64]
+    const float* Vb;
+    float* P;          // [B, H, n, k]
+    float* dS;         // [B, H, n, k]
+    float* dQ;         // [B, H, n, 64]
+    int B, H, n, k;
+    float scale;
+};
+
 // Dense projection Y = X . W^T of the encoder attention stack (linear_bf16.hip).
 struct LinearBf16Args {
     const uint16_t* W;   // [F, K] bf16, row f = output feature f
@@ -152,6 +181,12 @@ hipError_t launch_attend_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_dense_bf16(const DenseBf16Args& a, hipStream_t stream);
 hipError_t launch_linear_bf16(const LinearBf16Args& a, hipStream_t stream);
 hipError_t launch_conv_bf16(const ConvBf16Args& a, hipStream_t stream);
+hipError_t launch_bw_convert(const void* src, int src_bf16, float* dst, size_t count,
+                             const int32_t* lengths, int H, int n, int mask, hipStream_t stream);
+hipError_t launch_bw_mask_rows(float* x, size_t count, const int32_t* lengths, int H, int n,
+                               hipStream_t stream);
+hipError_t launch_bw_gemm(const BwGemm& g, hipStream_t stream);
+hipError_t launch_bw_attend(const BwAttendArgs& a, hipStream_t stream);
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kAttendThreads = 512;

@@ -24,7 +24,8 @@ LF_SHARE_NONE, LF_SHARE_HEADWISE, LF_SHARE_KV, LF_SHARE_LAYERWISE = 0, 1, 2, 3
 EXPORTS = ("linformer_status_string", "linformer_workspace_size", "linformer_kv_sizes",
            "linformer_project_kv", "linformer_attend", "linformer_forward",
            "attention_dense_forward", "linformer_stack_workspace_size",
-           "linformer_stack_forward", "linformer_project_kv_conv", "linformer_forward_conv")
+           "linformer_stack_forward", "linformer_project_kv_conv", "linformer_forward_conv",
+           "linformer_backward_workspace_size", "linformer_backward")
 
 
 class lf_problem(ctypes.Structure):
@@ -88,6 +89,10 @@ def lib() -> ctypes.CDLL:
     L.linformer_project_kv_conv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     L.linformer_forward_conv.restype = ctypes.c_int
     L.linformer_forward_conv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.linformer_backward_workspace_size.restype = ctypes.c_int
+    L.linformer_backward_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+    L.linformer_backward.restype = ctypes.c_int
+    L.linformer_backward.argtypes = [P] + [vp] * 12 + [vp, sz, vp]
     S = ctypes.POINTER(lf_stack)
     L.linformer_stack_workspace_size.restype = ctypes.c_int
     L.linformer_stack_workspace_size.argtypes = [S, ctypes.POINTER(sz)]
@@ -206,3 +211,20 @@ def linformer_forward_conv(p: lf_problem, Q, K, V, wE, wF, lengths, O, ws, ws_by
                                         _ptr(wF), _ptr(lengths), _ptr(O), _ptr(ws), wsb,
                                         _stream(stream))
     return _check(code, "linformer_forward_conv", check)
+
+
+def linformer_backward_workspace_size(p: lf_problem) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().linformer_backward_workspace_size(ctypes.byref(p), ctypes.byref(out)),
+           "linformer_backward_workspace_size", True)
+    return out.value
+
+
+def linformer_backward(p: lf_problem, Q, K, V, E, F, lengths, dO, dQ, dK, dV, dE, dF, ws,
+                       ws_bytes=None, stream=None, check: bool = True) -> int:
+    wsb = ws_bytes if ws_bytes is not None else (
+        0 if ws is None or isinstance(ws, int) else ws.numel() * ws.element_size())
+    code = lib().linformer_backward(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(E), _ptr(F),
+                                    _ptr(lengths), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                    _ptr(dE), _ptr(dF), _ptr(ws), wsb, _stream(stream))
+    return _check(code, "linformer_backward", check)

@@ -159,6 +159,24 @@ int linformer_forward_conv(const lf_problem* p, const void* Q, const void* K, co
                            const void* wE, const void* wF, const int32_t* lengths, void* O,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Backward pass for learned projections (Linformer card, section 方法适配: E and F are
+ * learned).  Given dO = dLoss/dO for the layer above, writes the gradients of the loss with
+ * respect to Q, K, V, E and F, from the softmax Jacobian: with P = softmax(s Q Kbar^T),
+ *   dVbar = P^T dO, dP = dO Vbar^T, dS = P o (dP - rowsum(P o dP)),
+ *   dQ = s dS Kbar, dKbar = s dS^T Q, dE = dKbar K^T, dK = E^T dKbar, dF = dVbar V^T, dV = F^T dVbar
+ * per (b, h); shared matrices collect every head that uses them.  Padding as in the forward:
+ * rows of dO past the length have no effect, and the gradients of K, V rows and of the E, F
+ * columns past the length are zero.  Inputs in p->dtype and the forward layouts; gradients fp32:
+ * dQ, dK, dV [B, H, n, d]; dE [H_E, k, n]; dF like dE when F is a separate matrix (headwise, or
+ * unshared with F given and != E), else dF must be NULL and dE holds both projections' parts.
+ * All arithmetic fp32 (Kbar, Vbar recomputed in fp32).  ws: linformer_backward_workspace_size()
+ * bytes of scratch. */
+int linformer_backward_workspace_size(const lf_problem* p, size_t* bytes);
+int linformer_backward(const lf_problem* p, const void* Q, const void* K, const void* V,
+                       const void* E, const void* F, const int32_t* lengths, const void* dO,
+                       float* dQ, float* dK, float* dV, float* dE, float* dF, void* ws,
+                       size_t ws_bytes, void* stream);
+
 /* ---- Encoder attention stack.  Each of `layers` layers maps its input X [B, n, d_model] to
  * every head's queries, keys and values, runs Linformer attention (above) on every head with one
  * layerwise-shared E, concatenates the heads and applies the output projection; the result is the

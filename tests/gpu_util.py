@@ -306,3 +306,26 @@ def run_conv(inp: synth.Inputs, wE: np.ndarray, wF, scale: float = 0.0, guard: b
     _, _, x = decode_kbar_bf16(Kbar.cpu().numpy(), shape)
     c = log2e_scale(wl, scale)
     return x / c, host(Vbar).reshape(shape), host(O), (guards_intact(buf) if guard else True)
+
+
+def run_backward(inp: synth.Inputs, dO: np.ndarray, scale: float = 0.0):
+    """linformer_backward on the inputs and an upstream gradient dO; returns (dQ, dK, dV, dE, dF)
+    as float64 numpy (dF None when F aliases E)."""
+    torch = torch_mod()
+    wl = inp.wl
+    p = prob(wl, scale)
+    Q, K, V = dev(inp.Q, wl.dtype), dev(inp.K, wl.dtype), dev(inp.V, wl.dtype)
+    E = dev(inp.E, wl.dtype)
+    F = dev(inp.F, wl.dtype) if inp.F is not None else None
+    G = dev(dO, wl.dtype)
+    lens = lengths_dev(inp.lengths)
+    f32 = lambda shape: torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    shp = (wl.batch, wl.heads, wl.n, wl.d)
+    dQ, dK, dV = f32(shp), f32(shp), f32(shp)
+    dE = f32(tuple(inp.E.shape))
+    dF = f32(tuple(inp.F.shape)) if inp.F is not None else None
+    wsb = L.linformer_backward_workspace_size(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    L.linformer_backward(p, Q, K, V, E, F, lens, G, dQ, dK, dV, dE, dF, ws, wsb)
+    torch.cuda.synchronize()
+    return tuple(None if t is None else t.double().cpu().numpy() for t in (dQ, dK, dV, dE, dF))
