@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdlib>
@@ -289,7 +290,7 @@ int do_conv(const lf_problem* p, const void* K, const void* V, const void* wE, c
 
 // ---- backward pass
 struct BwWs {
-    size_t q, k, v, g, e, f, kb, vb, p, ds, dkb, dvb, total;   // byte offsets
+    size_t q, k, v, g, e, f, kb, vb, p, ds, dkb, dvb, part, total;   // byte offsets
 };
 
 void bw_ws(const lf_problem* p, bool separate, BwWs* w) {
@@ -311,6 +312,14 @@ void bw_ws(const lf_problem* p, bool separate, BwWs* w) {
     w->ds = take(pk);
     w->dkb = take(kv);
     w->dvb = take(kv);
+    // split-reduction partial sums, the largest any of the backward's GEMMs asks for
+    const int B = p->batch, H = p->heads, n = p->n, k = p->k;
+    const bool unshared = p->share == LF_SHARE_NONE;
+    size_t part = lf::bw_gemm_part_bytes(k, 64, n, B * H);                         // Kbar, dXbar
+    part = std::max(part, lf::bw_gemm_part_bytes(k, n, unshared ? B * 64 : B * H * 64,
+                                                 unshared ? H : 1));                // dE, dF
+    part = std::max(part, lf::bw_gemm_part_bytes(n, 64, k, B * H));                // dK, dV
+    w->part = take(part);
     w->total = o;
 }
 
@@ -757,6 +766,12 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
     float *Gf = (float*)(b + w.g), *Ef = (float*)(b + w.e), *Ff = (float*)(b + w.f);
     float *Kb = (float*)(b + w.kb), *Vb = (float*)(b + w.vb), *P = (float*)(b + w.p);
     float *dS = (float*)(b + w.ds), *dKb = (float*)(b + w.dkb), *dVb = (float*)(b + w.dvb);
+    float* part = (float*)(b + w.part);
+    auto run_gemm = [&](lf::BwGemm& g) {
+        lf::bw_gemm_plan(g);
+        g.part = part;
+        return lf::launch_bw_gemm(g, strm);
+    };
     const int bf = p->dtype == LF_BF16 ? 1 : 0;
     const int B = p->batch, H = p->heads, n = p->n, k = p->k;
     const size_t cnt = (size_t)B * H * n * 64;
@@ -779,7 +794,7 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
         g.a_z2 = unshared ? kn : 0; g.a_i = n; g.a_kc = 1;
         g.b_z1 = H * hn64; g.b_z2 = hn64; g.b_kc = 64; g.b_j = 1;
         g.c_z1 = H * hk64; g.c_z2 = hk64; g.c_i = 64; g.c_j = 1;
-        return lf::launch_bw_gemm(g, strm);
+        return run_gemm(g);
     };
     e = project(Ef, Kf, Kb);
     if (e == hipSuccess) e = project(Ff, Vf, Vb);
@@ -788,15 +803,16 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
     at.Q = Qf; at.dO = Gf; at.Kb = Kb; at.Vb = Vb; at.P = P; at.dS = dS; at.dQ = dQ;
     at.B = B; at.H = H; at.n = n; at.k = k; at.scale = s;
     if (lf::launch_bw_attend(at, strm) != hipSuccess) return LF_ERR_LAUNCH;
-    // dVbar = P^T dO, dKbar = s dS^T Q: z = (b, h), M = k, N = 64, reduction over the n queries
+    // dVbar = P^T dO, dKbar = s dS^T Q (P, dS stored [B, H, k, n]): z = (b, h), M = k, N = 64,
+    // reduction over the n queries
     auto reduce_q = [&](const float* A, const float* X, float* out, float alpha) {
         lf::BwGemm g = gemm0();
         g.A = A; g.B = X; g.C = out; g.alpha = alpha;
         g.M = k; g.N = 64; g.K = n; g.Z = B * H; g.zdiv = H; g.kblk = n;
-        g.a_z1 = H * (long long)n * k; g.a_z2 = (long long)n * k; g.a_i = 1; g.a_kc = k;
+        g.a_z1 = H * kn; g.a_z2 = kn; g.a_i = n; g.a_kc = 1;
         g.b_z1 = H * hn64; g.b_z2 = hn64; g.b_kc = 64; g.b_j = 1;
         g.c_z1 = H * hk64; g.c_z2 = hk64; g.c_i = 64; g.c_j = 1;
-        return lf::launch_bw_gemm(g, strm);
+        return run_gemm(g);
     };
     e = reduce_q(P, Gf, dVb, 1.0f);
     if (e == hipSuccess) e = reduce_q(dS, Qf, dKb, s);
@@ -819,7 +835,7 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
         g.a_i = 64; g.a_kc = 1;
         g.b_kc = 1; g.b_j = 64;
         g.c_i = n; g.c_j = 1;
-        return lf::launch_bw_gemm(g, strm);
+        return run_gemm(g);
     };
     e = grad_mat(dKb, Kf, dE, 0.0f);
     if (e == hipSuccess) e = separate ? grad_mat(dVb, Vf, dF, 0.0f) : grad_mat(dVb, Vf, dE, 1.0f);
@@ -832,12 +848,11 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
         g.a_z2 = unshared ? kn : 0; g.a_i = 1; g.a_kc = n;
         g.b_z1 = H * hk64; g.b_z2 = hk64; g.b_kc = 64; g.b_j = 1;
         g.c_z1 = H * hn64; g.c_z2 = hn64; g.c_i = 64; g.c_j = 1;
-        return lf::launch_bw_gemm(g, strm);
+        g.row_len = lengths;   // positions past the length get zero gradients
+        return run_gemm(g);
     };
     e = back(Ef, dKb, dK);
     if (e == hipSuccess) e = back(Ff, dVb, dV);
-    if (e == hipSuccess) e = lf::launch_bw_mask_rows(dK, cnt, lengths, H, n, strm);
-    if (e == hipSuccess) e = lf::launch_bw_mask_rows(dV, cnt, lengths, H, n, strm);
     return launch_status(e);
 }
 

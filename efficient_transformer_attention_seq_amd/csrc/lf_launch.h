@@ -107,12 +107,15 @@ struct ConvBf16Args {
     float c;                // scale * log2(e)
 };
 
-// Backward pass (backward_f32.hip).  Strided batched fp32 GEMM:
+// Backward pass (backward_f32.hip).  Strided batched fp32 GEMM on the matrix cores:
 //   C(z, i, j) = alpha sum_{kk < K} A(z, i, kk) B(z, kk, j) + beta C(z, i, j)
 // with z1 = z / zdiv, z2 = z % zdiv, kb = kk / kblk, kc = kk % kblk and
 //   A(z, i, kk) at A + z1 a_z1 + z2 a_z2 + i a_i + kb a_kb + kc a_kc
 //   B(z, kk, j) at B + z1 b_z1 + z2 b_z2 + kb b_kb + kc b_kc + j b_j
 //   C(z, i, j)  at C + z1 c_z1 + z2 c_z2 + i c_i + j c_j
+// kblk must be a multiple of 32.  The reduction may be split into `splits` chunks of `kchunk`
+// (set by bw_gemm_plan); each chunk then writes its partial sums to `part` ([splits][Z][M][N]
+// fp32, bw_gemm_part_bytes) and a second kernel adds them in chunk order.
 struct BwGemm {
     const float* A;
     const float* B;
@@ -122,15 +125,23 @@ struct BwGemm {
     long long b_z1, b_z2, b_kb, b_kc, b_j;
     long long c_z1, c_z2, c_i, c_j;
     float alpha, beta;
+    int splits, kchunk;
+    float* part;
+    const int32_t* row_len;   // optional: rows i >= row_len[z1] of C are written as zero
 };
+
+// Chooses splits / kchunk for g's shape (enough workgroups to cover the chip).
+void bw_gemm_plan(BwGemm& g);
+// Partial-sum bytes a GEMM of this shape needs after bw_gemm_plan (0 without a split).
+size_t bw_gemm_part_bytes(int M, int N, int K, int Z);
 
 struct BwAttendArgs {
     const float* Q;    // [B, H, n, 64]
     const float* dO;   // [B, H, n, 64], rows past the lengths zero
     const float* Kb;   // [B, H, k, 64]
     const float* Vb;
-    float* P;          // [B, H, n, k]
-    float* dS;         // [B, H, n, k]
+    float* P;          // [B, H, k, n]  (transposed: row r holds P[., r] over the queries)
+    float* dS;         // [B, H, k, n]
     float* dQ;         // [B, H, n, 64]
     int B, H, n, k;
     float scale;
@@ -183,8 +194,6 @@ hipError_t launch_linear_bf16(const LinearBf16Args& a, hipStream_t stream);
 hipError_t launch_conv_bf16(const ConvBf16Args& a, hipStream_t stream);
 hipError_t launch_bw_convert(const void* src, int src_bf16, float* dst, size_t count,
                              const int32_t* lengths, int H, int n, int mask, hipStream_t stream);
-hipError_t launch_bw_mask_rows(float* x, size_t count, const int32_t* lengths, int H, int n,
-                               hipStream_t stream);
 hipError_t launch_bw_gemm(const BwGemm& g, hipStream_t stream);
 hipError_t launch_bw_attend(const BwAttendArgs& a, hipStream_t stream);
 
