@@ -396,8 +396,11 @@ void stack_ws(const lf_stack* s, const lf_problem& p, const lf::ProjGeom& g, Sta
 
 int do_linear(const lf::LinearBf16Args& base, hipStream_t stream) {
     lf::LinearBf16Args a = base;
-    const int ttiles = (a.T + lf::kLinearTileT - 1) / lf::kLinearTileT;
-    a.nlogical = (a.F / lf::kLinearTileF) * ttiles;
+    const int ftiles = a.F / lf::kLinearTileF;
+    // 256-token tiles unless that leaves compute units idle (MI355X: 256 CUs); the 128-token
+    // tile runs four waves and two workgroups fit on a CU
+    a.tile_t = ftiles * ((a.T + 255) / 256) < 256 ? 128 : 256;
+    a.nlogical = ftiles * ((a.T + a.tile_t - 1) / a.tile_t);
     return launch_status(lf::launch_linear_bf16(a, stream));
 }
 

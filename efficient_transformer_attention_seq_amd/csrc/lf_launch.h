@@ -152,7 +152,8 @@ struct LinearBf16Args {
     const uint16_t* W;   // [F, K] bf16, row f = output feature f
     const uint16_t* X;   // activations, per act_mode
     uint16_t* Y;         // output, per out_mode
-    int T, F, K;         // tokens (multiple of kLinearTileT), features (of kLinearTileF), K % 32 == 0
+    int T, F, K;         // tokens (a partial last tile reads zeros), features (multiple of
+                         // kLinearTileF), K % 64 == 0
     int n, H;            // tokens per batch item and heads (head-planar layouts)
     int act_mode;        // 0: row-major [T, K]; 1: head-planar [B, H, n, 64] with K = 64 H
     int out_mode;        // 0: row-major [T, F]; 1: head-planar planes [F / dm][B, H, n, 64];
@@ -165,7 +166,8 @@ struct LinearBf16Args {
     uint8_t* Ksc;        //   plane and Yv the Vbar plane
     uint16_t* Yv;
     float c;             // out_mode 2: scale * log2(e)
-    int nlogical;        // (F / kLinearTileF) * (T / kLinearTileT)
+    int tile_t;          // token tile: 256 or 128
+    int nlogical;        // (F / kLinearTileF) * ceil(T / tile_t)
 };
 
 struct DenseBf16Args {
@@ -201,6 +203,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kAttendThreads = 512;
 constexpr int kMaxAttendBatch = 4096;   // batch items the bf16 attention kernel tables in LDS
 constexpr int kDenseQTB = 256;  // queries per dense-attention workgroup
-constexpr int kLinearTileF = 192, kLinearTileT = 256;   // dense projection workgroup tile
+constexpr int kLinearTileF = 192;   // dense projection workgroup tile (features)
 
 }  // namespace lf

@@ -4,7 +4,8 @@
 // projection).
 //
 // GEMM with M = output features (rows of W), N = tokens, reduction over the K input features.
-// Workgroup tile 192 features x 256 tokens; 8 waves as 2 (features) x 4 (tokens), wave tile
+// Workgroup tile 192 features x 256 tokens (8 waves as 2 features x 4 tokens) or x 128 tokens (4
+// waves, 2 x 2, for grids too small to fill the chip); wave tile
 // 96 x 64 = 3 x 2 blocks of v_mfma_f32_32x32x16_bf16 with W as the A operand and the activations
 // as the B operand, so both operands are read K-contiguous, 8 bf16 per lane, from LDS and each
 // accumulator lane ends with runs of 4 consecutive features of one token.
@@ -28,19 +29,25 @@
 namespace lf {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kBF = kLinearTileF, kBT = kLinearTileT;   // 192 x 256
+constexpr int kBF = kLinearTileF;                       // 192 features per tile
 constexpr int kBK = 64;                                 // K per stage
 constexpr int kNS = 2;                                  // stages (double buffer)
 constexpr int kRowB = kBK * 2;                          // 128-byte LDS rows
 constexpr int kTileW = kBF * kRowB;                     // 24 KB
-constexpr int kTileX = kBT * kRowB;                     // 32 KB
-constexpr int kStage = kTileW + kTileX;                 // 56 KB
-constexpr int kDmaW = kTileW / 1024, kDmaX = kTileX / 1024;   // 24 + 32 instructions per stage
-constexpr int kDma = kDmaW + kDmaX;                     // 7 per wave
-static_assert(kDma % 8 == 0, "every wave issues the same number of loads");
 constexpr int kStgRow = 96 * 2 + 16;                    // epilogue staging row (bytes)
-static_assert(8 * 64 * kStgRow <= kNS * kStage, "staging fits in the ring");
+
+// Token tile BT = 256 (8 waves, 2 x 4) or 128 (4 waves, 2 x 2); the wave tile is 96 x 64 either way.
+template <int BT>
+struct LinTile {
+    static constexpr int kWaves = BT / 32;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kTileX = BT * kRowB;                 // 32 or 16 KB
+    static constexpr int kStage = kTileW + kTileX;
+    static constexpr int kDmaW = kTileW / 1024, kDmaX = kTileX / 1024;
+    static constexpr int kPer = (kDmaW + kDmaX) / kWaves;     // 7 or 10 per wave
+    static_assert((kDmaW + kDmaX) % kWaves == 0, "every wave issues the same number of loads");
+    static_assert(kWaves * 64 * kStgRow <= kNS * kStage, "staging fits in the ring");
+};
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -74,7 +81,12 @@ template <int N>
 __device__ __forceinline__ void vmcnt_le() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-__global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearBf16Args a) {
+template <int BT>
+__global__ __launch_bounds__(LinTile<BT>::kThreads) void linear_bf16_kernel(LinearBf16Args a) {
+    using Tl = LinTile<BT>;
+    constexpr int kWaves = Tl::kWaves, kTileX = Tl::kTileX, kStage = Tl::kStage;
+    constexpr int kDmaW = Tl::kDmaW, kPer = Tl::kPer;
+    constexpr int kBT = BT;
     __shared__ __attribute__((aligned(16))) uint8_t smem[kNS * kStage];
     const int lid = xcd_remap(blockIdx.x, a.nlogical);
     if (lid < 0) return;
@@ -90,16 +102,15 @@ __global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearBf16Args a)
     const uint32_t lds0 = lds_addr(smem);
     const int nsteps = a.K / kBK;   // K % 64 == 0
 
-    // ---- this wave's DMA instructions of a stage: I = wave + 8 j (j < 7); I < kDmaW covers the W
-    // rows 8 I .. 8 I + 7, the others the token rows 8 (I - kDmaW) ..; lane -> row lane / 8, LDS
-    // chunk lane % 8, which holds global chunk (lane % 8) ^ swz(row)
-    constexpr int kPer = kDma / 8;
+    // ---- this wave's DMA instructions of a stage: I = wave + kWaves j (j < kPer); I < kDmaW
+    // covers the W rows 8 I .. 8 I + 7, the others the token rows 8 (I - kDmaW) ..; lane -> row
+    // lane / 8, LDS chunk lane % 8, which holds global chunk (lane % 8) ^ swz(row)
     const i32x4 rw = make_rsrc(a.W, (uint32_t)((size_t)a.F * a.K * 2));
     const i32x4 rx = make_rsrc(a.X, (uint32_t)((size_t)a.T * a.K * 2));
     uint32_t base_off[kPer];   // per instruction: byte offset of this lane's 16 bytes at k = 0
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        const int I = wave + 8 * j;
+        const int I = wave + kWaves * j;
         const int r = (I < kDmaW ? I : I - kDmaW) * 8 + (lane >> 3);
         const int gch = (lane & 7) ^ swz(r);
         uint32_t off;
@@ -127,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearBf16Args a)
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             if (j % 4 != part) continue;
-            const int I = wave + 8 * j;
+            const int I = wave + kWaves * j;
             if (I < kDmaW) dma16(rw, sb + I * 1024, base_off[j] + (uint32_t)(k0 * 2));
             else dma16(rx, sb + kTileW + (I - kDmaW) * 1024, base_off[j] + xk);
         }
@@ -282,7 +293,14 @@ __global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearBf16Args a)
 
 hipError_t launch_linear_bf16(const LinearBf16Args& a, hipStream_t stream) {
     const int grid = ((a.nlogical + 7) / 8) * 8;
-    hipLaunchKernelGGL(linear_bf16_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+    if (a.tile_t == 128)
+        hipLaunchKernelGGL(linear_bf16_kernel<128>, dim3(grid), dim3(LinTile<128>::kThreads), 0,
+                           stream, a);
+    else if (a.tile_t == 256)
+        hipLaunchKernelGGL(linear_bf16_kernel<256>, dim3(grid), dim3(LinTile<256>::kThreads), 0,
+                           stream, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
