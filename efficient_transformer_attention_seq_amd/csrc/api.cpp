@@ -290,22 +290,14 @@ int do_conv(const lf_problem* p, const void* K, const void* V, const void* wE, c
 
 // ---- backward pass
 struct BwWs {
-    size_t q, k, v, g, e, f, kb, vb, p, ds, dkb, dvb, part, total;   // byte offsets
+    size_t kb, vb, p, ds, dkb, dvb, part, total;   // byte offsets
 };
 
-void bw_ws(const lf_problem* p, bool separate, BwWs* w) {
-    const size_t act = (size_t)p->batch * p->heads * p->n * 64 * 4;
-    const size_t mat = (size_t)(p->share == LF_SHARE_NONE ? p->heads : 1) * p->k * p->n * 4;
+void bw_ws(const lf_problem* p, BwWs* w) {
     const size_t kv = (size_t)p->batch * p->heads * p->k * 64 * 4;
     const size_t pk = (size_t)p->batch * p->heads * p->n * p->k * 4;
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o += round_up(bytes, 256); return at; };
-    w->q = take(act);
-    w->k = take(act);
-    w->v = take(act);
-    w->g = take(act);
-    w->e = take(mat);
-    w->f = separate ? take(mat) : w->e;
     w->kb = take(kv);
     w->vb = take(kv);
     w->p = take(pk);
@@ -726,7 +718,7 @@ int linformer_backward_workspace_size(const lf_problem* p, size_t* bytes) {
     if (st) return st;
     if (!bytes) return LF_ERR_NULL;
     BwWs w;
-    bw_ws(p, p->share == LF_SHARE_NONE || p->share == LF_SHARE_HEADWISE, &w);   // the larger
+    bw_ws(p, &w);
     *bytes = w.total;
     return LF_OK;
 }
@@ -749,7 +741,7 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
         return LF_ERR_ALIGN;
     if (lengths && ((uintptr_t)lengths & 3u)) return LF_ERR_ALIGN;
     BwWs w;
-    bw_ws(p, separate, &w);
+    bw_ws(p, &w);
     size_t need = 0;
     linformer_backward_workspace_size(p, &need);
     if (ws_bytes < need) return LF_ERR_WORKSPACE;
@@ -765,8 +757,6 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
 
     hipStream_t strm = (hipStream_t)stream;
     uint8_t* b = (uint8_t*)ws;
-    float *Qf = (float*)(b + w.q), *Kf = (float*)(b + w.k), *Vf = (float*)(b + w.v);
-    float *Gf = (float*)(b + w.g), *Ef = (float*)(b + w.e), *Ff = (float*)(b + w.f);
     float *Kb = (float*)(b + w.kb), *Vb = (float*)(b + w.vb), *P = (float*)(b + w.p);
     float *dS = (float*)(b + w.ds), *dKb = (float*)(b + w.dkb), *dVb = (float*)(b + w.dvb);
     float* part = (float*)(b + w.part);
@@ -775,56 +765,59 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
         g.part = part;
         return lf::launch_bw_gemm(g, strm);
     };
+    // Q, K, V, E, F and dO are read in their own dtype; rows of K, V and dO at or past a length are
+    // never read (the reductions over positions stop there, or read them as zero)
     const int bf = p->dtype == LF_BF16 ? 1 : 0;
     const int B = p->batch, H = p->heads, n = p->n, k = p->k;
-    const size_t cnt = (size_t)B * H * n * 64;
-    const size_t mcnt = (size_t)(p->share == LF_SHARE_NONE ? H : 1) * k * n;
     const float s = eff_scale(p);
     const bool unshared = p->share == LF_SHARE_NONE;
-    hipError_t e = lf::launch_bw_convert(Q, bf, Qf, cnt, lengths, H, n, 0, strm);
-    if (e == hipSuccess) e = lf::launch_bw_convert(K, bf, Kf, cnt, lengths, H, n, 1, strm);
-    if (e == hipSuccess) e = lf::launch_bw_convert(V, bf, Vf, cnt, lengths, H, n, 1, strm);
-    if (e == hipSuccess) e = lf::launch_bw_convert(dO, bf, Gf, cnt, lengths, H, n, 1, strm);
-    if (e == hipSuccess) e = lf::launch_bw_convert(E, bf, Ef, mcnt, nullptr, 1, 1, 0, strm);
-    if (e == hipSuccess && separate) e = lf::launch_bw_convert(Fr, bf, Ff, mcnt, nullptr, 1, 1, 0, strm);
-    if (e != hipSuccess) return LF_ERR_LAUNCH;
+    hipError_t e = hipSuccess;
     const long long hn64 = (long long)n * 64, hk64 = (long long)k * 64, kn = (long long)k * n;
-    // Kbar = E_h K, Vbar = F_h V: z = (b, h), M = k, N = 64, reduction over n
-    auto project = [&](const float* A, const float* X, float* out) {
+    // Kbar = E_h K, Vbar = F_h V: z = (b, h), M = k, N = 64, reduction over the positions before
+    // the length (K, V rows past it are zero)
+    auto project = [&](const void* A, const void* X, float* out) {
         lf::BwGemm g = gemm0();
-        g.A = A; g.B = X; g.C = out;
+        g.A = A; g.B = X; g.C = out; g.a_bf16 = g.b_bf16 = bf;
         g.M = k; g.N = 64; g.K = n; g.Z = B * H; g.zdiv = H; g.kblk = n;
+        g.k_len = lengths;
         g.a_z2 = unshared ? kn : 0; g.a_i = n; g.a_kc = 1;
         g.b_z1 = H * hn64; g.b_z2 = hn64; g.b_kc = 64; g.b_j = 1;
         g.c_z1 = H * hk64; g.c_z2 = hk64; g.c_i = 64; g.c_j = 1;
         return run_gemm(g);
     };
-    e = project(Ef, Kf, Kb);
-    if (e == hipSuccess) e = project(Ff, Vf, Vb);
+    e = project(E, K, Kb);
+    if (e == hipSuccess) e = project(Fr, V, Vb);
     if (e != hipSuccess) return LF_ERR_LAUNCH;
     lf::BwAttendArgs at{};
-    at.Q = Qf; at.dO = Gf; at.Kb = Kb; at.Vb = Vb; at.P = P; at.dS = dS; at.dQ = dQ;
-    at.B = B; at.H = H; at.n = n; at.k = k; at.scale = s;
+    at.Q = Q; at.dO = dO; at.in_bf16 = bf; at.Kb = Kb; at.Vb = Vb; at.P = P; at.dS = dS; at.dQ = dQ;
+    at.B = B; at.H = H; at.n = n; at.k = k; at.scale = s; at.lengths = lengths;
+    {   // about three rounds of one workgroup per compute unit (MI355X: 256)
+        const int nblk = (n + 127) / 128;
+        at.qb = std::max(1, std::min(nblk, nblk * B * H / 768));
+    }
     if (lf::launch_bw_attend(at, strm) != hipSuccess) return LF_ERR_LAUNCH;
-    // dVbar = P^T dO, dKbar = s dS^T Q (P, dS stored [B, H, k, n]): z = (b, h), M = k, N = 64,
-    // reduction over the n queries
-    auto reduce_q = [&](const float* A, const float* X, float* out, float alpha) {
+    // dVbar = P^T dO, dKbar = s dS^T Q: z = (b, h), M = k, N = 64, reduction over the queries
+    // before the length (P, dS rows past it are not written; dO and dS vanish there)
+    auto reduce_q = [&](const float* A, const void* X, float* out, float alpha) {
         lf::BwGemm g = gemm0();
-        g.A = A; g.B = X; g.C = out; g.alpha = alpha;
+        g.A = A; g.B = X; g.C = out; g.alpha = alpha; g.b_bf16 = bf;
         g.M = k; g.N = 64; g.K = n; g.Z = B * H; g.zdiv = H; g.kblk = n;
-        g.a_z1 = H * kn; g.a_z2 = kn; g.a_i = n; g.a_kc = 1;
+        g.k_len = lengths;
+        g.a_z1 = H * kn; g.a_z2 = kn; g.a_i = 1; g.a_kc = k;
         g.b_z1 = H * hn64; g.b_z2 = hn64; g.b_kc = 64; g.b_j = 1;
         g.c_z1 = H * hk64; g.c_z2 = hk64; g.c_i = 64; g.c_j = 1;
         return run_gemm(g);
     };
-    e = reduce_q(P, Gf, dVb, 1.0f);
-    if (e == hipSuccess) e = reduce_q(dS, Qf, dKb, s);
+    e = reduce_q(P, dO, dVb, 1.0f);
+    if (e == hipSuccess) e = reduce_q(dS, Q, dKb, s);
     if (e != hipSuccess) return LF_ERR_LAUNCH;
-    // dE (+)= dXbar X^T: M = k, N = n, reduction over (b, c) (unshared: z = h) or over (b, h, c)
-    auto grad_mat = [&](const float* dXb, const float* X, float* out, float beta) {
+    // dE (+)= dXbar X^T: M = k, N = n, reduction over (b, c) (unshared: z = h) or over (b, h, c);
+    // positions at or past item b's length read as zero
+    auto grad_mat = [&](const float* dXb, const void* X, float* out, float beta) {
         lf::BwGemm g = gemm0();
-        g.A = dXb; g.B = X; g.C = out; g.beta = beta;
+        g.A = dXb; g.B = X; g.C = out; g.beta = beta; g.b_bf16 = bf;
         g.M = k; g.N = n; g.kblk = 64;
+        g.bj_len = lengths; g.bj_div = unshared ? 1 : H;
         if (unshared) {
             g.Z = H; g.K = B * 64;
             g.a_z1 = hk64; g.a_kb = H * hk64;
@@ -840,13 +833,13 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
         g.c_i = n; g.c_j = 1;
         return run_gemm(g);
     };
-    e = grad_mat(dKb, Kf, dE, 0.0f);
-    if (e == hipSuccess) e = separate ? grad_mat(dVb, Vf, dF, 0.0f) : grad_mat(dVb, Vf, dE, 1.0f);
+    e = grad_mat(dKb, K, dE, 0.0f);
+    if (e == hipSuccess) e = separate ? grad_mat(dVb, V, dF, 0.0f) : grad_mat(dVb, V, dE, 1.0f);
     if (e != hipSuccess) return LF_ERR_LAUNCH;
     // dK = E_h^T dKbar, dV = F_h^T dVbar: z = (b, h), M = n, N = 64, reduction over k
-    auto back = [&](const float* A, const float* dXb, float* out) {
+    auto back = [&](const void* A, const float* dXb, float* out) {
         lf::BwGemm g = gemm0();
-        g.A = A; g.B = dXb; g.C = out;
+        g.A = A; g.B = dXb; g.C = out; g.a_bf16 = bf;
         g.M = n; g.N = 64; g.K = k; g.Z = B * H; g.zdiv = H; g.kblk = k;
         g.a_z2 = unshared ? kn : 0; g.a_i = 1; g.a_kc = n;
         g.b_z1 = H * hk64; g.b_z2 = hk64; g.b_kc = 64; g.b_j = 1;
@@ -854,8 +847,8 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
         g.row_len = lengths;   // positions past the length get zero gradients
         return run_gemm(g);
     };
-    e = back(Ef, dKb, dK);
-    if (e == hipSuccess) e = back(Ff, dVb, dV);
+    e = back(E, dKb, dK);
+    if (e == hipSuccess) e = back(Fr, dVb, dV);
     return launch_status(e);
 }
 

@@ -1,6 +1,6 @@
 // Backward pass of one Linformer layer for learned projections, in fp32 arithmetic (Linformer
 // card, 方法适配: E and F are learned, so training needs the gradients with respect to Q, K, V, E
-// and F).  Per (b, h), with the keys, values and dO rows past the length zeroed beforehand (those
+// and F).  Per (b, h), with the keys, values and dO rows past the length taken as zero (those
 // positions contribute nothing, and rows of O past the length are fixed at zero):
 //   Kbar = E K, Vbar = F V (recomputed),  P = softmax(s Q Kbar^T)
 //   dP = dO Vbar^T,  dS = P o (dP - rowsum(P o dP)),  dQ = s dS Kbar        (bw_attend_kernel)
@@ -8,40 +8,13 @@
 //   dE += dKbar K^T, dK = E^T dKbar, dF += dVbar V^T, dV = F^T dVbar         (bw_gemm_kernel)
 // Every contraction runs on the fp32 matrix cores: one strided, batched GEMM (split along the
 // reduction when its output is too small to fill the chip) and a fused kernel for P, the softmax
-// Jacobian and dQ with Kbar and Vbar resident in LDS.
+// Jacobian and dQ with Kbar and Vbar resident in LDS.  Both read the inputs in their own dtype
+// (bf16 values widen exactly to fp32 as they are staged) and never read the masked rows.
 #include "lf_device.h"
 #include "lf_launch.h"
 
 namespace lf {
 namespace {
-
-// ---- inputs to fp32, eight elements per thread; with `mask`, rows ([B, H, n, 64]) at or past
-// their item's length are written as zero
-__global__ __launch_bounds__(256) void bw_convert_kernel(const void* src, int src_bf16, float* dst,
-                                                        size_t count8, const int32_t* lengths,
-                                                        int H, int n, int mask) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= count8) return;
-    f32x4 lo, hi;
-    if (src_bf16) {
-        const u32x4 u = ((const u32x4*)src)[i];
-        lo = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                   __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
-        hi = f32x4{__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xFFFF0000u),
-                   __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xFFFF0000u)};
-    } else {
-        lo = ((const f32x4*)src)[2 * i];
-        hi = ((const f32x4*)src)[2 * i + 1];
-    }
-    if (mask) {
-        const uint32_t row = (uint32_t)(i >> 3);   // < 2^25 rows
-        const int t = (int)(row % (uint32_t)n);
-        const int b = (int)(row / ((uint32_t)n * (uint32_t)H));
-        if (t >= clamp_len(lengths, b, n)) lo = hi = f32x4{};
-    }
-    ((f32x4*)dst)[2 * i] = lo;
-    ((f32x4*)dst)[2 * i + 1] = hi;
-}
 
 // ---- C = alpha A B + beta C over a batch z, operands addressed through strides (BwGemm in
 // lf_launch.h), on the fp32 matrix cores (v_mfma_f32_32x32x2_f32).  Workgroup tile 128 x TN
@@ -51,6 +24,7 @@ __global__ __launch_bounds__(256) void bw_convert_kernel(const void* src, int sr
 // the operand's contiguous direction (the reduction index when its stride is 1, else the row or
 // column index), so global reads coalesce either way.
 constexpr int kGM = 128, kGK = 32, kGPad = 1;
+// Strides and bases must keep every 16-byte vector aligned: launch_bw_gemm checks them.
 
 __device__ __forceinline__ f32x16 mfma_f32_32(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -59,10 +33,93 @@ __device__ __forceinline__ f32x4 mfma_f32_16(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int NI>
+// 16 raw bytes (4 fp32 or 8 bf16) <-> fp32 values; the loads keep the raw bytes so that no
+// conversion forces an early wait on them
+__device__ __forceinline__ void unpack(const u32x4& w, float* v, float) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(w[e]);
+}
+__device__ __forceinline__ void unpack(const u32x4& w, float* v, uint16_t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+}
+// raw bits of element e of a vector
+__device__ __forceinline__ void put_raw(u32x4& w, int e, const float* p) { w[e] = *(const uint32_t*)p; }
+__device__ __forceinline__ void put_raw(u32x4& w, int e, const uint16_t* p) {
+    w[e >> 1] |= (uint32_t)*p << (16 * (e & 1));
+}
+
+// One operand's 32 x TX tile (reduction index kk < 32, row / column x < TX) per step, read in
+// 16-byte vectors along the operand's contiguous direction (kk when its stride is 1, else x) and
+// staged into LDS as [kk][x].  Vector v of this thread starts at (kk0 + v dkk, x0 + v dx).
+template <typename T, int TX, bool kf>   // kf: vectors along kk (its stride is 1), else along x
+struct TileLoader {
+    static constexpr int VEC = 16 / sizeof(T);
+    static constexpr int NV = kGK * TX / (256 * VEC);
+    int kk0, dkk, x0, dx;
+    long long sx, sk, off, st;   // element strides along x and kk; this thread's offsets
+    u32x4 raw[NV];
+    __device__ void init(int tid, long long stride_x, long long stride_k) {
+        sx = stride_x;
+        sk = stride_k;
+        if constexpr (kf) {
+            constexpr int per = kGK / VEC;   // vectors along one row
+            kk0 = (tid % per) * VEC; dkk = 0;
+            x0 = tid / per; dx = 256 / per;
+        } else {
+            constexpr int per = TX / VEC;
+            x0 = (tid % per) * VEC; dx = 0;
+            kk0 = tid / per; dkk = 256 / per;
+        }
+        off = (long long)x0 * sx + (long long)kk0 * sk;
+        st = (long long)dx * sx + (long long)dkk * sk;
+    }
+    // p: element (kk = 0, x = 0) of this step; elements with kk >= kn or x >= xn read as zero
+    __device__ void fetch(const T* p, int kn, int xn) {
+        if (kn >= kGK && xn >= TX) {   // the whole tile (uniform across the workgroup)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) raw[v] = *(const u32x4*)(p + off + v * st);
+            return;
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int kk = kk0 + v * dkk, x = x0 + v * dx;
+            const T* q = p + off + v * st;
+            constexpr bool k_vec = kf;
+            const bool full = k_vec ? (x < xn && kk + VEC <= kn) : (kk < kn && x + VEC <= xn);
+            if (full) {
+                raw[v] = *(const u32x4*)q;
+            } else {
+                raw[v] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    if (k_vec ? (x < xn && kk + e < kn) : (kk < kn && x + e < xn)) put_raw(raw[v], e, q + e);
+            }
+        }
+    }
+    template <int LD>
+    __device__ void stage(float (*S)[LD]) const {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int kk = kk0 + v * dkk, x = x0 + v * dx;
+            float d[VEC];
+            unpack(raw[v], d, T{});
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                if constexpr (kf) S[kk + e][x] = d[e];
+                else S[kk][x + e] = d[e];
+            }
+        }
+    }
+};
+
+// TA, TB: float or uint16_t (bf16) operands; AKF, BKF: the operand's reduction stride is 1
+template <int NI, typename TA, bool AKF, typename TB, bool BKF>
 __global__ __launch_bounds__(256) void bw_gemm_kernel(BwGemm g) {
     constexpr int TN = 64 * NI;
-    constexpr int AE = kGK * kGM / 256, BE = kGK * TN / 256;   // elements per thread and step
     __shared__ float As[kGK][kGM + kGPad];
     __shared__ float Bs[kGK][TN + kGPad];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -70,36 +127,24 @@ __global__ __launch_bounds__(256) void bw_gemm_kernel(BwGemm g) {
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * (TN / 2);
     const int i0 = blockIdx.y * kGM, j0 = blockIdx.x * TN;
     const int z = blockIdx.z / g.splits, sp = blockIdx.z % g.splits;
-    const int kbeg = sp * g.kchunk, kend = min(g.K, kbeg + g.kchunk);
     const long long z1 = z / g.zdiv, z2 = z % g.zdiv;
-    const float* A = g.A + z1 * g.a_z1 + z2 * g.a_z2;
-    const float* Bm = g.B + z1 * g.b_z1 + z2 * g.b_z2;
-    // element it of this thread: reduction index kk0 + it dkk, row / column x0 + it dx
-    const bool akf = g.a_kc == 1, bkf = g.b_kc == 1;
-    const int a_kk0 = akf ? tid % kGK : tid / kGM, a_dkk = akf ? 0 : 256 / kGM;
-    const int a_x0 = akf ? tid / kGK : tid % kGM, a_dx = akf ? 256 / kGK : 0;
-    const int b_kk0 = bkf ? tid % kGK : tid / TN, b_dkk = bkf ? 0 : 256 / TN;
-    const int b_x0 = bkf ? tid / kGK : tid % TN, b_dx = bkf ? 256 / kGK : 0;
-    const long long a_off = (long long)a_x0 * g.a_i + (long long)a_kk0 * g.a_kc;
-    const long long b_off = (long long)b_x0 * g.b_j + (long long)b_kk0 * g.b_kc;
-    const long long a_st = (long long)a_dx * g.a_i + (long long)a_dkk * g.a_kc;   // uniform
-    const long long b_st = (long long)b_dx * g.b_j + (long long)b_dkk * g.b_kc;
-    float ra[AE], rb[BE];
+    const int row_end = g.row_len ? clamp_len(g.row_len, (int)z1, g.M) : g.M;
+    const int kbeg = sp * g.kchunk;
+    int kend = min(g.K, kbeg + g.kchunk);
+    if (g.k_len) kend = min(kend, clamp_len(g.k_len, (int)z1, g.K));   // terms past it are zero
+    if (i0 >= row_end) kend = kbeg;                                      // rows written as zero
+    const TA* A = (const TA*)g.A + z1 * g.a_z1 + z2 * g.a_z2 + (long long)i0 * g.a_i;
+    const TB* Bm = (const TB*)g.B + z1 * g.b_z1 + z2 * g.b_z2 + (long long)j0 * g.b_j;
+    TileLoader<TA, kGM, AKF> la;
+    TileLoader<TB, TN, BKF> lb;
+    la.init(tid, g.a_i, g.a_kc);
+    lb.init(tid, g.b_j, g.b_kc);
     auto fetch = [&](int k0) {
-        const float* pa = A + (long long)(k0 / g.kblk) * g.a_kb + (long long)(k0 % g.kblk) * g.a_kc +
-                          (long long)i0 * g.a_i + a_off;
-        const float* pb = Bm + (long long)(k0 / g.kblk) * g.b_kb + (long long)(k0 % g.kblk) * g.b_kc +
-                          (long long)j0 * g.b_j + b_off;
-#pragma unroll
-        for (int it = 0; it < AE; ++it) {
-            const int kk = a_kk0 + it * a_dkk, x = a_x0 + it * a_dx;
-            ra[it] = (k0 + kk < kend && i0 + x < g.M) ? pa[it * a_st] : 0.0f;
-        }
-#pragma unroll
-        for (int it = 0; it < BE; ++it) {
-            const int kk = b_kk0 + it * b_dkk, x = b_x0 + it * b_dx;
-            rb[it] = (k0 + kk < kend && j0 + x < g.N) ? pb[it * b_st] : 0.0f;
-        }
+        const long long kb = k0 / g.kblk, kc = k0 % g.kblk;
+        // columns of B at or past the length of the reduction block's item read as zero
+        const int jend = g.bj_len ? clamp_len(g.bj_len, (int)(kb / g.bj_div), g.N) : g.N;
+        la.fetch(A + kb * g.a_kb + kc * g.a_kc, kend - k0, g.M - i0);
+        lb.fetch(Bm + kb * g.b_kb + kc * g.b_kc, kend - k0, jend - j0);
     };
     f32x16 acc[2][NI];
 #pragma unroll
@@ -108,29 +153,33 @@ __global__ __launch_bounds__(256) void bw_gemm_kernel(BwGemm g) {
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
     if (kbeg < kend) fetch(kbeg);
     for (int k0 = kbeg; k0 < kend; k0 += kGK) {
-#pragma unroll
-        for (int it = 0; it < AE; ++it) As[a_kk0 + it * a_dkk][a_x0 + it * a_dx] = ra[it];
-#pragma unroll
-        for (int it = 0; it < BE; ++it) Bs[b_kk0 + it * b_dkk][b_x0 + it * b_dx] = rb[it];
+        la.stage(As);
+        lb.stage(Bs);
         __syncthreads();
         if (k0 + kGK < kend) fetch(k0 + kGK);
+        // operands of pair kp + 2 are read while the products of pair kp run
+        float av[2][2], bv[2][NI];
+        auto read_ops = [&](int kp, float (&a2)[2], float (&b2)[NI]) {
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) a2[mi] = As[kp + h][wm + 32 * mi + l];
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) b2[ni] = Bs[kp + h][wn + 32 * ni + l];
+        };
+        read_ops(0, av[0], bv[0]);
 #pragma unroll
         for (int kp = 0; kp < kGK; kp += 2) {
-            float av[2], bv[NI];
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi) av[mi] = As[kp + h][wm + 32 * mi + l];
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni) bv[ni] = Bs[kp + h][wn + 32 * ni + l];
+            const int cur = (kp >> 1) & 1;
+            if (kp + 2 < kGK) read_ops(kp + 2, av[cur ^ 1], bv[cur ^ 1]);
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma_f32_32(av[mi], bv[ni], acc[mi][ni]);
+                for (int ni = 0; ni < NI; ++ni)
+                    acc[mi][ni] = mfma_f32_32(av[cur][mi], bv[cur][ni], acc[mi][ni]);
         }
         __syncthreads();
     }
     // C tile element j of lane (h, l): row 8 (j / 4) + 4 h + j % 4, column l
     float* C = g.C + z1 * g.c_z1 + z2 * g.c_z2;
-    const int row_end = g.row_len ? clamp_len(g.row_len, (int)z1, g.M) : g.M;
     float* part = g.splits > 1 ? g.part + ((size_t)sp * g.Z + z) * g.M * g.N : nullptr;
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
@@ -168,20 +217,41 @@ __global__ __launch_bounds__(256) void bw_gemm_reduce_kernel(BwGemm g) {
     *c = (!g.row_len || i < clamp_len(g.row_len, (int)z1, g.M)) ? v : 0.0f;
 }
 
-// ---- per (b, h) and 128 query rows: P and dS (stored transposed, [k, n]) and dQ, on the fp32
-// matrix cores (v_mfma_f32_16x16x4_f32).  Kbar and Vbar sit in LDS (row stride 68 floats).  Each
-// wave owns 16 query rows q0 + l and works on transposed products, so that a lane (g, l) holds
-// the values of query column l:
+// ---- per (b, h) and a range of 128-query blocks: P and dS ([n, k]) and dQ, on the fp32 matrix
+// cores (v_mfma_f32_16x16x4_f32).  Kbar and Vbar sit in LDS (row stride 68 floats) for the whole
+// range.  Each wave owns 16 query rows q0 + l of a block and works on transposed products, so
+// that lane (g, l) holds the values of query l:
 //   S^T = Kbar Q^T, dP^T = Vbar dO^T   (k x 16: lane holds rows r = 16 rb + 4 g + e, e < 4)
 //   softmax and the Jacobian down each column (within the lane, then across the four lanes g)
 //   dQ^T = Kbar^T dS^T                  (64 x 16), its B operand taken straight from the dS^T
 //                                       accumulators by matching the reduction order
 // In the first two products the reduction index c runs over 16 g + t for lane group g, so the
-// lane's B operand is its own query row's slice Q[q][16 g .. 16 g + 15] held in registers.
+// lane's B operand is its own query row's slice Q[q][16 g .. 16 g + 15] held in registers; the
+// next block's slices are loaded into the same registers before this block's dQ products.  A wave whose 16 rows all lie at or past the item's length only writes
+// zero dQ rows: its P and dS rows are left unwritten (the reductions over queries stop at the
+// length) and its gradients are zero.
 constexpr int kKS = 68;   // LDS row stride of Kbar / Vbar (floats)
 constexpr int kAttWaves = 8, kAttRows = 16 * kAttWaves;
 
-template <int KB>   // KB = k / 16 row blocks
+// 16 consecutive elements (16-element aligned) as four f32x4
+__device__ __forceinline__ void load16(const float* p, f32x4 (&v)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *(const f32x4*)(p + 4 * u);
+}
+__device__ __forceinline__ void load16(const uint16_t* p, f32x4 (&v)[4]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const u32x4 w = *(const u32x4*)(p + 8 * h);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t x = w[2 * i], y = w[2 * i + 1];
+            v[2 * h + i] = f32x4{__uint_as_float(x << 16), __uint_as_float(x & 0xFFFF0000u),
+                                 __uint_as_float(y << 16), __uint_as_float(y & 0xFFFF0000u)};
+        }
+    }
+}
+
+template <int KB, typename TQ>   // KB = k / 16 row blocks; TQ: float or uint16_t (bf16) Q, dO
 __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs a) {
     constexpr int K = KB * 16;
     extern __shared__ float lds[];
@@ -190,7 +260,6 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l = lane & 15;
     const int bh = blockIdx.y;
-    const int q0 = blockIdx.x * kAttRows + wave * 16;
     const float* kg = a.Kb + (size_t)bh * K * 64;
     const float* vg = a.Vb + (size_t)bh * K * 64;
     for (int e = tid; e < K * 16; e += 64 * kAttWaves) {   // 16-byte pieces
@@ -198,103 +267,133 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
         *(f32x4*)(kb + r * kKS + 4 * c4) = *(const f32x4*)(kg + 4 * e);
         *(f32x4*)(vb + r * kKS + 4 * c4) = *(const f32x4*)(vg + 4 * e);
     }
-    __syncthreads();
-    if (q0 >= a.n) return;   // no barrier follows
+    __syncthreads();   // the only barrier
+    const int L = clamp_len(a.lengths, bh / a.H, a.n);
     const size_t head = (size_t)bh * a.n * 64;
-    const int q = q0 + l;
+    const float c = a.scale * 1.4426950408889634f;   // scores to base-2 exponents
+    const int nblk = (a.n + kAttRows - 1) / kAttRows;
+    const int blk0 = blockIdx.x * a.qb, blk1 = min(nblk, blk0 + a.qb);
+    // the row's slice [16 g, 16 g + 16) of Q and of dO (zero at or past the length)
+    auto load_rows = [&](int q, f32x4 (&qr)[4], f32x4 (&gr)[4]) {
+        load16((const TQ*)a.Q + head + (size_t)q * 64 + 16 * g, qr);
+        load16((const TQ*)a.dO + head + (size_t)q * 64 + 16 * g, gr);
+        if (q >= L) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) gr[u] = f32x4{};
+        }
+    };
     f32x4 qr[4], gr[4];
+    bool loaded = false;
+    for (int blk = blk0; blk < blk1; ++blk) {
+        const int q0 = blk * kAttRows + wave * 16;
+        if (q0 >= a.n) break;
+        const int q = q0 + l;
+        if (q0 >= L) {   // wholly past the length: zero dQ
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        qr[u] = *(const f32x4*)(a.Q + head + (size_t)q * 64 + 16 * g + 4 * u);
-        gr[u] = *(const f32x4*)(a.dO + head + (size_t)q * 64 + 16 * g + 4 * u);
-    }
-    f32x4 st[KB], dp[KB];
+            for (int cb = 0; cb < 4; ++cb)
+                *(f32x4*)(a.dQ + head + (size_t)q * 64 + 16 * cb + 4 * g) = f32x4{};
+            continue;
+        }
+        if (!loaded) load_rows(q, qr, gr);
+        f32x4 st[KB], dp[KB];
 #pragma unroll
-    for (int r = 0; r < KB; ++r) {
-        st[r] = f32x4{};
-        dp[r] = f32x4{};
-    }
+        for (int r = 0; r < KB; ++r) {
+            st[r] = f32x4{};
+            dp[r] = f32x4{};
+        }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int r = 0; r < KB; r += 2) {
-            const f32x4 k0 = *(const f32x4*)(kb + (16 * r + l) * kKS + 16 * g + 4 * u);
-            const f32x4 k1 = *(const f32x4*)(kb + (16 * r + 16 + l) * kKS + 16 * g + 4 * u);
-            const f32x4 v0 = *(const f32x4*)(vb + (16 * r + l) * kKS + 16 * g + 4 * u);
-            const f32x4 v1 = *(const f32x4*)(vb + (16 * r + 16 + l) * kKS + 16 * g + 4 * u);
+            for (int r = 0; r < KB; r += 2) {
+                const f32x4 k0 = *(const f32x4*)(kb + (16 * r + l) * kKS + 16 * g + 4 * u);
+                const f32x4 k1 = *(const f32x4*)(kb + (16 * r + 16 + l) * kKS + 16 * g + 4 * u);
+                const f32x4 v0 = *(const f32x4*)(vb + (16 * r + l) * kKS + 16 * g + 4 * u);
+                const f32x4 v1 = *(const f32x4*)(vb + (16 * r + 16 + l) * kKS + 16 * g + 4 * u);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                st[r] = mfma_f32_16(k0[t], qr[u][t], st[r]);
-                st[r + 1] = mfma_f32_16(k1[t], qr[u][t], st[r + 1]);
-                dp[r] = mfma_f32_16(v0[t], gr[u][t], dp[r]);
-                dp[r + 1] = mfma_f32_16(v1[t], gr[u][t], dp[r + 1]);
+                for (int t = 0; t < 4; ++t) {
+                    st[r] = mfma_f32_16(k0[t], qr[u][t], st[r]);
+                    st[r + 1] = mfma_f32_16(k1[t], qr[u][t], st[r + 1]);
+                    dp[r] = mfma_f32_16(v0[t], gr[u][t], dp[r]);
+                    dp[r + 1] = mfma_f32_16(v1[t], gr[u][t], dp[r + 1]);
+                }
             }
         }
+        float mx = st[0][0];
+#pragma unroll
+        for (int r = 0; r < KB; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, st[r][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mc = mx * c;
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < KB; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                st[r][e] = __builtin_amdgcn_exp2f(fmaf(st[r][e], c, -mc));
+                sum += st[r][e];
+            }
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        const float inv = 1.0f / sum;
+        float dsum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < KB; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                st[r][e] *= inv;   // P
+                dsum = fmaf(st[r][e], dp[r][e], dsum);
+            }
+        dsum += __shfl_xor(dsum, 16);
+        dsum += __shfl_xor(dsum, 32);
+        float* prow = a.P + ((size_t)bh * a.n + q) * K + 4 * g;
+        float* drow = a.dS + ((size_t)bh * a.n + q) * K + 4 * g;
+#pragma unroll
+        for (int r = 0; r < KB; ++r) {
+            dp[r] = st[r] * (dp[r] - dsum);   // dS
+            *(f32x4*)(prow + 16 * r) = st[r];
+            *(f32x4*)(drow + 16 * r) = dp[r];
+        }
+        // next block's rows into the same registers; they arrive during the dQ products
+        loaded = false;
+        if (blk + 1 < blk1 && q0 + kAttRows < min(a.n, L)) {
+            load_rows(q + kAttRows, qr, gr);
+            loaded = true;
+        }
+        // dQ^T = Kbar^T dS^T: reduction step (r, e) takes row 16 r + 4 g + e in lane group g
+        f32x4 dq[4] = {};
+#pragma unroll
+        for (int r = 0; r < KB; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float* krow = kb + (16 * r + 4 * g + e) * kKS + l;
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) dq[cb] = mfma_f32_16(krow[16 * cb], dp[r][e], dq[cb]);
+            }
+        // dq[cb] element e of lane (g, l): dQ[q][16 cb + 4 g + e]
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+            *(f32x4*)(a.dQ + head + (size_t)q * 64 + 16 * cb + 4 * g) = dq[cb] * a.scale;
     }
-    float mx = st[0][0];
-#pragma unroll
-    for (int r = 0; r < KB; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, st[r][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    float sum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < KB; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            st[r][e] = expf(a.scale * (st[r][e] - mx));
-            sum += st[r][e];
-        }
-    sum += __shfl_xor(sum, 16);
-    sum += __shfl_xor(sum, 32);
-    const float inv = 1.0f / sum;
-    float dsum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < KB; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            st[r][e] *= inv;   // P
-            dsum = fmaf(st[r][e], dp[r][e], dsum);
-        }
-    dsum += __shfl_xor(dsum, 16);
-    dsum += __shfl_xor(dsum, 32);
-    const size_t pcol = (size_t)bh * K * a.n + q;
-#pragma unroll
-    for (int r = 0; r < KB; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const size_t at = pcol + (size_t)(16 * r + 4 * g + e) * a.n;
-            dp[r][e] = st[r][e] * (dp[r][e] - dsum);   // dS
-            a.P[at] = st[r][e];
-            a.dS[at] = dp[r][e];
-        }
-    // dQ^T = Kbar^T dS^T: reduction step (r, e) takes row 16 r + 4 g + e in lane group g
-    f32x4 dq[4] = {};
-#pragma unroll
-    for (int r = 0; r < KB; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float* krow = kb + (16 * r + 4 * g + e) * kKS + l;
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) dq[cb] = mfma_f32_16(krow[16 * cb], dp[r][e], dq[cb]);
-        }
-    // dq[cb] element e of lane (g, l): dQ[q][16 cb + 4 g + e]
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-        *(f32x4*)(a.dQ + head + (size_t)q * 64 + 16 * cb + 4 * g) = dq[cb] * a.scale;
 }
 
 }  // namespace
 
-hipError_t launch_bw_convert(const void* src, int src_bf16, float* dst, size_t count,
-                             const int32_t* lengths, int H, int n, int mask, hipStream_t stream) {
-    if (count % 8) return hipErrorInvalidValue;
-    const size_t count8 = count / 8;
-    const int grid = (int)((count8 + 255) / 256);
-    hipLaunchKernelGGL(bw_convert_kernel, dim3(grid), dim3(256), 0, stream, src, src_bf16, dst,
-                       count8, lengths, H, n, mask);
-    return hipGetLastError();
+// Every 16-byte vector the tile loaders read stays aligned: bases 16-byte aligned, every stride a
+// multiple of the elements per vector.
+static bool vec_aligned(const BwGemm& g) {
+    auto ok = [](long long contiguous, long long other, long long z1, long long z2, long long kb,
+                 long long vec) {
+        return contiguous == 1 && other % vec == 0 && z1 % vec == 0 && z2 % vec == 0 &&
+               kb % vec == 0;
+    };
+    const long long va = g.a_bf16 ? 8 : 4, vb = g.b_bf16 ? 8 : 4;
+    const bool a = g.a_kc == 1 ? ok(g.a_kc, g.a_i, g.a_z1, g.a_z2, g.a_kb, va)
+                               : ok(g.a_i, g.a_kc, g.a_z1, g.a_z2, g.a_kb, va);
+    const bool b = g.b_kc == 1 ? ok(g.b_kc, g.b_j, g.b_z1, g.b_z2, g.b_kb, vb)
+                               : ok(g.b_j, g.b_kc, g.b_z1, g.b_z2, g.b_kb, vb);
+    return a && b && ((uintptr_t)g.A & 15) == 0 && ((uintptr_t)g.B & 15) == 0;
 }
 
 void bw_gemm_plan(BwGemm& g) {
@@ -316,14 +415,34 @@ size_t bw_gemm_part_bytes(int M, int N, int K, int Z) {
 
 hipError_t launch_bw_gemm(const BwGemm& g, hipStream_t stream) {
     if (g.kblk % kGK || g.splits < 1 || g.kchunk % kGK || (g.splits > 1 && !g.part) ||
+        (g.bj_len && g.bj_div < 1) || !vec_aligned(g) ||
         (long long)g.Z * g.splits > 65535 || (g.M + kGM - 1) / kGM > 65535)
         return hipErrorInvalidValue;
     const dim3 grid(g.N <= 64 ? (g.N + 63) / 64 : (g.N + 127) / 128, (g.M + kGM - 1) / kGM,
                     g.Z * g.splits);
-    if (g.N <= 64)
-        hipLaunchKernelGGL(bw_gemm_kernel<1>, grid, dim3(256), 0, stream, g);
-    else
-        hipLaunchKernelGGL(bw_gemm_kernel<2>, grid, dim3(256), 0, stream, g);
+    const int v = (g.N <= 64 ? 0 : 16) + (g.a_bf16 ? 8 : 0) + (g.a_kc == 1 ? 4 : 0) +
+                  (g.b_bf16 ? 2 : 0) + (g.b_kc == 1 ? 1 : 0);
+    switch (v) {
+#define LF_BW_GEMM(V, NI, TA, AKF, TB, BKF)                                                     \
+    case V:                                                                                     \
+        hipLaunchKernelGGL((bw_gemm_kernel<NI, TA, AKF, TB, BKF>), grid, dim3(256), 0, stream, g); \
+        break;
+#define LF_BW_GEMM_B(V, NI, TA, AKF)                 \
+    LF_BW_GEMM(V + 0, NI, TA, AKF, float, false)     \
+    LF_BW_GEMM(V + 1, NI, TA, AKF, float, true)      \
+    LF_BW_GEMM(V + 2, NI, TA, AKF, uint16_t, false)  \
+    LF_BW_GEMM(V + 3, NI, TA, AKF, uint16_t, true)
+        LF_BW_GEMM_B(0, 1, float, false)
+        LF_BW_GEMM_B(4, 1, float, true)
+        LF_BW_GEMM_B(8, 1, uint16_t, false)
+        LF_BW_GEMM_B(12, 1, uint16_t, true)
+        LF_BW_GEMM_B(16, 2, float, false)
+        LF_BW_GEMM_B(20, 2, float, true)
+        LF_BW_GEMM_B(24, 2, uint16_t, false)
+        LF_BW_GEMM_B(28, 2, uint16_t, true)
+#undef LF_BW_GEMM_B
+#undef LF_BW_GEMM
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.splits == 1) return e;
     const size_t total = (size_t)g.Z * g.M * g.N;
@@ -332,31 +451,37 @@ hipError_t launch_bw_gemm(const BwGemm& g, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int KB>
+template <int KB, typename TQ>
 static hipError_t launch_attend_kb(const BwAttendArgs& a, hipStream_t stream) {
     const size_t lds = (size_t)2 * KB * 16 * kKS * sizeof(float);
-    auto kern = bw_attend_kernel<KB>;
+    auto kern = bw_attend_kernel<KB, TQ>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((a.n + kAttRows - 1) / kAttRows, a.B * a.H),
-                       dim3(64 * kAttWaves), lds, stream, a);
+    const int nblk = (a.n + kAttRows - 1) / kAttRows;
+    hipLaunchKernelGGL(kern, dim3((nblk + a.qb - 1) / a.qb, a.B * a.H), dim3(64 * kAttWaves), lds,
+                       stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_bw_attend(const BwAttendArgs& a, hipStream_t stream) {
-    if (a.n % 16 || a.B * a.H > 65535) return hipErrorInvalidValue;
+template <typename TQ>
+static hipError_t launch_attend_t(const BwAttendArgs& a, hipStream_t stream) {
     switch (a.k / 32) {   // k % 32 == 0, 32 .. 256
-        case 1: return launch_attend_kb<2>(a, stream);
-        case 2: return launch_attend_kb<4>(a, stream);
-        case 3: return launch_attend_kb<6>(a, stream);
-        case 4: return launch_attend_kb<8>(a, stream);
-        case 5: return launch_attend_kb<10>(a, stream);
-        case 6: return launch_attend_kb<12>(a, stream);
-        case 7: return launch_attend_kb<14>(a, stream);
-        case 8: return launch_attend_kb<16>(a, stream);
+        case 1: return launch_attend_kb<2, TQ>(a, stream);
+        case 2: return launch_attend_kb<4, TQ>(a, stream);
+        case 3: return launch_attend_kb<6, TQ>(a, stream);
+        case 4: return launch_attend_kb<8, TQ>(a, stream);
+        case 5: return launch_attend_kb<10, TQ>(a, stream);
+        case 6: return launch_attend_kb<12, TQ>(a, stream);
+        case 7: return launch_attend_kb<14, TQ>(a, stream);
+        case 8: return launch_attend_kb<16, TQ>(a, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_bw_attend(const BwAttendArgs& a, hipStream_t stream) {
+    if (a.n % 16 || a.B * a.H > 65535 || a.qb < 1) return hipErrorInvalidValue;
+    return a.in_bf16 ? launch_attend_t<uint16_t>(a, stream) : launch_attend_t<float>(a, stream);
 }
 
 }  // namespace lf

@@ -117,17 +117,22 @@ struct ConvBf16Args {
 // (set by bw_gemm_plan); each chunk then writes its partial sums to `part` ([splits][Z][M][N]
 // fp32, bw_gemm_part_bytes) and a second kernel adds them in chunk order.
 struct BwGemm {
-    const float* A;
-    const float* B;
+    const void* A;     // fp32, or bf16 with a_bf16
+    const void* B;     // fp32, or bf16 with b_bf16
     float* C;
     int M, N, K, Z, zdiv, kblk;
-    long long a_z1, a_z2, a_i, a_kb, a_kc;
+    long long a_z1, a_z2, a_i, a_kb, a_kc;   // strides in elements
     long long b_z1, b_z2, b_kb, b_kc, b_j;
     long long c_z1, c_z2, c_i, c_j;
     float alpha, beta;
     int splits, kchunk;
     float* part;
     const int32_t* row_len;   // optional: rows i >= row_len[z1] of C are written as zero
+    const int32_t* k_len;     // optional: the reduction stops at kk < k_len[z1] (the terms past
+                              // it are known to be zero, or their operands unwritten)
+    const int32_t* bj_len;    // optional: B(z, kk, j) reads as zero for j >= bj_len[kb / bj_div]
+    int bj_div;
+    int a_bf16, b_bf16;
 };
 
 // Chooses splits / kchunk for g's shape (enough workgroups to cover the chip).
@@ -136,14 +141,17 @@ void bw_gemm_plan(BwGemm& g);
 size_t bw_gemm_part_bytes(int M, int N, int K, int Z);
 
 struct BwAttendArgs {
-    const float* Q;    // [B, H, n, 64]
-    const float* dO;   // [B, H, n, 64], rows past the lengths zero
+    const void* Q;     // [B, H, n, 64], fp32 or (in_bf16) bf16
+    const void* dO;    // [B, H, n, 64]; rows at or past the length read as zero
     const float* Kb;   // [B, H, k, 64]
     const float* Vb;
-    float* P;          // [B, H, k, n]  (transposed: row r holds P[., r] over the queries)
-    float* dS;         // [B, H, k, n]
+    const int32_t* lengths;   // optional per-item lengths
+    float* P;          // [B, H, n, k]; rows of 16-query groups wholly past the length unwritten
+    float* dS;         // [B, H, n, k]
     float* dQ;         // [B, H, n, 64]
     int B, H, n, k;
+    int qb;            // 128-query blocks per workgroup
+    int in_bf16;
     float scale;
 };
 
@@ -194,8 +202,6 @@ hipError_t launch_attend_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_dense_bf16(const DenseBf16Args& a, hipStream_t stream);
 hipError_t launch_linear_bf16(const LinearBf16Args& a, hipStream_t stream);
 hipError_t launch_conv_bf16(const ConvBf16Args& a, hipStream_t stream);
-hipError_t launch_bw_convert(const void* src, int src_bf16, float* dst, size_t count,
-                             const int32_t* lengths, int H, int n, int mask, hipStream_t stream);
 hipError_t launch_bw_gemm(const BwGemm& g, hipStream_t stream);
 hipError_t launch_bw_attend(const BwAttendArgs& a, hipStream_t stream);
 

@@ -69,3 +69,28 @@ def test_backward_unshared_same_f_as_e():
     ref = orc.backward(inp.Q, inp.K, inp.V, inp.E, None, NONE, dO, inp.lengths)
     assert got[4] is None and ref[4] is None
     assert _mat_err(got[3], ref[3]) <= TOL and orc.slice_rel_err(got[1], ref[1]) <= TOL
+
+
+@pytest.mark.parametrize("dtype,share", [(BF, NONE), (F32, LAYER)])
+def test_backward_ignores_padded_rows(dtype, share):
+    """Rows of K, V and dO at or past an item's length are not part of the problem: filled with
+    other values they change nothing (the oracle ignores them by construction)."""
+    B, H, n, k, lengths = 2, 2, 320, 64, [200, 77]
+    inp = synth.random_inputs(B, H, n, 64, k, dtype, share, seed=11, lengths=lengths)
+    rng = np.random.default_rng(12)
+    dO = rng.standard_normal((B, H, n, 64))
+    Q, K, V = inp.Q.copy(), inp.K.copy(), inp.V.copy()
+    for b, L in enumerate(lengths):
+        for x in (Q, K, V, dO):
+            x[b, :, L:] = 3.0 * rng.standard_normal(x[b, :, L:].shape)
+    Q, K, V, dO = (synth.to_dtype(x, dtype) for x in (Q, K, V, dO))
+    inp = synth.Inputs(inp.wl, Q, K, V, inp.E, inp.F, inp.lengths)
+    got = G.run_backward(inp, dO)
+    ref = orc.backward(Q, K, V, inp.E, inp.F, share, dO, inp.lengths)
+    for name, g, r in zip(("dQ", "dK", "dV", "dE", "dF"), got, ref):
+        if r is None:
+            continue
+        e = orc.slice_rel_err(g, r) if name in ("dQ", "dK", "dV") else _mat_err(g, r)
+        assert e <= TOL, (name, e)
+    for b, L in enumerate(lengths):
+        assert np.all(got[0][b, :, L:] == 0) and np.all(got[1][b, :, L:] == 0)
