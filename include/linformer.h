@@ -165,12 +165,12 @@ int linformer_forward_conv(const lf_problem* p, const void* Q, const void* K, co
  *   dVbar = P^T dO, dP = dO Vbar^T, dS = P o (dP - rowsum(P o dP)),
  *   dQ = s dS Kbar, dKbar = s dS^T Q, dE = dKbar K^T, dK = E^T dKbar, dF = dVbar V^T, dV = F^T dVbar
  * per (b, h); shared matrices collect every head that uses them.  Padding as in the forward:
- * rows of dO past the length have no effect, and the gradients of K, V rows and of the E, F
- * columns past the length are zero.  Inputs in p->dtype and the forward layouts; gradients fp32:
+ * rows of K, V and dO past the length are not read (they have no effect), and the gradients of
+ * K, V rows and of the E, F columns past the length are zero.  Inputs in p->dtype and the forward layouts; gradients fp32:
  * dQ, dK, dV [B, H, n, d]; dE [H_E, k, n]; dF like dE when F is a separate matrix (headwise, or
  * unshared with F given and != E), else dF must be NULL and dE holds both projections' parts.
- * All arithmetic fp32 (Kbar, Vbar recomputed in fp32).  ws: linformer_backward_workspace_size()
- * bytes of scratch. */
+ * All arithmetic fp32 (Kbar, Vbar recomputed in fp32; bf16 inputs widen exactly).  ws:
+ * linformer_backward_workspace_size() bytes of scratch (16-byte aligned). */
 int linformer_backward_workspace_size(const lf_problem* p, size_t* bytes);
 int linformer_backward(const lf_problem* p, const void* Q, const void* K, const void* V,
                        const void* E, const void* F, const int32_t* lengths, const void* dO,
