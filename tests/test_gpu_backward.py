@@ -94,3 +94,30 @@ def test_backward_ignores_padded_rows(dtype, share):
         assert e <= TOL, (name, e)
     for b, L in enumerate(lengths):
         assert np.all(got[0][b, :, L:] == 0) and np.all(got[1][b, :, L:] == 0)
+
+
+def test_backward_long_padded_sampled():
+    """The benchmarked shape (B8 H12 n4096 k256, per-head E, F, padded lengths), one launch over
+    the whole batch; checked on one head against the oracle run on that head alone (dE, dF of a
+    head collect only that head's items, so the slice is exact), every item of it."""
+    wl = synth.WORKLOADS["long_b8_h12_n4096_k256_unshared_padded"]
+    inp = synth.make_inputs(wl)
+    dO = synth.to_dtype(np.random.default_rng(1).standard_normal((wl.batch, wl.heads, wl.n, wl.d)),
+                        wl.dtype)
+    G.log(f"backward {wl.name} full launch")
+    got = G.run_backward(inp, dO)
+    h = 5
+    ref = orc.backward(inp.Q[:, h:h + 1], inp.K[:, h:h + 1], inp.V[:, h:h + 1], inp.E[h:h + 1],
+                       inp.F[h:h + 1], wl.share, dO[:, h:h + 1], inp.lengths)
+    errs = [("dQ", orc.slice_rel_err(got[0][:, h:h + 1], ref[0])),
+            ("dK", orc.slice_rel_err(got[1][:, h:h + 1], ref[1])),
+            ("dV", orc.slice_rel_err(got[2][:, h:h + 1], ref[2])),
+            ("dE", _mat_err(got[3][h:h + 1], ref[3])), ("dF", _mat_err(got[4][h:h + 1], ref[4]))]
+    G.log("  " + "  ".join(f"{n_} {e:.2e}" for n_, e in errs))
+    for name, e in errs:
+        assert e <= TOL, (name, e)
+    for b, L in enumerate(inp.lengths):   # padded positions: zero gradients, every head
+        assert np.all(got[1][b, :, L:] == 0) and np.all(got[2][b, :, L:] == 0)
+    Lmax = int(max(inp.lengths))   # no item reaches these positions
+    assert np.all(got[3][:, :, Lmax:] == 0) and np.all(got[4][:, :, Lmax:] == 0)
+    assert all(np.all(np.isfinite(g)) for g in got)
