@@ -167,3 +167,45 @@ def test_stack_argument_errors_before_any_device_work():
     assert f(fake(0), fake(1), fake(2), fake(3), None, fake(4), fake(5), need - 1) == 5
     assert f(fake(0), fake(1), fake(2), fake(3), None, fake(0) + 64, fake(5), big) == 7
     assert f(fake(0), fake(1), fake(2), fake(3), None, fake(4), fake(4) + 256, big) == 7
+
+
+def test_backward_workspace_and_argument_errors():
+    p = L.problem(2, 2, 256, 64, 64, L.LF_BF16, L.LF_SHARE_NONE)
+    need = L.linformer_backward_workspace_size(p)
+    # at least Kbar, Vbar, their gradients (fp32 [B, H, k, 64]) and P, dS (fp32 [B, H, n, k])
+    assert need >= 4 * (2 * 2 * 64 * 64 * 4) + 2 * (2 * 2 * 256 * 64 * 4)
+    big = 1 << 33
+    f = lambda *a, **kw: L.linformer_backward(p, *a, check=False, **kw)
+    ok = [fake(0), fake(1), fake(2), fake(3), fake(4), None, fake(5),
+          fake(6), fake(7), fake(8), fake(9), fake(10), fake(11), big]
+    def args(i, v):
+        a = list(ok)
+        a[i] = v
+        return a
+    assert f(*args(0, None)) == 1                # Q missing
+    assert f(*args(11, None)) == 1               # dF missing while F is separate
+    assert f(*args(4, fake(3))) == 4             # F = E: dF must be NULL
+    assert f(*args(7, fake(7) + 4)) == 6         # misaligned dQ
+    assert f(*args(13, need - 1)) == 5           # workspace too small
+    assert f(*args(8, fake(1) + 64)) == 7        # dK overlaps K
+    pk = L.problem(2, 2, 256, 64, 64, L.LF_BF16, L.LF_SHARE_KV)
+    assert L.linformer_backward(pk, fake(0), fake(1), fake(2), fake(3), None, None, fake(5),
+                                fake(6), fake(7), fake(8), fake(9), fake(10), fake(11), big,
+                                check=False) == 4       # shared F: no dF
+    assert L.linformer_backward(pk, fake(0), fake(1), fake(2), fake(3), None, None, fake(5),
+                                fake(6), fake(7), fake(8), fake(9), None, fake(11), big,
+                                check=False) in (0, 8)  # valid up to the device check
+
+
+def test_conv_argument_errors():
+    p = L.problem(2, 2, 256, 64, 64, L.LF_BF16, L.LF_SHARE_NONE)
+    f = lambda *a: L.linformer_project_kv_conv(p, *a, check=False)
+    assert f(None, fake(1), fake(2), fake(3), None, fake(4), fake(5)) == 1
+    assert f(fake(0) + 2, fake(1), fake(2), fake(3), None, fake(4), fake(5)) == 6
+    assert f(fake(0), fake(1), fake(2), fake(3), None, fake(0), fake(5)) == 7   # Kbar over K
+    p3 = L.problem(2, 2, 256, 64, 96, L.LF_BF16, L.LF_SHARE_NONE)                # n % k != 0
+    assert L.linformer_project_kv_conv(p3, fake(0), fake(1), fake(2), fake(3), None, fake(4),
+                                       fake(5), check=False) == 2
+    p32 = L.problem(2, 2, 256, 64, 64, L.LF_F32, L.LF_SHARE_NONE)
+    assert L.linformer_project_kv_conv(p32, fake(0), fake(1), fake(2), fake(3), None, fake(4),
+                                       fake(5), check=False) == 3
