@@ -585,6 +585,9 @@ bool proj_geometry(int B, int H, int n, int k, int share, int split_override,
         const int slots = 256 * (per_cu > 0 ? per_cu : 1);
         S = slots / tiles;
         if (S > steps / 4) S = steps / 4;
+        // a short reduction (<= 1024 positions) over tiles that already fill a quarter of the
+        // slots gains less from splitting than the fixup pass costs
+        if (steps <= 16 && 4 * tiles >= slots) S = 1;
         if (S < 1) S = 1;
     }
     if (S > steps) S = steps;
