@@ -203,18 +203,32 @@ __global__ __launch_bounds__(256) void bw_gemm_kernel(BwGemm g) {
 }
 
 // ---- sum of the split partials in chunk order, then alpha / beta into C
+template <int V>   // V consecutive columns per thread (4 when C's rows are contiguous, N % 4 == 0)
 __global__ __launch_bounds__(256) void bw_gemm_reduce_kernel(BwGemm g) {
     const size_t mn = (size_t)g.M * g.N, total = mn * g.Z;
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t idx = ((size_t)blockIdx.x * 256 + threadIdx.x) * V;
     if (idx >= total) return;
-    float s = 0.0f;
-    for (int sp = 0; sp < g.splits; ++sp) s += g.part[(size_t)sp * total + idx];
+    float s[V] = {};
+    for (int sp = 0; sp < g.splits; ++sp) {
+        const float* q = g.part + (size_t)sp * total + idx;
+        if constexpr (V == 4) {
+            const f32x4 w = *(const f32x4*)q;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[e] += w[e];
+        } else {
+            s[0] += *q;
+        }
+    }
     const int z = (int)(idx / mn);
     const int i = (int)((idx % mn) / g.N), j = (int)(idx % g.N);
     const long long z1 = z / g.zdiv, z2 = z % g.zdiv;
+    const bool keep = !g.row_len || i < clamp_len(g.row_len, (int)z1, g.M);
     float* c = g.C + z1 * g.c_z1 + z2 * g.c_z2 + (long long)i * g.c_i + (long long)j * g.c_j;
-    const float v = g.alpha * s + (g.beta != 0.0f ? g.beta * *c : 0.0f);
-    *c = (!g.row_len || i < clamp_len(g.row_len, (int)z1, g.M)) ? v : 0.0f;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        const float v = g.alpha * s[e] + (g.beta != 0.0f ? g.beta * c[e] : 0.0f);
+        c[e] = keep ? v : 0.0f;
+    }
 }
 
 // ---- per (b, h) and a range of 128-query blocks: P and dS ([n, k]) and dQ, on the fp32 matrix
@@ -446,8 +460,12 @@ hipError_t launch_bw_gemm(const BwGemm& g, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.splits == 1) return e;
     const size_t total = (size_t)g.Z * g.M * g.N;
-    hipLaunchKernelGGL(bw_gemm_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       stream, g);
+    if (g.c_j == 1 && g.N % 4 == 0)   // four contiguous columns per thread
+        hipLaunchKernelGGL(bw_gemm_reduce_kernel<4>, dim3((unsigned)((total / 4 + 255) / 256)),
+                           dim3(256), 0, stream, g);
+    else
+        hipLaunchKernelGGL(bw_gemm_reduce_kernel<1>, dim3((unsigned)((total + 255) / 256)),
+                           dim3(256), 0, stream, g);
     return hipGetLastError();
 }
 
