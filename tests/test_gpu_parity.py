@@ -95,6 +95,45 @@ def test_project_tile_configs_and_splits(k, cfg, split):
     assert ev <= 4e-3
 
 
+@pytest.mark.parametrize("split", [2, 5])
+def test_project_split_workspace_contents_do_not_matter(split):
+    """With a split, the partial sums pass through the workspace; whatever it holds on entry
+    (zeros, ones, random bytes, a previous call's partials) the output is bitwise the same, call
+    after call."""
+    torch = G.torch_mod()
+    inp = synth.random_inputs(3, 4, 1024, 64, 128, BF, NONE, seed=21, lengths=[1024, 700, 65])
+    wl = inp.wl
+    p = G.prob(wl)
+    K, V, E, F = (G.dev(x, wl.dtype) for x in (inp.K, inp.V, inp.E, inp.F))
+    lens = G.lengths_dev(inp.lengths)
+    kbytes, _ = L.linformer_kv_sizes(p)
+    outs = []
+    with G.env(LINFORMER_PROJ_SPLIT=split):
+        wsb = L.linformer_workspace_size(p)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        gen = torch.Generator(device="cuda").manual_seed(3)
+        for fill in ("zero", "ones", "random", "again", "again"):
+            if fill == "zero":
+                ws.zero_()
+            elif fill == "ones":
+                ws.fill_(255)
+            elif fill == "random":
+                ws.copy_(torch.randint(0, 256, (wsb,), dtype=torch.uint8, device="cuda",
+                                       generator=gen))
+            Kbar = torch.empty(kbytes, dtype=torch.uint8, device="cuda")
+            Vbar = G.empty((wl.batch, wl.heads, wl.k, wl.d), wl.dtype)
+            L.linformer_project_kv(p, K, V, E, F, lens, Kbar, Vbar, ws, wsb)
+            torch.cuda.synchronize()
+            outs.append((Kbar.cpu().numpy(), G.host(Vbar)))
+    G.log(f"split {split}: {len(outs)} calls")
+    for kb, vb in outs[1:]:
+        assert np.array_equal(kb, outs[0][0]) and np.array_equal(vb, outs[0][1])
+    rk, rv = _ref_project(inp)
+    _, _, x = G.decode_kbar_bf16(outs[0][0], (wl.batch, wl.heads, wl.k, wl.d))
+    assert orc.slice_rel_err(x / G.log2e_scale(wl), rk) <= KBAR_TOL
+    assert orc.slice_rel_err(outs[0][1], rv) <= 4e-3
+
+
 @pytest.mark.parametrize("split", [1, 3])
 def test_kbar_storage_format(split):
     """The bf16 Kbar bytes follow the documented format, from both the single-split epilogue and
