@@ -366,6 +366,32 @@ def test_forward_without_lengths_equals_full_lengths():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("split,k", [(1, 128), (2, 256), (3, 128), (6, 96)])
+def test_forward_equals_project_then_attend(split, k):
+    """linformer_forward gives bitwise the output of linformer_project_kv followed by
+    linformer_attend, with and without a split projection."""
+    torch = G.torch_mod()
+    inp = synth.random_inputs(2, 3, 768, 64, k, BF, NONE, seed=31 + k, lengths=[768, 301])
+    wl = inp.wl
+    p = G.prob(wl)
+    Q, K, V, E, F = (G.dev(x, wl.dtype) for x in (inp.Q, inp.K, inp.V, inp.E, inp.F))
+    lens = G.lengths_dev(inp.lengths)
+    with G.env(LINFORMER_PROJ_SPLIT=split):
+        wsb = L.linformer_workspace_size(p)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        O1 = G.empty((wl.batch, wl.heads, wl.n, wl.d), wl.dtype)
+        L.linformer_forward(p, Q, K, V, E, F, lens, O1, ws, wsb)
+        kbytes, _ = L.linformer_kv_sizes(p)
+        Kbar = torch.empty(kbytes, dtype=torch.uint8, device="cuda")
+        Vbar = G.empty((wl.batch, wl.heads, wl.k, wl.d), wl.dtype)
+        O2 = G.empty((wl.batch, wl.heads, wl.n, wl.d), wl.dtype)
+        L.linformer_project_kv(p, K, V, E, F, lens, Kbar, Vbar, ws, wsb)
+        L.linformer_attend(p, Q, Kbar, Vbar, lens, O2)
+    torch.cuda.synchronize()
+    G.log(f"forward vs project + attend, split {split} k {k}")
+    assert torch.equal(O1, O2)
+
+
 def test_forward_is_deterministic():
     inp = synth.random_inputs(2, 3, 1024, 64, 256, BF, NONE, seed=23, lengths=[1000, 517])
     a, _ = G.run_forward(inp)
