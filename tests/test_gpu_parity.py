@@ -476,3 +476,51 @@ def test_error_paths_on_device():
     # valid call succeeds
     assert L.linformer_forward(p, Q, K, K, E, None, None, O, ws, wsb, check=False) == 0
     torch.cuda.synchronize()
+
+
+def test_forward_in_hip_graph():
+    """linformer_forward captured once into a HIP graph and replayed: every replay, with new
+    inputs copied into the captured buffers and eager work between replays, equals the eager
+    call bitwise (the library enqueues kernels only: no allocation, no memset, no host sync)."""
+    torch = G.torch_mod()
+    wl0 = synth.random_inputs(2, 3, 1024, 64, 128, BF, NONE, seed=41, lengths=[1024, 555])
+    wl = wl0.wl
+    p = G.prob(wl)
+    shp = (wl.batch, wl.heads, wl.n, wl.d)
+    Q, K, V = (G.empty(shp, wl.dtype) for _ in range(3))
+    E, F = G.dev(wl0.E, wl.dtype), G.dev(wl0.F, wl.dtype)
+    lens = G.lengths_dev(wl0.lengths)
+    O = G.empty(shp, wl.dtype)
+    wsb = L.linformer_workspace_size(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    inputs = [synth.random_inputs(2, 3, 1024, 64, 128, BF, NONE, seed=50 + i, lengths=[1024, 555])
+              for i in range(3)]
+
+    def load(inp):
+        Q.copy_(G.dev(inp.Q, wl.dtype))
+        K.copy_(G.dev(inp.K, wl.dtype))
+        V.copy_(G.dev(inp.V, wl.dtype))
+
+    load(inputs[0])
+    torch.cuda.synchronize()
+    with G.env(LINFORMER_PROJ_SPLIT=2):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):   # warm up on the capture stream
+            L.linformer_forward(p, Q, K, V, E, F, lens, O, ws, wsb)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            L.linformer_forward(p, Q, K, V, E, F, lens, O, ws, wsb)
+        torch.cuda.synchronize()
+        for inp in inputs:
+            load(inp)
+            ref = G.empty(shp, wl.dtype)
+            L.linformer_forward(p, Q, K, V, E, F, lens, ref, ws, wsb)   # eager
+            torch.cuda.synchronize()
+            O.fill_(7.0)
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(O, ref)
+    G.log("graph replays equal the eager calls")
