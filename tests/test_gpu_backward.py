@@ -5,6 +5,7 @@ magnitude (per (b, h) for dQ, dK, dV; per matrix for dE, dF), for both input dty
 import numpy as np
 import pytest
 
+from efficient_transformer_attention_seq_amd import linformer as L
 from efficient_transformer_attention_seq_amd import synth
 from oracle import linformer_oracle as orc
 from tests import gpu_util as G
@@ -121,3 +122,42 @@ def test_backward_long_padded_sampled():
     Lmax = int(max(inp.lengths))   # no item reaches these positions
     assert np.all(got[3][:, :, Lmax:] == 0) and np.all(got[4][:, :, Lmax:] == 0)
     assert all(np.all(np.isfinite(g)) for g in got)
+
+
+def test_backward_in_hip_graph():
+    """linformer_backward captured once into a HIP graph (split reductions included) and
+    replayed for new upstream gradients: every replay equals the eager call bitwise."""
+    torch = G.torch_mod()
+    B, H, n, k = 2, 2, 1024, 128
+    inp = synth.random_inputs(B, H, n, 64, k, BF, NONE, seed=61, lengths=[1024, 640])
+    wl = inp.wl
+    p = G.prob(wl)
+    Q, K, V, E, F = (G.dev(x, wl.dtype) for x in (inp.Q, inp.K, inp.V, inp.E, inp.F))
+    lens = G.lengths_dev(inp.lengths)
+    dO = G.empty((B, H, n, 64), wl.dtype)
+    f32 = lambda shape: torch.empty(shape, dtype=torch.float32, device="cuda")
+    outs = [f32((B, H, n, 64)) for _ in range(3)] + [f32(inp.E.shape), f32(inp.F.shape)]
+    wsb = L.linformer_backward_workspace_size(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    call = lambda o: L.linformer_backward(p, Q, K, V, E, F, lens, dO, *o, ws, wsb)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(outs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(outs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(62)
+    for _ in range(3):
+        dO.copy_(G.dev(synth.to_dtype(rng.standard_normal((B, H, n, 64)), BF), BF))
+        ref = [torch.empty_like(o) for o in outs]
+        call(ref)
+        torch.cuda.synchronize()
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(o, r) for o, r in zip(outs, ref))

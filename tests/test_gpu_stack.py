@@ -12,6 +12,7 @@ the 12-layer workload its own 0.02.
 import numpy as np
 import pytest
 
+from efficient_transformer_attention_seq_amd import linformer as L
 from efficient_transformer_attention_seq_amd import synth
 from oracle import linformer_oracle as orc
 from tests import gpu_util as G
@@ -107,3 +108,40 @@ def test_stack_full_size_sampled():
     err = orc.slice_rel_err(Y[-1][items], ref)
     G.log(f"  end to end: err {err:.3e}")
     assert err <= END_TOL
+
+
+def test_stack_in_hip_graph():
+    """linformer_stack_forward captured once into a HIP graph and replayed for new inputs:
+    every replay equals the eager call bitwise."""
+    torch = G.torch_mod()
+    wl = synth.StackWorkload("graph_stack", 2, 512, 384, 6, 128, 2, 0.5 / np.sqrt(384), False, 7)
+    si = synth.make_stack_inputs(wl)
+    s = L.stack(wl.batch, wl.n, wl.d_model, wl.heads, wl.k, wl.layers)
+    BF = synth.DT_BF16
+    X = G.empty((wl.batch, wl.n, wl.d_model), BF)
+    Wq, Wo, E = G.dev(si.Wqkv, BF), G.dev(si.Wo, BF), G.dev(si.E, BF)
+    Y = G.empty((wl.batch, wl.n, wl.d_model), BF)
+    wsb = L.linformer_stack_workspace_size(s)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    call = lambda out: L.linformer_stack_forward(s, X, Wq, Wo, E, None, out, ws, wsb)
+    X.copy_(G.dev(si.X, BF))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(Y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(Y)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    for _ in range(3):
+        X.copy_(G.dev(synth.to_dtype(rng.standard_normal(X.shape), BF), BF))
+        ref = torch.empty_like(Y)
+        call(ref)
+        torch.cuda.synchronize()
+        Y.fill_(7.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, ref)
