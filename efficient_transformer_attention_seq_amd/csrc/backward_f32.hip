@@ -23,7 +23,12 @@ namespace {
 // while the current one is multiplied.  Operand tiles are read with consecutive threads along
 // the operand's contiguous direction (the reduction index when its stride is 1, else the row or
 // column index), so global reads coalesce either way.
-constexpr int kGM = 128, kGK = 32, kGPad = 1;
+constexpr int kGM = 128, kGK = 32;
+// LDS row padding (floats) of an operand tile: 1 when it is staged down columns (vectors along
+// the reduction index: consecutive rows land in consecutive banks), 4 when it is staged along
+// rows (16-byte aligned rows, so each vector is one 16-byte write)
+template <bool kf>
+constexpr int kGPad = kf ? 1 : 4;
 // Strides and bases must keep every 16-byte vector aligned: launch_bw_gemm checks them.
 
 __device__ __forceinline__ f32x16 mfma_f32_32(float a, float b, f32x16 c) {
@@ -107,10 +112,13 @@ struct TileLoader {
             const int kk = kk0 + v * dkk, x = x0 + v * dx;
             float d[VEC];
             unpack(raw[v], d, T{});
+            if constexpr (kf) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                if constexpr (kf) S[kk + e][x] = d[e];
-                else S[kk][x + e] = d[e];
+                for (int e = 0; e < VEC; ++e) S[kk + e][x] = d[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; e += 4)
+                    *(f32x4*)&S[kk][x + e] = f32x4{d[e], d[e + 1], d[e + 2], d[e + 3]};
             }
         }
     }
@@ -120,8 +128,8 @@ struct TileLoader {
 template <int NI, typename TA, bool AKF, typename TB, bool BKF>
 __global__ __launch_bounds__(256) void bw_gemm_kernel(BwGemm g) {
     constexpr int TN = 64 * NI;
-    __shared__ float As[kGK][kGM + kGPad];
-    __shared__ float Bs[kGK][TN + kGPad];
+    __shared__ __attribute__((aligned(16))) float As[kGK][kGM + kGPad<AKF>];
+    __shared__ __attribute__((aligned(16))) float Bs[kGK][TN + kGPad<BKF>];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l = lane & 31, h = lane >> 5;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * (TN / 2);
