@@ -38,6 +38,7 @@ def _mat_err(out, ref):
     (1, 2, 2112, 96, BF, NONE, [2000]),   # reduction split 8 ways, ragged last chunk and row block
     (2, 4, 256, 64, BF, KV, [256, 100]),  # dE's reduction split, second part added with beta
     (1, 3, 384, 192, BF, HEAD, [333]),
+    (3, 2, 256, 64, BF, NONE, [0, 256, 17]),   # an empty item
     (2, 1, 256, 224, F32, NONE, [256, 129]),
 ])
 def test_backward_parity(B, H, n, k, dtype, share, lengths):
