@@ -556,10 +556,20 @@ bool proj_geometry(int B, int H, int n, int k, int share, int split_override,
         for (const CfgInfo& c : kCfgs)
             if (std::strcmp(c.name, cfg_override) == 0 && k % c.ks == 0) cfg = c.id;
     }
+    const int steps = n / kStep;
     if (cfg < 0) {
         if (k % 128 == 0) cfg = 3;
         else if (k % 64 == 0) cfg = 4;
         else cfg = 5;
+        // A short reduction (no split) over more 128-slot tiles than there are compute units
+        // leaves a partial second round of workgroups; 256-slot tiles halve the count (one
+        // round at n = 512, B32 H12 key-value: 36.3 -> 31.5 us) and read fewer LDS bytes per
+        // product.
+        if (k % 256 == 0 && steps <= 16) {
+            const long long t128 = (long long)g.groups * (k / kCfgs[3].ks) *
+                                   ((g.members + kCfgs[3].upt - 1) / kCfgs[3].upt);
+            if (t128 > 256) cfg = 1;
+        }
     }
     const CfgInfo& ci = kCfgs[cfg];
     g.cfg = cfg;
@@ -572,7 +582,6 @@ bool proj_geometry(int B, int H, int n, int k, int share, int split_override,
     if (ns < 2) ns = 2;
     g.stages = ns;
     g.threads = ci.nw * 64;
-    const int steps = n / kStep;
     const int tiles = g.groups * g.slot_tiles * g.tiles_per_group;
     int S;
     if (split_override > 0) {
