@@ -37,6 +37,10 @@
 //      (1, 1)), and each output column (one query) is divided by it.
 //   The score MFMAs of block j+1 are issued before the softmax of block j so that matrix and
 //   vector work interleave within the wave.
+// Q and O move between HBM and the wave as whole rows: a 32-query tile is 4 KB of contiguous
+// memory, loaded (and stored) by four 1 KB wave instructions and rearranged through a 4 KB
+// per-wave LDS staging buffer into (out of) the operand layout, in which each lane holds 16 or 8
+// bytes of every one of 32 rows.
 #include "lf_device.h"
 #include "lf_launch.h"
 
@@ -167,6 +171,10 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
     __shared__ int s_next;   // next tile of the current segment (relative to its start)
     __shared__ int s_len[kMaxAttendBatch];       // clamped length per batch item
     __shared__ int s_cum[kMaxAttendBatch + 1];   // valid tiles (all heads) before each batch item
+    // per-wave staging of one 32-query tile (32 rows x 128 bytes, 16-byte chunks swizzled by
+    // swz16(row)): Q on its way in and O on its way out, so that both move between HBM and the
+    // wave as whole contiguous rows (each wave instruction covers 1 KB, eight full rows)
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[kThreads / 64][kTileQ * 128];
     const uint32_t lds0 = lds_addr(smem);
 
     const int G = gridDim.x;
@@ -293,12 +301,35 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
         // ---- tiles of this segment, taken dynamically by the waves from an LDS counter (so waves
         // that finish early take more), Q of the next tile prefetched during the current one
         int tt = t + wave;
-        bf16x8 qop[4];
+        bf16x8 qop[4];   // operand layout: columns 16 ks + 8 hh + (0..7) of query q0 + l32
+        u32x4 qraw[4];   // the tile as loaded: row 8 i + lane / 8, chunk lane % 8, i = 0..3
         auto load_q = [&](int tile) {
             const int q0 = (p0.j + (tile - t)) * kTileQ;
-            const uint16_t* qrow = a.Q + (rowbase + q0 + l32) * kHeadDim + hh * 8;
+            const u32x4* src = (const u32x4*)(a.Q + (rowbase + q0) * kHeadDim) + lane;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) qop[ks] = *(const bf16x8*)(qrow + ks * 16);
+            for (int i = 0; i < 4; ++i) qraw[i] = src[64 * i];
+        };
+        // lane's chunk of the coalesced layout: row 8 i + crow, chunk ccol, at this LDS offset
+        const int crow = lane >> 3, ccol = lane & 7;
+        uint32_t coff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 8 * i + crow;
+            coff[i] = r * 128 + ((ccol ^ swz16(r)) << 4);
+        }
+        const uint32_t stg = lds_addr(&s_stage[wave][0]);
+        const int sw_l = swz16(l32);
+        // raw Q -> staging -> operand layout (the LDS operations of a wave execute in order, so
+        // the previous tile's output staging reads are done before these writes land)
+        auto stage_q = [&]() {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(stg + coff[i]) = qraw[i];
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes have landed
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qop[ks] = lds_ld<bf16x8>(stg, l32 * 128 + (((2 * ks + hh) ^ sw_l) << 4));
         };
         auto grab = [&]() {
             int v = 0;
@@ -313,6 +344,7 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
         int tnext = grab();
         for (; tt < seg_end; tt = tnext, tnext = (tnext < seg_end ? grab() : tnext)) {
             const int q0 = (p0.j + (tt - t)) * kTileQ;
+            stage_q();
             if (bias_dirty) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) asm volatile("v_mov_b32 %0, 0" : "+v"(bias[j]));
@@ -363,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
             for (int blk = 0; blk < NBLK; ++blk) {
                 const int cur = blk & 1;
                 if (blk + 1 < NBLK) scores(blk + 1, sc[cur ^ 1]);
-                else if (tnext < seg_end) load_q(tnext);   // Q is dead: prefetch the next tile
+                else if (tnext < seg_end) load_q(tnext);
                 __builtin_amdgcn_sched_barrier(0);
                 const int nrb = min(2, KB - 2 * blk);
                 // block max of s - mref (both lanes of a query)
@@ -431,21 +463,28 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
             z += other_half(z, hh);
             const float inv = 1.0f / z;
 
-            // ---- store: lane holds O[q0 + l32][c] for c = 32 mt + 8 gq + 4 hh + (0..3)
-            const int q = q0 + l32;
-            uint16_t* orow = a.O + (rowbase + q) * kHeadDim + 4 * hh;
-            const bool valid = q < L;
+            // ---- store: lane holds O[q0 + l32][c] for c = 32 mt + 8 gq + 4 hh + (0..3), i.e.
+            // 8 bytes of chunk 4 mt + gq; staged, then written as whole rows (rows past the
+            // length as zeros)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                u32x2 v0 = {0u, 0u}, v1 = {0u, 0u};
-                if (valid) {
-                    v0[0] = pack_bf16x2(o0[4 * gq] * inv, o0[4 * gq + 1] * inv);
-                    v0[1] = pack_bf16x2(o0[4 * gq + 2] * inv, o0[4 * gq + 3] * inv);
-                    v1[0] = pack_bf16x2(o1[4 * gq] * inv, o1[4 * gq + 1] * inv);
-                    v1[1] = pack_bf16x2(o1[4 * gq + 2] * inv, o1[4 * gq + 3] * inv);
-                }
-                *(u32x2*)(orow + 8 * gq) = v0;
-                *(u32x2*)(orow + 32 + 8 * gq) = v1;
+                const u32x2 v0 = {pack_bf16x2(o0[4 * gq] * inv, o0[4 * gq + 1] * inv),
+                                  pack_bf16x2(o0[4 * gq + 2] * inv, o0[4 * gq + 3] * inv)};
+                const u32x2 v1 = {pack_bf16x2(o1[4 * gq] * inv, o1[4 * gq + 1] * inv),
+                                  pack_bf16x2(o1[4 * gq + 2] * inv, o1[4 * gq + 3] * inv)};
+                *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(
+                    stg + l32 * 128 + ((gq ^ sw_l) << 4) + 8 * hh) = v0;
+                *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(
+                    stg + l32 * 128 + (((4 + gq) ^ sw_l) << 4) + 8 * hh) = v1;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes have landed
+            __builtin_amdgcn_wave_barrier();
+            u32x4* dst = (u32x4*)(a.O + (rowbase + q0) * kHeadDim) + lane;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                u32x4 v = lds_ld<u32x4>(stg, coff[i]);
+                if (q0 + 8 * i + crow >= L) v = u32x4{0u, 0u, 0u, 0u};
+                dst[64 * i] = v;
             }
         }
         t = seg_end;
