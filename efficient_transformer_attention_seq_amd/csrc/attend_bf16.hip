@@ -40,7 +40,9 @@
 // Q and O move between HBM and the wave as whole rows: a 32-query tile is 4 KB of contiguous
 // memory, loaded (and stored) by four 1 KB wave instructions and rearranged through a 4 KB
 // per-wave LDS staging buffer into (out of) the operand layout, in which each lane holds 16 or 8
-// bytes of every one of 32 rows.
+// bytes of every one of 32 rows.  O and the zero rows are written with streaming
+// (non-temporal) stores: this kernel never reads them back, and lines that do not linger dirty in
+// L2 leave less to write back when the kernel ends.
 #include "lf_device.h"
 #include "lf_launch.h"
 
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
             for (int i = 0; i < 4; ++i) {
                 u32x4 v = lds_ld<u32x4>(stg, coff[i]);
                 if (q0 + 8 * i + crow >= L) v = u32x4{0u, 0u, 0u, 0u};
-                dst[64 * i] = v;
+                __builtin_nontemporal_store(v, &dst[64 * i]);
             }
         }
         t = seg_end;
@@ -514,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
                 if (lo >= hi2) continue;
                 u32x4* blk = (u32x4*)(a.O + ((size_t)(b * a.H + h) * a.n + r0) * kHeadDim);
                 for (int c = (int)(lo - base) + tid; c < (int)(hi2 - base); c += kThreads)
-                    blk[c] = zero;
+                    __builtin_nontemporal_store(zero, &blk[c]);
             }
         }
     }
