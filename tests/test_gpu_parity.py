@@ -358,6 +358,22 @@ def test_forward_edge_lengths(lens):
         assert np.all(out[b, :, Lb:] == 0.0)
 
 
+@pytest.mark.parametrize("k", [128, 256])
+def test_forward_tile_edge_lengths_with_guard(k):
+    """Lengths one below, at and one above a 32-query tile edge and inside a later tile, at the
+    production tile shapes: the attention moves Q and O as whole 32-row tiles, so rows past a
+    length inside the last tile must come out zero and nothing outside O may be written."""
+    lens = [31, 32, 33, 95]
+    inp = synth.random_inputs(4, 3, 256, 64, k, BF, NONE, seed=41 + k, lengths=lens)
+    G.log(f"tile-edge lengths {lens}, k {k}")
+    out, ok = G.run_forward(inp, guard=True)
+    ref = _ref_forward(inp)
+    assert ok
+    assert orc.slice_rel_err(out, ref) <= 2e-2
+    for b, Lb in enumerate(lens):
+        assert np.all(out[b, :, Lb:] == 0.0)
+
+
 def test_forward_without_lengths_equals_full_lengths():
     inp = synth.random_inputs(2, 2, 256, 64, 128, BF, KV, seed=22)
     a, _ = G.run_forward(inp)
