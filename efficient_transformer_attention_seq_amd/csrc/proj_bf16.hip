@@ -519,6 +519,7 @@ using Cfg128x256w4 = ProjCfg<2, 2, 2, 2>; // 4 waves, 64x128 wave tiles
 using Cfg128x256 = ProjCfg<2, 1, 2, 4>;   // 8 waves, 64x64 wave tiles
 using Cfg64x512 = ProjCfg<2, 1, 1, 8>;    // 8 waves, 64x64 wave tiles
 using Cfg32x512 = ProjCfg<1, 1, 1, 8>;    // 8 waves, 32x64 wave tiles (any k % 32 == 0)
+using Cfg128x128w4 = ProjCfg<2, 1, 2, 2>; // 4 waves, 64x64 wave tiles
 
 struct CfgInfo {
     const char* name;
@@ -531,6 +532,7 @@ constexpr CfgInfo kCfgs[] = {
     {"128x256", 3, Cfg128x256::KS, Cfg128x256::UPT, Cfg128x256::NW},
     {"64x512", 4, Cfg64x512::KS, Cfg64x512::UPT, Cfg64x512::NW},
     {"32x512", 5, Cfg32x512::KS, Cfg32x512::UPT, Cfg32x512::NW},
+    {"128x128w4", 6, Cfg128x128w4::KS, Cfg128x128w4::UPT, Cfg128x128w4::NW},
 };
 
 }  // namespace
@@ -580,37 +582,44 @@ bool proj_geometry(int B, int H, int n, int k, int share, int split_override,
             if (t128 > 256) cfg = 1;
         }
     }
-    const CfgInfo& ci = kCfgs[cfg];
-    g.cfg = cfg;
-    g.upt = ci.upt;
-    g.slot_tiles = k / ci.ks;
-    g.tiles_per_group = (g.members + ci.upt - 1) / ci.upt;
-    const int stage = ci.ks * 128 + ci.upt * kUnitTile;
-    int ns = kLdsBudget / stage;
-    if (ns > 5) ns = 5;
-    if (ns < 2) ns = 2;
-    g.stages = ns;
-    g.threads = ci.nw * 64;
-    const int tiles = g.groups * g.slot_tiles * g.tiles_per_group;
-    int S;
-    if (split_override > 0) {
-        S = split_override;
-    } else {
-        // workgroups resident per compute unit (LDS-limited), 256 compute units: split the
-        // positions so that all tiles x splits fit in one wave of workgroups, keeping at least
-        // 4 steps (256 positions) per split.
-        const int per_cu = (160 * 1024) / (ns * stage);
-        const int slots = 256 * (per_cu > 0 ? per_cu : 1);
-        S = slots / tiles;
-        if (S > steps / 4) S = steps / 4;
-        // a short reduction (<= 1024 positions) over tiles that already fill a quarter of the
-        // slots gains less from splitting than the fixup pass costs
-        if (steps <= 16 && 4 * tiles >= slots) S = 1;
-        if (S < 1) S = 1;
-    }
-    if (S > steps) S = steps;
-    g.steps_per_split = (steps + S - 1) / S;
-    g.S = (steps + g.steps_per_split - 1) / g.steps_per_split;
+    auto plan = [&](int c) {
+        const CfgInfo& ci = kCfgs[c];
+        g.cfg = c;
+        g.upt = ci.upt;
+        g.slot_tiles = k / ci.ks;
+        g.tiles_per_group = (g.members + ci.upt - 1) / ci.upt;
+        const int stage = ci.ks * 128 + ci.upt * kUnitTile;
+        int ns = kLdsBudget / stage;
+        if (ns > 5) ns = 5;
+        if (ns < 2) ns = 2;
+        g.stages = ns;
+        g.threads = ci.nw * 64;
+        const int tiles = g.groups * g.slot_tiles * g.tiles_per_group;
+        int S;
+        if (split_override > 0) {
+            S = split_override;
+        } else {
+            // workgroups resident per compute unit (LDS-limited), 256 compute units: split the
+            // positions so that all tiles x splits fit in one wave of workgroups, keeping at
+            // least 4 steps (256 positions) per split.
+            const int per_cu = (160 * 1024) / (ns * stage);
+            const int slots = 256 * (per_cu > 0 ? per_cu : 1);
+            S = slots / tiles;
+            if (S > steps / 4) S = steps / 4;
+            // a short reduction (<= 1024 positions) over tiles that already fill a quarter of
+            // the slots gains less from splitting than the fixup pass costs
+            if (steps <= 16 && 4 * tiles >= slots) S = 1;
+            if (S < 1) S = 1;
+        }
+        if (S > steps) S = steps;
+        g.steps_per_split = (steps + S - 1) / S;
+        g.S = (steps + g.steps_per_split - 1) / g.steps_per_split;
+        return tiles;
+    };
+    const int tiles = plan(cfg);
+    // An unsplit reduction over 128 x 256 tiles that occupy at most half of the compute units
+    // (the stack's E . X: 96 tiles) runs on twice as many 128 x 128 tiles instead.
+    if (!(cfg_override && cfg_override[0]) && cfg == 3 && g.S == 1 && 2 * tiles <= 256) plan(6);
     g.nlogical = g.groups * g.S * g.slot_tiles * g.tiles_per_group;
     *out = g;
     return true;
@@ -643,6 +652,7 @@ hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream) {
         case 2: e = launch_cfg<Cfg128x256w4>(a, stream); break;
         case 3: e = launch_cfg<Cfg128x256>(a, stream); break;
         case 4: e = launch_cfg<Cfg64x512>(a, stream); break;
+        case 6: e = launch_cfg<Cfg128x128w4>(a, stream); break;
         default: e = launch_cfg<Cfg32x512>(a, stream); break;
     }
     if (e != hipSuccess || g.S == 1) return e;

@@ -78,7 +78,7 @@ def test_project_parity(case, dtype):
     (256, "256x128", 1), (256, "256x256", 2), (256, "128x256w4", 3), (256, "128x256", 5),
     (256, "64x512", 2), (256, "32x512", 1), (128, "128x256", 8), (128, "128x256w4", 2),
     (128, "64x512", 3), (96, "32x512", 2), (192, "64x512", 4), (64, "64x512", 1),
-    (128, "128x256", 10), (64, "64x512", 10)])
+    (128, "128x256", 10), (64, "64x512", 10), (256, "128x128w4", 1), (128, "128x128w4", 3)])
 def test_project_tile_configs_and_splits(k, cfg, split):
     """Every tile configuration and split count computes the same thing (fixed-order split
     sums), including tiles whose later steps lie entirely past every length."""
