@@ -7,7 +7,8 @@
 // equal contiguous ranges, one per workgroup; consecutive workgroups go to the same XCD so the
 // workgroups that share a head's Kbar/Vbar share an L2.  The lengths are read once into LDS
 // tables (length and valid-tile prefix per batch item).  Rows past the lengths are zero-filled
-// with plain stores after the tiles, spread evenly over the workgroups.
+// with streaming stores issued early in each workgroup's tile work, spread evenly over the
+// workgroups.
 //
 // Kbar arrives pre-scaled by c = scale * log2(e) (so scores come out as base-2 logits) as a bf16
 // plane plus an fp8 residual plane with per-block scales (format in lf_launch.h).  Per (b, h)
@@ -260,6 +261,40 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
     for (int part = 0; part < 2; ++part)
         laddr[part] = opaque(lds0 + OFF_L + l32 * 64 + (((2 * hh + part) ^ ((l32 >> 1) & 3)) << 4));
 
+    // ---- zero the rows wholly past each length.  Each wave issues its share once its first
+    // tile's Q is in registers, so the streaming stores drain under the tile work (the next wait
+    // that counts them is for the Q prefetch, a whole tile later); the chunks are split by thread,
+    // so waves may do this at different times.  Per (b, h) those rows are one contiguous
+    // block of per_h 16-byte chunks; concatenated over (b, h) the blocks of batch item b start at
+    // chunk zb(b) = 8 (b H n - 32 cum[b]), and each workgroup zeroes an equal share of the chunks.
+    bool zeroed = false;
+    auto zero_fill = [&]() {
+        zeroed = true;
+        const long long Z = 8LL * ((long long)a.B * a.H * a.n - 32LL * T);
+        if (Z <= 0) return;
+        const long long z0 = Z * w / G, z1 = Z * (w + 1) / G;
+        auto zb = [&](int b) { return 8LL * ((long long)b * a.H * a.n - 32LL * s_cum[b]); };
+        int b = 0, hi = a.B - 1;   // last batch item whose blocks start at or before z0
+        while (b < hi) {
+            const int mid = (b + hi + 1) >> 1;
+            if (zb(mid) <= z0) b = mid;
+            else hi = mid - 1;
+        }
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        for (; b < a.B && zb(b) < z1; ++b) {
+            const int r0 = ((s_len[b] + kTileQ - 1) / kTileQ) * kTileQ;
+            const long long per_h = (long long)(a.n - r0) * 8;
+            long long base = zb(b);
+            for (int h = 0; h < a.H && base < z1; ++h, base += per_h) {
+                const long long lo = max(z0, base), hi2 = min(z1, base + per_h);
+                if (lo >= hi2) continue;
+                u32x4* blk = (u32x4*)(a.O + ((size_t)(b * a.H + h) * a.n + r0) * kHeadDim);
+                for (int c = (int)(lo - base) + tid; c < (int)(hi2 - base); c += kThreads)
+                    __builtin_nontemporal_store(zero, &blk[c]);
+            }
+        }
+    };
+
     int t = t_lo;
     while (t < t_hi) {
         const TilePos p0 = tile_pos(s_cum, s_len, a.B, t);
@@ -347,6 +382,7 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
         for (; tt < seg_end; tt = tnext, tnext = (tnext < seg_end ? grab() : tnext)) {
             const int q0 = (p0.j + (tt - t)) * kTileQ;
             stage_q();
+            if (!zeroed) zero_fill();   // once, after the first tile's Q is in registers
             if (bias_dirty) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) asm volatile("v_mov_b32 %0, 0" : "+v"(bias[j]));
@@ -489,37 +525,12 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
                 __builtin_nontemporal_store(v, &dst[64 * i]);
             }
         }
+        if (!zeroed) zero_fill();   // a wave that took no tile of the segment
         t = seg_end;
     }
 
-    // ---- zero the rows wholly past each length, after the tiles so the stores drain while other
-    // workgroups still compute.  Per (b, h) those rows are one contiguous block of per_h 16-byte
-    // chunks; concatenated over (b, h) the blocks of batch item b start at chunk
-    // zb(b) = 8 (b H n - 32 cum[b]), and each workgroup zeroes an equal share of the chunks.
-    const long long Z = 8LL * ((long long)a.B * a.H * a.n - 32LL * T);
-    if (Z > 0) {
-        const long long z0 = Z * w / G, z1 = Z * (w + 1) / G;
-        auto zb = [&](int b) { return 8LL * ((long long)b * a.H * a.n - 32LL * s_cum[b]); };
-        int b = 0, hi = a.B - 1;   // last batch item whose blocks start at or before z0
-        while (b < hi) {
-            const int mid = (b + hi + 1) >> 1;
-            if (zb(mid) <= z0) b = mid;
-            else hi = mid - 1;
-        }
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-        for (; b < a.B && zb(b) < z1; ++b) {
-            const int r0 = ((s_len[b] + kTileQ - 1) / kTileQ) * kTileQ;
-            const long long per_h = (long long)(a.n - r0) * 8;
-            long long base = zb(b);
-            for (int h = 0; h < a.H && base < z1; ++h, base += per_h) {
-                const long long lo = max(z0, base), hi2 = min(z1, base + per_h);
-                if (lo >= hi2) continue;
-                u32x4* blk = (u32x4*)(a.O + ((size_t)(b * a.H + h) * a.n + r0) * kHeadDim);
-                for (int c = (int)(lo - base) + tid; c < (int)(hi2 - base); c += kThreads)
-                    __builtin_nontemporal_store(zero, &blk[c]);
-            }
-        }
-    }
+    if (!zeroed) zero_fill();   // a workgroup without tiles
+
 }
 
 }  // namespace
