@@ -55,6 +55,26 @@ def test_sizes_match_layout():
     assert L.linformer_workspace_size(p32) >= kb + vb
 
 
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,H,n,k,share,splits", [
+    (8, 12, 4096, 256, L.LF_SHARE_NONE, 2),       # bench shape: 96 tiles x 2 position splits
+    (1, 12, 1024, 128, L.LF_SHARE_LAYERWISE, 4),  # 6 tiles, at least 256 positions per split
+    (1, 12, 512, 128, L.LF_SHARE_LAYERWISE, 1),   # at most 512 positions: never split
+    (32, 12, 512, 256, L.LF_SHARE_KV, 1),         # short reduction over many tiles: unsplit
+])
+def test_workspace_holds_partials_only_for_split_projections(B, H, n, k, share, splits):
+    """The forward workspace is Kbar | Vbar | fp32 partial sums of the position splits
+    ([splits, 2, B, H, k, 64]), each region 256-byte aligned; an unsplit projection needs no
+    partials.  Pins the host's split plan for a few shapes."""
+    p = L.problem(B, H, n, 64, k, L.LF_BF16, share)
+    kb, vb = L.linformer_kv_sizes(p)
+    part = splits * 2 * B * H * k * 64 * 4 if splits > 1 else 0
+    assert L.linformer_workspace_size(p) == _r256(kb) + _r256(vb) + _r256(part)
+
+
 @pytest.mark.parametrize("field,value,code", [
     ("d", 32, 2), ("n", 100, 2), ("n", 0, 2), ("k", 48, 2), ("k", 288, 2), ("k", 0, 2),
     ("batch", 0, 2), ("batch", 4097, 2), ("heads", 0, 2), ("dtype", 5, 3), ("share", 9, 4),
