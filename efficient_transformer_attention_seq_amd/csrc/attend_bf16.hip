@@ -356,13 +356,14 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
         }
         const uint32_t stg = lds_addr(&s_stage[wave][0]);
         const int sw_l = swz16(l32);
-        // raw Q -> staging -> operand layout (the LDS operations of a wave execute in order, so
-        // the previous tile's output staging reads are done before these writes land)
+        // raw Q -> staging -> operand layout.  The LDS operations of a wave execute in issue
+        // order, so a read issued after a write sees it (no counter wait in between, only a
+        // compiler barrier against reordering), and the previous tile's output staging reads are
+        // done before these writes land.
         auto stage_q = [&]() {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(stg + coff[i]) = qraw[i];
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes have landed
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
@@ -515,7 +516,6 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
                 *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(
                     stg + l32 * 128 + (((4 + gq) ^ sw_l) << 4) + 8 * hh) = v1;
             }
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes have landed
             __builtin_amdgcn_wave_barrier();
             u32x4* dst = (u32x4*)(a.O + (rowbase + q0) * kHeadDim) + lane;
 #pragma unroll
