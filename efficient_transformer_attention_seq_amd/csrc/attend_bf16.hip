@@ -369,18 +369,22 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
             for (int ks = 0; ks < 4; ++ks)
                 qop[ks] = lds_ld<bf16x8>(stg, l32 * 128 + (((2 * ks + hh) ^ sw_l) << 4));
         };
-        auto grab = [&]() {
+        // the counter's reply (lane 0) is read into a scalar only where the tile is first needed,
+        // so the atomic's round trip overlaps the current tile's work
+        auto grab_raw = [&]() {
             int v = 0;
             if (lane == 0) v = atomicAdd(&s_next, 1);
-            return t + __builtin_amdgcn_readfirstlane(v);
+            return v;
         };
         f32x16 bias;   // -mref of this lane's query, the score accumulators' start value
 #pragma unroll
         for (int j = 0; j < 16; ++j) bias[j] = 0.0f;
         bool bias_dirty = false;
         if (tt < seg_end) load_q(tt);
-        int tnext = grab();
-        for (; tt < seg_end; tt = tnext, tnext = (tnext < seg_end ? grab() : tnext)) {
+        int tnext = t + __builtin_amdgcn_readfirstlane(grab_raw());
+        int gv = 0;              // reply of the grab for the tile after tt, if `pending`
+        bool pending = false;
+        for (; tt < seg_end; tt = tnext, pending = tnext < seg_end, gv = pending ? grab_raw() : 0) {
             const int q0 = (p0.j + (tt - t)) * kTileQ;
             stage_q();
             if (!zeroed) zero_fill();   // once, after the first tile's Q is in registers
@@ -434,7 +438,11 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
             for (int blk = 0; blk < NBLK; ++blk) {
                 const int cur = blk & 1;
                 if (blk + 1 < NBLK) scores(blk + 1, sc[cur ^ 1]);
-                else if (tnext < seg_end) load_q(tnext);
+                else {
+                    if (pending) tnext = t + __builtin_amdgcn_readfirstlane(gv);
+                    pending = false;
+                    if (tnext < seg_end) load_q(tnext);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 const int nrb = min(2, KB - 2 * blk);
                 // block max of s - mref (both lanes of a query)
