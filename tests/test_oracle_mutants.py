@@ -113,3 +113,86 @@ def test_stack_mutant_is_caught(idx, monkeypatch):
     for check in checks:
         with pytest.raises((AssertionError, ValueError)):
             check()
+
+
+# ---- batched entries: the per-item length and the (b, h) slice a result is written to
+def _dense_forward_lengths_by_head(Q, K, V, lengths=None, scale=None, pairs=None):
+    Q = np.asarray(Q, dtype=np.float64)
+    B, H, n, d = Q.shape
+    O = np.zeros((B, H, n, d))
+    todo = [(b, h) for b in range(B) for h in range(H)] if pairs is None else list(pairs)
+    for b, h in todo:
+        L = None if lengths is None else int(lengths[h])           # slip: indexed by head
+        O[b, h] = orc.dense_attention(Q[b, h], K[b, h], V[b, h], scale, L)
+    return O
+
+
+def _dense_forward_swapped(Q, K, V, lengths=None, scale=None, pairs=None):
+    Q = np.asarray(Q, dtype=np.float64)
+    B, H, n, d = Q.shape
+    O = np.zeros((B, H, n, d))
+    todo = [(b, h) for b in range(B) for h in range(H)] if pairs is None else list(pairs)
+    for b, h in todo:
+        L = None if lengths is None else int(lengths[b])
+        O[h, b] = orc.dense_attention(Q[b, h], K[b, h], V[b, h], scale, L)   # slip: O[h, b]
+    return O
+
+
+def _forward_variant(slip):
+    def fwd(Q, K, V, E, F, share, lengths=None, scale=None, pairs=None,
+            return_intermediates=False):
+        Q = np.asarray(Q, dtype=np.float64)
+        B, H, n, d = Q.shape
+        Es, Fs = orc.head_projections(E, F, share, H)
+        k = Es[0].shape[0]
+        O = np.zeros((B, H, n, d))
+        Kb = np.zeros((B, H, k, d))
+        Vb = np.zeros((B, H, k, d))
+        every = [(b, h) for b in range(B) for h in range(H)]
+        todo = every if (pairs is None or slip == "pairs_ignored") else list(pairs)
+        for b, h in todo:
+            L = None if lengths is None else int(lengths[h if slip == "lengths_by_head" else b])
+            ib, ih = (h, b) if slip == "swapped" else (b, h)
+            Kb[b, h] = orc.project(Es[h], K[ib, ih], L)
+            Vb[b, h] = orc.project(Fs[h], V[ib, ih], L)
+            O[b, h] = orc.attend(Q[ib, ih], Kb[b, h], Vb[b, h], scale, L)
+        if return_intermediates:
+            return O, Kb, Vb
+        return O
+    return fwd
+
+
+def _run_all(test, params):
+    for args in params:
+        test(*args)
+
+
+_DENSE_CASES = [(3, 3, 5, [0, 5, 3]), (4, 2, 6, [2, 6, 0, 5])]
+_FWD_CASES = [(3, 3, 7, [0, 7, 4]), (4, 2, 6, [3, 6, 0, 1])]
+
+BATCH_MUTANTS = [
+    ("dense_forward", _dense_forward_lengths_by_head,
+     lambda: _run_all(pins.test_dense_forward_batch_matches_brute_per_item, _DENSE_CASES)),
+    ("dense_forward", _dense_forward_swapped,
+     lambda: _run_all(pins.test_dense_forward_batch_matches_brute_per_item, _DENSE_CASES)),
+    ("forward", _forward_variant("lengths_by_head"),
+     lambda: _run_all(pins.test_forward_batch_matches_brute_per_item, _FWD_CASES)),
+    ("forward", _forward_variant("swapped"),
+     lambda: _run_all(pins.test_forward_batch_matches_brute_per_item, _FWD_CASES)),
+    ("forward", _forward_variant("pairs_ignored"),
+     lambda: pins.test_forward_pairs_subset_equals_full(orc.SHARE_NONE)),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(BATCH_MUTANTS)))
+def test_batch_mutant_is_caught(idx, monkeypatch):
+    name, fn, check = BATCH_MUTANTS[idx]
+    monkeypatch.setattr(orc, name, fn)
+    with pytest.raises((AssertionError, ValueError)):
+        check()
+
+
+def test_batch_mutant_harness_passes_unmutated():
+    # the same checks pass on the oracle as written, so a caught mutant is the slip's doing
+    for _, _, check in BATCH_MUTANTS:
+        check()

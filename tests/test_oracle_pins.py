@@ -347,3 +347,106 @@ def test_golden_orientation_sharing_modes(share):
         want = g["O_kv_shared"]
     for h in range(2):
         np.testing.assert_allclose(O[0, h], want, rtol=0, atol=1e-13)
+
+
+# ------------------------------------------ batched entries: each (b, h) on its own item's length
+# The batched entry points look up one length per batch item and write slice (b, h) from the
+# inputs of slice (b, h).  Checked per slice against the separately written brute force, on
+# batches whose items all have different lengths (0 and n included), with as many heads as
+# batch items so that a slip between the two indices gives a wrong value rather than an
+# index error.
+def _per_item_lengths_batch(seed, B, H, n, d):
+    rng = np.random.default_rng(seed)
+    Q, K, V = _rand(rng, B, H, n, d), _rand(rng, B, H, n, d), _rand(rng, B, H, n, d)
+    return rng, Q, K, V
+
+
+@pytest.mark.parametrize("B,H,n,lengths", [(3, 3, 5, [0, 5, 3]), (4, 2, 6, [2, 6, 0, 5])])
+def test_dense_forward_batch_matches_brute_per_item(B, H, n, lengths):
+    d = 3
+    _, Q, K, V = _per_item_lengths_batch(81 + B, B, H, n, d)
+    scale = 1 / math.sqrt(d)
+    O = orc.dense_forward(Q, K, V, lengths)
+    for b in range(B):
+        for h in range(H):
+            ref = brute_attention(Q[b, h].tolist(), K[b, h].tolist(), V[b, h].tolist(), scale,
+                                  valid=lengths[b])
+            np.testing.assert_allclose(O[b, h], ref, rtol=1e-12, atol=1e-12)
+    # no lengths: every key and every row of every slice
+    O = orc.dense_forward(Q, K, V)
+    for b in range(B):
+        for h in range(H):
+            ref = brute_attention(Q[b, h].tolist(), K[b, h].tolist(), V[b, h].tolist(), scale)
+            np.testing.assert_allclose(O[b, h], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("B,H,n,lengths", [(3, 3, 7, [0, 7, 4]), (4, 2, 6, [3, 6, 0, 1])])
+def test_forward_batch_matches_brute_per_item(B, H, n, lengths):
+    # Kbar = E_h[:, :L] K[:L] and Vbar = F_h[:, :L] V[:L] by explicit loops, then the textbook
+    # attention over all k projected slots, then rows past the item's length set to zero
+    d, k = 3, 4
+    rng, Q, K, V = _per_item_lengths_batch(91 + B, B, H, n, d)
+    E, F = _rand(rng, H, k, n), _rand(rng, H, k, n)
+    scale = 0.7
+    O = orc.forward(Q, K, V, E, F, orc.SHARE_NONE, lengths=lengths, scale=scale)
+    for b in range(B):
+        L = lengths[b]
+        for h in range(H):
+            Kb = brute_matmul(E[h][:, :L].tolist(), K[b, h][:L].tolist()) if L else np.zeros((k, d))
+            Vb = brute_matmul(F[h][:, :L].tolist(), V[b, h][:L].tolist()) if L else np.zeros((k, d))
+            ref = brute_attention(Q[b, h].tolist(), Kb.tolist(), Vb.tolist(), scale)
+            ref[L:] = 0.0
+            np.testing.assert_allclose(O[b, h], ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------ the (b, h) subset mode used by bounded checks
+PAIRS = [(0, 3), (2, 1), (1, 0), (2, 2)]
+
+
+def _subset_inputs():
+    rng = np.random.default_rng(101)
+    B, H, n, d, k = 3, 4, 8, 3, 5
+    Q, K, V = _rand(rng, B, H, n, d), _rand(rng, B, H, n, d), _rand(rng, B, H, n, d)
+    return rng, Q, K, V, [8, 3, 0], k
+
+
+def _check_subset(sub, full):
+    assert sub.shape == full.shape
+    for b in range(full.shape[0]):
+        for h in range(full.shape[1]):
+            if (b, h) in PAIRS:
+                np.testing.assert_array_equal(sub[b, h], full[b, h])
+            else:
+                assert np.all(sub[b, h] == 0.0)
+
+
+@pytest.mark.parametrize("share", [orc.SHARE_NONE, orc.SHARE_HEADWISE, orc.SHARE_KV])
+def test_forward_pairs_subset_equals_full(share):
+    rng, Q, K, V, lengths, k = _subset_inputs()
+    H, n = Q.shape[1], Q.shape[2]
+    HE = H if share == orc.SHARE_NONE else 1
+    E = _rand(rng, HE, k, n)
+    F = None if share == orc.SHARE_KV else _rand(rng, HE, k, n)
+    full = orc.forward(Q, K, V, E, F, share, lengths=lengths)
+    fullO, fullK, fullV = orc.forward(Q, K, V, E, F, share, lengths=lengths,
+                                      return_intermediates=True)
+    np.testing.assert_array_equal(full, fullO)
+    # the slices the subset touches are not all zero, so "equal" is not vacuous
+    assert all(np.abs(fullO[b, h]).max() > 0 for b, h in PAIRS if lengths[b] > 0)
+    _check_subset(orc.forward(Q, K, V, E, F, share, lengths=lengths, pairs=PAIRS), full)
+    subO, subK, subV = orc.forward(Q, K, V, E, F, share, lengths=lengths, pairs=PAIRS,
+                                   return_intermediates=True)
+    _check_subset(subO, fullO)
+    _check_subset(subK, fullK)
+    _check_subset(subV, fullV)
+
+
+def test_conv_and_dense_pairs_subset_equal_full():
+    rng, Q, K, V, lengths, _ = _subset_inputs()
+    H, n = Q.shape[1], Q.shape[2]
+    wE, wF = _rand(rng, H, 2), _rand(rng, H, 2)   # window 2: k = n / 2
+    full = orc.conv_forward(Q, K, V, wE, wF, orc.SHARE_NONE, lengths=lengths)
+    _check_subset(orc.conv_forward(Q, K, V, wE, wF, orc.SHARE_NONE, lengths=lengths,
+                                   pairs=PAIRS), full)
+    full = orc.dense_forward(Q, K, V, lengths)
+    _check_subset(orc.dense_forward(Q, K, V, lengths, pairs=PAIRS), full)
