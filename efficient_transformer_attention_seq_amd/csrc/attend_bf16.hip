@@ -21,7 +21,8 @@
 // Per wave and tile of 32 queries:
 //   1. S^T (k x 32) = Kbar . Q^T: per 32 slots four v_mfma_f32_32x32x16_bf16 for the hi plane
 //      times Q, then one v_mfma_scale_f32_32x32x64_f8f6f4 for the residual (fp8 lo plane times Q
-//      rounded to e4m3, scaled back by the block scales), so the scores carry Kbar to within
+//      rounded to e4m3 with a power-of-two scale per query and 32-column block, both scaled back
+//      by their block scales), so the scores carry Kbar to within
 //      2^-12 of each row half's largest value.  The accumulators start from -mref (see 2), so
 //      they hold s - mref directly.
 //   2. Exact softmax per query in one streaming pass over blocks of 64 slots: the scores of a query
@@ -107,38 +108,80 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t vo
                  : "memory");
 }
 
+// The value lane l ^ 32 holds, as raw bits.
+__device__ __forceinline__ uint32_t other_half_u(uint32_t x, bool upper) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return upper ? r[0] : r[1];
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
 // Q of this lane (32 values: columns 16 ks + 8 hh + j, j = 0..7, for ks = 0..3) as e4m3 bytes in
 // the same order (byte 8 ks + j), round to nearest even: the B operand of the residual product.
-__device__ __forceinline__ i32x8 q_fp8(const bf16x8 (&qop)[4]) {
-    // v_cvt_scalef32_pk_fp8_bf16 (scale 1) converts a bf16 pair straight into one 16-bit half of
-    // the destination, keeping the other half (op_sel[2] picks the high half).  Inline asm with
-    // the destination tied, so that both halves are written into the same register in order.
-    i32x8 r;
-    const float one = 1.0f;
+// Each (query, 32-column block) gets its own power of two 2^s, chosen so that the block's largest
+// |q| times 2^s lies in [128, 256): below e4m3's largest finite value (448; unscaled, elements of
+// 464 and more would convert to NaN) and high enough that small queries keep their precision.
+// Columns 0..31 are block 0 (bytes 0..15 of both lanes of the query), 32..63 block 1.  `qsc`
+// receives 127 - s of block hh, the E8M0 scale byte the matrix core multiplies the products of
+// that block back by (lane 32 b + q supplies block b of query q).
+__device__ __forceinline__ i32x8 q_fp8(const bf16x8 (&qop)[4], bool upper, int& qsc) {
+    // largest magnitude per block: bf16 magnitudes order like their bit patterns without the sign
+    uint32_t mb[2];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const u32x4 w = __builtin_bit_cast(u32x4, qop[m >> 1]);
+    for (int blk = 0; blk < 2; ++blk) {
+        const u32x4 w0 = __builtin_bit_cast(u32x4, qop[2 * blk]);
+        const u32x4 w1 = __builtin_bit_cast(u32x4, qop[2 * blk + 1]);
+        uint32_t m = w0[0] & 0x7FFF7FFFu;
+#pragma unroll
+        for (int i = 1; i < 4; ++i) m = max_u16x2(m, w0[i] & 0x7FFF7FFFu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max_u16x2(m, w1[i] & 0x7FFF7FFFu);
+        mb[blk] = m;
+    }
+    // (block 0, block 1) maxima of this lane's 16-bit halves, then of the query's two lanes
+    uint32_t m = max_u16x2(__builtin_amdgcn_perm(mb[1], mb[0], 0x05040100u),
+                           __builtin_amdgcn_perm(mb[1], mb[0], 0x07060302u));
+    m = max_u16x2(m, other_half_u(m, upper));
+    // 127 - s = biased exponent of the block max - 7, kept in [1, 247] (zero blocks take s = 126)
+    const int sb0 = min(max((int)((m >> 7) & 0xFF) - 7, 1), 247);
+    const int sb1 = min(max((int)((m >> 23) & 0xFF) - 7, 1), 247);
+    qsc = upper ? sb1 : sb0;
+    // the conversion divides by its scale operand: 2^(127 - s - 127) = 2^-s
+    const float dv[2] = {__uint_as_float((uint32_t)sb0 << 23), __uint_as_float((uint32_t)sb1 << 23)};
+    // v_cvt_scalef32_pk_fp8_bf16 converts a bf16 pair straight into one 16-bit half of the
+    // destination, keeping the other half (op_sel[2] picks the high half).  Inline asm with the
+    // destination tied, so that both halves are written into the same register in order.
+    i32x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const u32x4 w = __builtin_bit_cast(u32x4, qop[i >> 1]);
+        const float d = dv[i >> 2];
         uint32_t v = 0;
-        asm volatile("v_cvt_scalef32_pk_fp8_bf16 %0, %1, %2" : "+v"(v) : "v"(w[2 * (m & 1)]), "v"(one));
-        asm volatile("v_cvt_scalef32_pk_fp8_bf16 %0, %1, %2 op_sel:[0,0,1]" : "+v"(v) : "v"(w[2 * (m & 1) + 1]), "v"(one));
-        r[m] = (int)v;
+        asm volatile("v_cvt_scalef32_pk_fp8_bf16 %0, %1, %2" : "+v"(v) : "v"(w[2 * (i & 1)]), "v"(d));
+        asm volatile("v_cvt_scalef32_pk_fp8_bf16 %0, %1, %2 op_sel:[0,0,1]" : "+v"(v) : "v"(w[2 * (i & 1) + 1]), "v"(d));
+        r[i] = (int)v;
     }
     return r;
 }
 
 // acc + (residual block of 32 slots) . (Q e4m3): the A operand's two 32-column blocks of row l32
 // are scaled by 2^(byte - 127) with the byte taken from byte `SEL` of `scl` in lanes l32 (block 0)
-// and l32 + 32 (block 1).
+// and l32 + 32 (block 1); the B operand's blocks of query l32 likewise by byte 0 of `qsc`.
 template <int SEL>
-__device__ __forceinline__ f32x16 mfma_lo_sel(i32x8 lo, i32x8 q8, f32x16 acc, int scl) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lo, q8, acc, 0, 0, SEL, scl, 0, 0x7F7F7F7F);
+__device__ __forceinline__ f32x16 mfma_lo_sel(i32x8 lo, i32x8 q8, f32x16 acc, int scl, int qsc) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lo, q8, acc, 0, 0, SEL, scl, 0, qsc);
 }
-__device__ __forceinline__ f32x16 mfma_lo(int sel, i32x8 lo, i32x8 q8, f32x16 acc, int scl) {
+__device__ __forceinline__ f32x16 mfma_lo(int sel, i32x8 lo, i32x8 q8, f32x16 acc, int scl,
+                                          int qsc) {
     switch (sel) {   // sel is a compile-time constant after unrolling
-        case 0: return mfma_lo_sel<0>(lo, q8, acc, scl);
-        case 1: return mfma_lo_sel<1>(lo, q8, acc, scl);
-        case 2: return mfma_lo_sel<2>(lo, q8, acc, scl);
-        default: return mfma_lo_sel<3>(lo, q8, acc, scl);
+        case 0: return mfma_lo_sel<0>(lo, q8, acc, scl, qsc);
+        case 1: return mfma_lo_sel<1>(lo, q8, acc, scl, qsc);
+        case 2: return mfma_lo_sel<2>(lo, q8, acc, scl, qsc);
+        default: return mfma_lo_sel<3>(lo, q8, acc, scl, qsc);
     }
 }
 
@@ -393,7 +436,8 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
                 for (int j = 0; j < 16; ++j) asm volatile("v_mov_b32 %0, 0" : "+v"(bias[j]));
                 bias_dirty = false;
             }
-            const i32x8 q8 = q_fp8(qop);
+            int qsc;
+            const i32x8 q8 = q_fp8(qop, hh, qsc);
 
             constexpr int NBLK = (KB + 1) / 2;
             f32x16 sc[2][2];   // [buffer][rb within block]
@@ -419,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
                         const u32x4 l1 = lds_ld<u32x4>(laddr[1], rb * 2048);
                         const i32x8 lop = __builtin_bit_cast(
                             i32x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
-                        dst[r2] = mfma_lo(rb & 3, lop, q8, dst[r2], scl[rb >> 2]);
+                        dst[r2] = mfma_lo(rb & 3, lop, q8, dst[r2], scl[rb >> 2], qsc);
                     }
                 }
             };

@@ -32,9 +32,11 @@
  *   LF_BF16 : bf16 Q, K, V, E, F, O; all sums accumulate in fp32; the softmax runs in fp32.
  *             Kbar is kept to within 2^-12 of the largest value of each row half, as a bf16
  *             plane plus an fp8 (e4m3) residual plane with power-of-two block scales (layout
- *             below); Vbar and
- *             the softmax weights are rounded once to bf16 (round to nearest even) for the
- *             matrix cores.
+ *             below); the residual's product with Q takes Q in e4m3 with its own power-of-two
+ *             scale per query and 32-column block, so every finite bf16 Q is in range (e4m3
+ *             alone ends at 448).  Vbar and the softmax weights are rounded once to bf16 (round
+ *             to nearest even) for the matrix cores.
+ *   Inputs must be finite; results for NaN or infinite inputs are not defined.
  *
  * Shape limits: d == 64; k % 32 == 0 and 32 <= k <= 256; n % 64 == 0 and n >= 64;
  * 1 <= batch <= 4096, heads >= 1; batch * heads * n * d < 2^31 elements.

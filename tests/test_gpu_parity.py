@@ -253,6 +253,38 @@ def test_attend_extreme_logits(kind):
     assert np.all(np.isfinite(out)) and err <= 2e-2
 
 
+@pytest.mark.parametrize("kind", ["large", "mixed_blocks", "mixed_queries"])
+def test_forward_query_magnitudes_beyond_e4m3(kind):
+    """Queries far outside e4m3's range (largest finite value 448), where the residual product
+    takes Q: every element scaled up to |q| of 1e3-1e4 (keys scaled down by the same factor so
+    the logits stay moderate); the two 32-column blocks of every query at 4000x and 1/512x (each
+    block of the keys scaled inversely, so both blocks carry the logits); alternate queries of
+    every tile at 8000x and 1e-3x (keys at 1/8000x, so the small queries' softmax is near
+    uniform).  Every result must be finite and within the bf16 bar."""
+    B, H, n, k = 2, 2, 256, 128
+    inp = synth.random_inputs(B, H, n, 64, k, BF, NONE, seed=77, lengths=[256, 161])
+    Q, K = inp.Q.astype(np.float64), inp.K.astype(np.float64)
+    if kind == "large":
+        Q, K = Q * 3000.0, K / 3000.0
+    elif kind == "mixed_blocks":
+        Q[..., :32] *= 4000.0
+        Q[..., 32:] /= 512.0
+        K[..., :32] /= 4000.0
+        K[..., 32:] *= 512.0
+    else:
+        Q[:, :, 0::2] *= 8000.0
+        Q[:, :, 1::2] *= 1e-3
+        K = K / 8000.0
+    inp = synth.Inputs(inp.wl, synth.to_dtype(Q, BF), synth.to_dtype(K, BF), inp.V, inp.E,
+                       inp.F, inp.lengths)
+    G.log(f"forward query magnitudes {kind}: max|q| {np.abs(inp.Q).max():.3e}")
+    out, ok = G.run_forward(inp, guard=True)
+    err = orc.slice_rel_err(out, _ref_forward(inp))
+    G.log(f"  err {err:.3e}")
+    assert ok and np.all(np.isfinite(out))
+    assert err <= G.TOL[BF]
+
+
 def test_attend_explicit_scale():
     B, H, n, k = 1, 1, 128, 64
     pr = synth.random_projected(B, H, n, 64, k, BF, seed=4, kbar_std=1.0)
