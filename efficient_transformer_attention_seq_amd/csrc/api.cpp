@@ -2,13 +2,14 @@
 // The operations are declared (with their citations) in include/linformer.h.
 #include "linformer.h"
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "lf_launch.h"
 
@@ -396,6 +397,88 @@ int do_linear(const lf::LinearBf16Args& base, hipStream_t stream) {
     return launch_status(lf::launch_linear_bf16(a, stream));
 }
 
+// Workspace of one forward call: Kbar | Vbar | split partial sums, each 256-byte aligned.
+size_t forward_ws_bytes(const lf_problem* p, const lf::ProjGeom& g) {
+    return round_up(kbar_bytes(p), 256) + round_up(vbar_bytes(p), 256) +
+           round_up(part_bytes(p, g), 256);
+}
+
+// Validation of a forward call, everything but the device; `own_ws`: the workspace is the
+// library's fixed scratch (not the caller's), so only its size is checked, by the caller.
+struct FwdPlan {
+    lf::ProjGeom g;
+    size_t kb, vb, pb, need;
+    const void* Fr;
+};
+
+int forward_validate(const lf_problem* p, const void* Q, const void* K, const void* V,
+                     const void* E, const void* F, const int32_t* lengths, void* O, void* ws,
+                     size_t ws_bytes, bool own_ws, FwdPlan* pl) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!geometry(p, &pl->g)) return LF_ERR_SHAPE;
+    pl->kb = round_up(kbar_bytes(p), 256);
+    pl->vb = round_up(vbar_bytes(p), 256);
+    pl->pb = part_bytes(p, pl->g);
+    pl->need = forward_ws_bytes(p, pl->g);
+    pl->Fr = nullptr;
+    st = check_project_args(p, K, V, E, F, lengths, pl->g, ws, ws_bytes, own_ws ? 0 : pl->need,
+                            &pl->Fr);
+    if (st) return st;
+    if (!Q || !O) return LF_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(O)) return LF_ERR_ALIGN;
+    const Range ins[] = {{Q, qkv_bytes(p)}, {K, qkv_bytes(p)}, {V, qkv_bytes(p)},
+                         {E, ef_bytes(p)},  {pl->Fr, ef_bytes(p)},
+                         {lengths, lengths ? 4u * p->batch : 0u}};
+    const Range outs[] = {{O, qkv_bytes(p)}, {own_ws ? nullptr : ws, pl->need}};
+    if (any_overlap(outs, 2, ins, 6)) return LF_ERR_ALIAS;
+    return LF_OK;
+}
+
+// The projection into the workspace (Kbar | Vbar | partials), then the attention.
+int forward_run(const lf_problem* p, const FwdPlan& pl, const void* Q, const void* K,
+                const void* V, const void* E, const int32_t* lengths, void* O, void* ws,
+                void* stream) {
+    uint8_t* w = (uint8_t*)ws;
+    void* Kbar = w;
+    void* Vbar = w + pl.kb;
+    void* part = pl.pb ? (void*)(w + pl.kb + pl.vb) : nullptr;
+    hipStream_t s = (hipStream_t)stream;
+    int st = do_project(p, K, V, E, pl.Fr, lengths, Kbar, Vbar, part, pl.g, s);
+    if (st) return st;
+    return do_attend(p, Q, Kbar, Vbar, lengths, O, s);
+}
+
+// ---- fixed scratch of the no-allocation forward.  Every GPU the library runs on holds its own
+// copy of this array from the first use on that device until the process ends.  On the host,
+// `scratch` names a host-side stand-in, not device memory: host code only ever uses the device
+// address hipGetSymbolAddress returns for the current device, kept per device below.
+constexpr size_t kScratchBytes = (size_t)LINFORMER_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_ptr(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return LF_ERR_NO_DEVICE;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return LF_ERR_ARCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return LF_ERR_SCRATCH;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return LF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -413,6 +496,9 @@ const char* linformer_status_string(int status) {
         case LF_ERR_NO_DEVICE: return "LF_ERR_NO_DEVICE: no HIP device available";
         case LF_ERR_ARCH: return "LF_ERR_ARCH: the current device is not gfx950";
         case LF_ERR_LAUNCH: return "LF_ERR_LAUNCH: kernel launch failed";
+        case LF_ERR_SCRATCH:
+            return "LF_ERR_SCRATCH: the problem needs more than the no-allocation scratch buffer "
+                   "holds, or the buffer could not be located on this device";
         default: return "unknown liblinformer status";
     }
 }
@@ -432,8 +518,7 @@ int linformer_workspace_size(const lf_problem* p, size_t* bytes) {
     if (!bytes) return LF_ERR_NULL;
     lf::ProjGeom g;
     if (!geometry(p, &g)) return LF_ERR_SHAPE;
-    *bytes = round_up(kbar_bytes(p), 256) + round_up(vbar_bytes(p), 256) +
-             round_up(part_bytes(p, g), 256);
+    *bytes = forward_ws_bytes(p, g);
     return LF_OK;
 }
 
@@ -478,32 +563,27 @@ int linformer_attend(const lf_problem* p, const void* Q, const void* Kbar, const
 int linformer_forward(const lf_problem* p, const void* Q, const void* K, const void* V,
                       const void* E, const void* F, const int32_t* lengths, void* O, void* ws,
                       size_t ws_bytes, void* stream) {
-    int st = check_problem(p);
+    FwdPlan pl;
+    int st = forward_validate(p, Q, K, V, E, F, lengths, O, ws, ws_bytes, false, &pl);
     if (st) return st;
-    lf::ProjGeom g;
-    if (!geometry(p, &g)) return LF_ERR_SHAPE;
-    const size_t kb = round_up(kbar_bytes(p), 256), vb = round_up(vbar_bytes(p), 256);
-    const size_t pb = part_bytes(p, g);
-    const size_t need = kb + vb + round_up(pb, 256);
-    const void* Fr = nullptr;
-    st = check_project_args(p, K, V, E, F, lengths, g, ws, ws_bytes, need, &Fr);
-    if (st) return st;
-    if (!Q || !O) return LF_ERR_NULL;
-    if (!aligned16(Q) || !aligned16(O)) return LF_ERR_ALIGN;
-    const Range ins[] = {{Q, qkv_bytes(p)}, {K, qkv_bytes(p)}, {V, qkv_bytes(p)},
-                         {E, ef_bytes(p)},  {Fr, ef_bytes(p)}, {lengths, lengths ? 4u * p->batch : 0u}};
-    const Range outs[] = {{O, qkv_bytes(p)}, {ws, need}};
-    if (any_overlap(outs, 2, ins, 6)) return LF_ERR_ALIAS;
     st = check_device();
     if (st) return st;
-    uint8_t* w = (uint8_t*)ws;
-    void* Kbar = w;
-    void* Vbar = w + kb;
-    void* part = pb ? (void*)(w + kb + vb) : nullptr;
-    hipStream_t s = (hipStream_t)stream;
-    st = do_project(p, K, V, E, Fr, lengths, Kbar, Vbar, part, g, s);
+    return forward_run(p, pl, Q, K, V, E, lengths, O, ws, stream);
+}
+
+int linformer_forward_noalloc(const lf_problem* p, const void* Q, const void* K, const void* V,
+                              const void* E, const void* F, const int32_t* lengths, void* O,
+                              void* stream) {
+    FwdPlan pl;
+    int st = forward_validate(p, Q, K, V, E, F, lengths, O, nullptr, 0, true, &pl);
     if (st) return st;
-    return do_attend(p, Q, Kbar, Vbar, lengths, O, s);
+    if (pl.need > kScratchBytes) return LF_ERR_SCRATCH;
+    st = check_device();
+    if (st) return st;
+    void* ws = nullptr;
+    st = scratch_ptr(&ws);   // first call on this device: locate its copy of the array
+    if (st) return st;
+    return forward_run(p, pl, Q, K, V, E, lengths, O, ws, stream);
 }
 
 int attention_dense_forward(const lf_problem* p, const void* Q, const void* K, const void* V,

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "liblinformer.so")
 LF_OK = 0
 STATUS = {0: "LF_OK", 1: "LF_ERR_NULL", 2: "LF_ERR_SHAPE", 3: "LF_ERR_DTYPE", 4: "LF_ERR_SHARE",
           5: "LF_ERR_WORKSPACE", 6: "LF_ERR_ALIGN", 7: "LF_ERR_ALIAS", 8: "LF_ERR_NO_DEVICE",
-          9: "LF_ERR_ARCH", 10: "LF_ERR_LAUNCH"}
+          9: "LF_ERR_ARCH", 10: "LF_ERR_LAUNCH", 11: "LF_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20   # LINFORMER_NOALLOC_SCRATCH_BYTES
 LF_F32, LF_BF16 = 0, 1
 LF_SHARE_NONE, LF_SHARE_HEADWISE, LF_SHARE_KV, LF_SHARE_LAYERWISE = 0, 1, 2, 3
 
@@ -25,7 +26,8 @@ EXPORTS = ("linformer_status_string", "linformer_workspace_size", "linformer_kv_
            "linformer_project_kv", "linformer_attend", "linformer_forward",
            "attention_dense_forward", "linformer_stack_workspace_size",
            "linformer_stack_forward", "linformer_project_kv_conv", "linformer_forward_conv",
-           "linformer_backward_workspace_size", "linformer_backward")
+           "linformer_backward_workspace_size", "linformer_backward",
+           "linformer_forward_noalloc")
 
 
 class lf_problem(ctypes.Structure):
@@ -83,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.linformer_attend.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.linformer_forward.restype = ctypes.c_int
     L.linformer_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.linformer_forward_noalloc.restype = ctypes.c_int
+    L.linformer_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     L.attention_dense_forward.restype = ctypes.c_int
     L.attention_dense_forward.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.linformer_project_kv_conv.restype = ctypes.c_int
@@ -171,6 +175,13 @@ def linformer_forward(p: lf_problem, Q, K, V, E, F, lengths, O, ws, ws_bytes=Non
     code = lib().linformer_forward(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(E), _ptr(F),
                                    _ptr(lengths), _ptr(O), _ptr(ws), wsb, _stream(stream))
     return _check(code, "linformer_forward", check)
+
+
+def linformer_forward_noalloc(p: lf_problem, Q, K, V, E, F, lengths, O, stream=None,
+                              check: bool = True) -> int:
+    code = lib().linformer_forward_noalloc(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(E),
+                                           _ptr(F), _ptr(lengths), _ptr(O), _stream(stream))
+    return _check(code, "linformer_forward_noalloc", check)
 
 
 def attention_dense_forward(p: lf_problem, Q, K, V, lengths, O, stream=None,

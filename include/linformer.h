@@ -43,7 +43,9 @@
  *
  * Ownership and threading: the caller owns every buffer (device memory) and keeps it alive until
  * the stream has finished the call.  The library allocates nothing and keeps no state between
- * calls except a per-device architecture check; calls are reentrant.  Work is enqueued on
+ * calls except a per-device architecture check (and, for linformer_forward_noalloc(), the device
+ * address of its fixed scratch buffer); calls are reentrant, except that overlapping
+ * linformer_forward_noalloc() calls on one device share that buffer.  Work is enqueued on
  * `stream` (a hipStream_t; NULL means the default stream) and the calls return before it runs.
  *
  * Errors: every argument is validated on the host before anything is enqueued, so an error
@@ -71,7 +73,10 @@ enum lf_status {
     LF_ERR_ALIAS = 7,      /* an output range overlaps an input or another output range     */
     LF_ERR_NO_DEVICE = 8,  /* no HIP device is available                                    */
     LF_ERR_ARCH = 9,       /* the current device is not gfx950                              */
-    LF_ERR_LAUNCH = 10     /* a kernel launch was rejected by the runtime                   */
+    LF_ERR_LAUNCH = 10,    /* a kernel launch was rejected by the runtime                   */
+    LF_ERR_SCRATCH = 11    /* linformer_forward_noalloc: the problem's workspace exceeds
+                              LINFORMER_NOALLOC_SCRATCH_BYTES, or the fixed buffer could not
+                              be located on the current device                              */
 };
 
 enum lf_dtype { LF_F32 = 0, LF_BF16 = 1 };
@@ -135,6 +140,24 @@ int linformer_attend(const lf_problem* p, const void* Q, const void* Kbar, const
 int linformer_forward(const lf_problem* p, const void* Q, const void* K, const void* V,
                       const void* E, const void* F, const int32_t* lengths, void* O, void* ws,
                       size_t ws_bytes, void* stream);
+
+/* Bytes of the fixed scratch buffer linformer_forward_noalloc() uses (64 MiB per device). */
+#define LINFORMER_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* linformer_forward() for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The workspace comes from a
+ * buffer of LINFORMER_NOALLOC_SCRATCH_BYTES inside the library instead of an argument; every
+ * device the library runs on holds its own copy from the first call on that device until the
+ * process ends.  The caller still owns Q, K, V, E, F, lengths and O, with the layouts, sharing
+ * rules and errors of linformer_forward(); the call allocates nothing (no hipMalloc, no library
+ * allocation) and, like linformer_forward(), only enqueues kernels on `stream`.
+ * Returns LF_ERR_SCRATCH, before anything is enqueued, when linformer_workspace_size(p) exceeds
+ * the buffer (the pages' workloads need at most about 33 MiB).  The buffer's contents on entry do
+ * not matter, and every call on one device shares it: calls that can overlap in time on the same
+ * device (other streams, other host threads) race, and the caller must order them. */
+int linformer_forward_noalloc(const lf_problem* p, const void* Q, const void* K, const void* V,
+                              const void* E, const void* F, const int32_t* lengths, void* O,
+                              void* stream);
 
 /* Standard O(n^2) softmax attention of every (b, h) on the same device, the comparison
  * baseline for Linformer (Linformer 요약 설명, section "Transformer and Self-Attention"):

@@ -229,3 +229,29 @@ def test_conv_argument_errors():
     p32 = L.problem(2, 2, 256, 64, 64, L.LF_F32, L.LF_SHARE_NONE)
     assert L.linformer_project_kv_conv(p32, fake(0), fake(1), fake(2), fake(3), None, fake(4),
                                        fake(5), check=False) == 3
+
+
+def test_noalloc_forward_validates_on_the_host():
+    # a workload whose workspace exceeds the fixed scratch buffer is refused before any device work
+    big_p = L.problem(256, 12, 512, 64, 256, L.LF_BF16, L.LF_SHARE_KV)
+    assert L.linformer_workspace_size(big_p) > L.NOALLOC_SCRATCH_BYTES
+    f = lambda p, *a: L.linformer_forward_noalloc(p, *a, check=False)
+    assert f(big_p, fake(0), fake(1), fake(2), fake(3), None, None, fake(4)) == 11
+    assert "scratch" in L.status_string(11)
+    # the benchmarked workloads fit
+    for B, H, n, k, share in ((8, 12, 4096, 256, L.LF_SHARE_NONE), (32, 12, 512, 256, L.LF_SHARE_KV),
+                              (1, 12, 65536, 128, L.LF_SHARE_LAYERWISE),
+                              (16, 12, 1024, 256, L.LF_SHARE_LAYERWISE)):
+        p = L.problem(B, H, n, 64, k, L.LF_BF16, share)
+        assert L.linformer_workspace_size(p) <= L.NOALLOC_SCRATCH_BYTES
+    # argument errors as for linformer_forward
+    p = L.problem(2, 2, 256, 64, 64, L.LF_BF16, L.LF_SHARE_NONE)
+    assert f(p, None, fake(1), fake(2), fake(3), None, None, fake(4)) == 1
+    assert f(p, fake(0), fake(1), fake(2), fake(3), None, None, None) == 1
+    assert f(p, fake(0) + 2, fake(1), fake(2), fake(3), None, None, fake(4)) == 6
+    assert f(p, fake(0), fake(1), fake(2), fake(3), None, None, fake(1) + 64) == 7
+    bad = L.problem(2, 2, 200, 64, 64, L.LF_BF16, L.LF_SHARE_NONE)
+    assert f(bad, fake(0), fake(1), fake(2), fake(3), None, None, fake(4)) == 2
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert f(p, fake(0), fake(1), fake(2), fake(3), None, None, fake(4)) == 8

@@ -1,0 +1,56 @@
+"""The no-allocation forward (linformer_forward_noalloc, for callers that cannot allocate device
+memory) against linformer_forward on the same inputs, through the C ABI: the same kernels in the
+same order, so the outputs must be bitwise equal, and both within the bf16 bar of the oracle.
+Two calls in a row share the library's fixed scratch buffer, the second on a smaller problem of
+another shape and sharing mode, so what the first left in the buffer must not leak into it."""
+import numpy as np
+import pytest
+
+from efficient_transformer_attention_seq_amd import linformer as L
+from efficient_transformer_attention_seq_amd import synth
+from oracle import linformer_oracle as orc
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, H, n, k, share, lengths: the first needs split partials in the scratch, the second not
+    (4, 6, 2048, 256, synth.SHARE_NONE, [2048, 1500, 700, 33]),
+    (2, 3, 512, 128, synth.SHARE_KV, [512, 257]),
+]
+
+
+def _run_both(case, seed):
+    torch = G.torch_mod()
+    B, H, n, k, share, lens = case
+    inp = synth.random_inputs(B, H, n, 64, k, synth.DT_BF16, share, seed=seed, lengths=lens)
+    wl = inp.wl
+    p = G.prob(wl)
+    assert L.linformer_workspace_size(p) <= L.NOALLOC_SCRATCH_BYTES
+    Q, K, V, E = (G.dev(x, wl.dtype) for x in (inp.Q, inp.K, inp.V, inp.E))
+    F = G.dev(inp.F, wl.dtype) if inp.F is not None else None
+    ld = G.lengths_dev(inp.lengths)
+    G.log(f"noalloc case B{B} H{H} n{n} k{k} share={share} lengths={lens}")
+    buf, O_na = G.guarded((B, H, n, 64), wl.dtype)
+    L.linformer_forward_noalloc(p, Q, K, V, E, F, ld, O_na)
+    torch.cuda.synchronize()
+    wsb = L.linformer_workspace_size(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    O = G.empty((B, H, n, 64), wl.dtype)
+    L.linformer_forward(p, Q, K, V, E, F, ld, O, ws, wsb)
+    torch.cuda.synchronize()
+    assert G.guards_intact(buf), "write outside the output tensor"
+    assert torch.equal(O_na, O), "no-allocation forward differs from linformer_forward"
+    ref = orc.forward(inp.Q, inp.K, inp.V, inp.E, inp.F, share, inp.lengths)
+    err = orc.slice_rel_err(G.host(O_na), ref)
+    G.log(f"  bitwise equal to linformer_forward; err vs oracle {err:.3e}")
+    assert err <= G.TOL[synth.DT_BF16]
+
+
+def test_noalloc_forward_twice_second_smaller():
+    if G.torch_mod().cuda.device_count() < 1:
+        pytest.skip("no GPU")
+    _run_both(CASES[0], seed=31)
+    _run_both(CASES[1], seed=32)
+    # the larger problem again, after the smaller one left its values in the buffer
+    _run_both(CASES[0], seed=33)
