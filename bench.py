@@ -39,6 +39,44 @@ def source_hash(kernel: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def source_hashes() -> dict:
+    """sha256/16 of every kernel and host source of the library and of its header, and one hash
+    over all of them: the key that ties a recorded number to the code that produced it."""
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp", ".h")))
+    out, h = {}, hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            data = fh.read()
+        out[f] = hashlib.sha256(data).hexdigest()[:16]
+        h.update(data)
+    with open(os.path.join(ROOT, "include", "linformer.h"), "rb") as fh:
+        data = fh.read()
+    out["linformer.h"] = hashlib.sha256(data).hexdigest()[:16]
+    h.update(data)
+    out["all"] = h.hexdigest()[:16]
+    return out
+
+
+def rocprof_us(kernel: str, workload: str):
+    """Average kernel duration (us) from the committed rocprofv3 kernel trace of this workload,
+    if it was taken on the current kernel source (profiles/kernel_times.txt); else None.
+
+    kernel_times.txt lines: <kernel> <workload> <source sha256, 16 hex> <average ns>
+    """
+    path = os.path.join(PROFILES, "kernel_times.txt")
+    if not os.path.exists(path):
+        return None
+    sha = source_hash(kernel)
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if line.startswith("#") or len(parts) != 4:
+                continue
+            if parts[0] == kernel and parts[1] == workload and parts[2] == sha:
+                return float(parts[3]) / 1e3
+    return None
+
+
 def traffic_bytes(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (copy-calibrated), from
     profiles/traffic.txt, if they were taken on the current kernel source; else None.
@@ -207,15 +245,32 @@ def run_sweep(L, synth, torch, np):
                 (f", dense {row['dense_us']:9.1f} us, {row['speedup']:.2f}x" if "dense_us" in row else ""))
             del Q, K, V, E, O, ws
     print(json.dumps({"sweep": rows, "config": {"batch": 1, "heads": 12, "head_dim": 64,
-                                                "share": "layerwise", "dtype": "bf16"}}), flush=True)
+                                                "share": "layerwise", "dtype": "bf16"},
+                      "time_basis": "median of per-call HIP event pairs on the launch stream",
+                      "source_sha": source_hashes(),
+                      "command": "python bench.py " + " ".join(sys.argv[1:])}), flush=True)
 
 
 def stack_flops(wl) -> float:
-    """Matrix flops of one pass of the encoder attention stack: per layer the input projection
-    (2 T d_model 3 d_model), Linformer attention (8 n k d per head and batch item: Kbar, Vbar,
-    scores, weighted sum) and the output projection (2 T d_model^2), T = B n tokens."""
+    """Method-equivalent matrix flops of one pass of the encoder attention stack, counted as the
+    definition states it: per layer the input projection (2 T d_model 3 d_model), Linformer
+    attention (8 n k d per head and batch item: Kbar, Vbar, scores, weighted sum) and the output
+    projection (2 T d_model^2), T = B n tokens."""
     T, dm = wl.batch * wl.n, wl.d_model
     per_layer = 2.0 * T * dm * 3 * dm + 2.0 * T * dm * dm + 8.0 * wl.batch * wl.heads * wl.n * wl.k * 64
+    return wl.layers * per_layer
+
+
+def stack_executed_flops(wl) -> float:
+    """bf16 matrix flops linformer_stack_forward executes per pass (the keys and values are
+    formed as (E X) W^T over the k projected rows, not as E (X W^T)): per layer the query
+    projection (2 T d_model^2), the sequence projection of the layer input E X (2 B k n d_model),
+    the projected keys and values (2 B k d_model 2 d_model), the scores and weighted sum
+    (4 n k d per head and batch item) and the output projection (2 T d_model^2).  The residual
+    product of the scores (e4m3, at twice the bf16 rate) is not counted."""
+    T, dm, B, k, n = wl.batch * wl.n, wl.d_model, wl.batch, wl.k, wl.n
+    per_layer = (2.0 * T * dm * dm + 2.0 * B * k * n * dm + 2.0 * B * k * dm * 2 * dm +
+                 4.0 * B * wl.heads * n * k * 64 + 2.0 * T * dm * dm)
     return wl.layers * per_layer
 
 
@@ -281,10 +336,12 @@ def run_stack_bench(args, L, synth, torch, np):
     wall = time.perf_counter() - w0
     ms = ev0.elapsed_time(ev1) / args.steps
     tokens = wl.batch * wl.n
-    flops = stack_flops(wl)
+    flops = stack_executed_flops(wl)
     tflops = flops / (ms * 1e-3) / 1e12
+    eq_flops = stack_flops(wl)
     log(f"stack: {ms * 1e3:.1f} us/step ({tokens / (ms / 1e3):.3e} tokens/s), "
-        f"{tflops:.1f} TFLOP/s")
+        f"{tflops:.1f} TFLOP/s executed ({flops / 1e9:.0f} GFLOP per step; method-equivalent "
+        f"{eq_flops / 1e9:.0f} GFLOP)")
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host cores ...")
@@ -302,7 +359,13 @@ def run_stack_bench(args, L, synth, torch, np):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "kernel": "whole step (projections, attention)",
-                     "algorithmic_flops": flops},
+                     "executed_flops": flops,
+                     "method_equivalent_flops": eq_flops,
+                     "method_equivalent_frac": round(eq_flops / (ms * 1e-3) / 1e12 /
+                                                     PEAK_BF16_TFLOPS, 4)},
+        "time_basis": "HIP events around the timed back-to-back stack calls on the launch stream",
+        "source_sha": source_hashes(),
+        "command": "python bench.py " + " ".join(sys.argv[1:]),
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
         "wall_s": round(wall, 4),
@@ -310,36 +373,126 @@ def run_stack_bench(args, L, synth, torch, np):
     print(json.dumps(out), flush=True)
 
 
-def run_memory(L, synth, torch, np):
-    """Device memory of one Linformer layer against standard attention, per batch item, and the
-    largest batch that fits on this GPU (B H=12, d=64, bf16, layerwise E = F).
+def library_allocation(torch, fn, warm: int = 2, calls: int = 3) -> int:
+    """Change of the device's free memory (hipMemGetInfo, through torch.cuda.mem_get_info) over
+    `calls` calls of `fn` after `warm` warm-up calls: the device memory the library itself takes.
+    Torch allocates nothing in between, so only the library or the runtime could move it."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(calls):
+        fn()
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    return int(free0 - free1)
 
-    Linformer: Q, K, V, O plus the library's workspace (Kbar, Vbar, split partial sums), whose
-    per-item size is the slope of linformer_workspace_size over the batch, plus E once.  Standard
-    attention as the pages' baseline computes it keeps the n x n context matrix: fp32 scores and
-    bf16 probabilities per head (6 n^2 bytes per head) besides Q, K, V, O.  The in-repo dense
-    comparator streams keys and keeps no n x n matrix, so its footprint is Q, K, V, O only.  The
-    Linformer figure is also measured: the peak allocation of a forward call at a fixed batch."""
+
+def standard_attention_bytes(torch, B, H, n, d):
+    """Peak device bytes, beyond its inputs and output, of standard softmax attention written
+    with plain torch operations as the pages' baseline computes it: the n x n scores in fp32,
+    their softmax, the probabilities in bf16, then the weighted sum of V (torch's allocator
+    sees every one of these tensors)."""
+    bf = torch.bfloat16
+    Q = torch.randn(B, H, n, d, device="cuda").to(bf)
+    K = torch.randn(B, H, n, d, device="cuda").to(bf)
+    V = torch.randn(B, H, n, d, device="cuda").to(bf)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    # fp32 operands (a transposed bf16 right operand of a batched product is avoided)
+    Kt = K.float().transpose(-1, -2).contiguous()
+    S = torch.matmul(Q.float(), Kt) * (1.0 / d ** 0.5)
+    del Kt
+    P = torch.softmax(S, dim=-1).to(bf)
+    del S
+    O = torch.matmul(P, V)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    del Q, K, V, P, O
+    torch.cuda.empty_cache()
+    return int(peak)
+
+
+def run_memory(L, synth, torch, np):
+    """Device memory of one attention layer per batch item, Linformer against standard attention,
+    and the largest batch that fits on this GPU (H = 12, d = 64, bf16, layerwise E = F) -- the
+    pages' memory figure is a ratio of such largest batches.
+
+    Measured: (1) what liblinformer itself allocates on the device -- the change of free device
+    memory around warmed-up forward, no-allocation forward, backward and stack calls (0 bytes:
+    every buffer is the caller's); (2) the caller's buffers per item -- Q, K, V, O and the
+    workspace linformer_workspace_size asks for, per item at the largest batch one call takes,
+    plus E once; (3) standard attention written with torch operations (n x n fp32 scores and
+    bf16 probabilities), its peak beyond Q, K, V, O from torch's allocator at batch 1 and 2
+    (the difference is the per-item bytes), where one item fits on the device; where it does not
+    (n = 65536), the same recipe's size as a model (6 n^2 bytes per head), labelled as such.
+    The in-repo dense comparator streams the keys and keeps no n x n matrix: its footprint is
+    Q, K, V, O, and it allocates nothing either (measured like (1))."""
     H, d = 12, 64
     free, total = torch.cuda.mem_get_info()
     budget = free - (1 << 30)   # leave 1 GiB for the runtime
+    bf = torch.bfloat16
+
+    # (1) the library's own device allocations, after warm-up
+    B, n, k = 4, 4096, 256
+    p = L.problem(B, H, n, d, k, synth.DT_BF16, synth.SHARE_LAYERWISE, 0.0)
+    Q = torch.randn(B, H, n, d, device="cuda").to(bf)
+    K = torch.randn(B, H, n, d, device="cuda").to(bf)
+    V = torch.randn(B, H, n, d, device="cuda").to(bf)
+    E = (torch.randn(1, k, n, device="cuda") / 16).to(bf)
+    O = torch.empty_like(Q)
+    wsb = L.linformer_workspace_size(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    f32 = lambda *shape: torch.empty(*shape, dtype=torch.float32, device="cuda")
+    dQ, dK, dV, dE = f32(B, H, n, d), f32(B, H, n, d), f32(B, H, n, d), f32(1, k, n)
+    bwb = L.linformer_backward_workspace_size(p)
+    bws = torch.empty(bwb, dtype=torch.uint8, device="cuda")
+    st = L.stack(2, 1024, 768, 12, 256, 2, False, 0.0)
+    X = torch.randn(2, 1024, 768, device="cuda").to(bf)
+    Wq = (torch.randn(2, 3 * 768, 768, device="cuda") * 0.02).to(bf)
+    Wo = (torch.randn(2, 768, 768, device="cuda") * 0.02).to(bf)
+    Es = (torch.randn(1, 256, 1024, device="cuda") / 16).to(bf)
+    Y = torch.empty(2, 1024, 768, dtype=bf, device="cuda")
+    swb = L.linformer_stack_workspace_size(st)
+    sws = torch.empty(swb, dtype=torch.uint8, device="cuda")
+    lib_alloc = {
+        "forward": library_allocation(torch, lambda: L.linformer_forward(p, Q, K, V, E, None, None, O, ws, wsb)),
+        "forward_noalloc": library_allocation(torch, lambda: L.linformer_forward_noalloc(p, Q, K, V, E, None, None, O)),
+        "backward": library_allocation(torch, lambda: L.linformer_backward(p, Q, K, V, E, None, None, O, dQ, dK, dV, dE, None, bws, bwb)),
+        "stack": library_allocation(torch, lambda: L.linformer_stack_forward(st, X, Wq, Wo, Es, None, Y, sws, swb)),
+        "dense_comparator": library_allocation(torch, lambda: L.attention_dense_forward(p, Q, K, V, None, O)),
+    }
+    log(f"device memory the library allocates per call after warm-up: {lib_alloc}")
+    del Q, K, V, E, O, ws, dQ, dK, dV, dE, bws, X, Wq, Wo, Es, Y, sws
+    torch.cuda.empty_cache()
+
     rows = []
     for n in (512, 4096, 65536):
         for k in (128, 256):
-            # the workspace per item at the largest batch one call takes (the position split,
-            # and with it the partial sums, shrinks as the batch grows)
+            # (2) the caller's buffers, per item at the largest batch one call takes (the
+            # position split, and with it the partial sums, shrinks as the batch grows)
             bmax = min(4096, ((1 << 31) - 1) // (H * n * d))
             pb = L.problem(bmax, H, n, d, k, synth.DT_BF16, synth.SHARE_LAYERWISE, 0.0)
             qkvo = 4 * H * n * d * 2
             lin_item = qkvo + L.linformer_workspace_size(pb) / bmax
             lin_fixed = k * n * 2
-            std_item = qkvo + 6 * H * n * n
-            flash_item = qkvo
+            # (3) standard attention: measured where one item fits, else the recipe's size
+            if n <= 4096:
+                # the first batched product allocates the BLAS workspace once: not per item
+                standard_attention_bytes(torch, 1, H, n, d)
+                s1 = standard_attention_bytes(torch, 1, H, n, d)
+                s2 = standard_attention_bytes(torch, 2, H, n, d)
+                std_extra, std_kind = s2 - s1, "measured: torch operations, peak over Q, K, V, O, slope over batch 1 -> 2"
+            else:
+                std_extra, std_kind = 6 * H * n * n, "model: 6 n^2 bytes per head (fp32 scores + bf16 probabilities); one item does not fit"
+            std_item = qkvo + std_extra
             row = {"n": n, "k": k, "linformer_bytes_per_item": int(lin_item),
-                   "standard_bytes_per_item": std_item, "streamed_dense_bytes_per_item": flash_item,
+                   "standard_bytes_per_item": int(std_item), "standard_kind": std_kind,
+                   "streamed_dense_bytes_per_item": qkvo,
                    "linformer_max_batch": int((budget - lin_fixed) // lin_item),
                    "standard_max_batch": int(budget // std_item),
-                   "streamed_dense_max_batch": int(budget // flash_item),
+                   "streamed_dense_max_batch": int(budget // qkvo),
                    "bytes_per_item_ratio_vs_standard": round(std_item / lin_item, 2),
                    "max_batch_per_call": bmax}
             row["max_batch_ratio_vs_standard"] = (
@@ -348,35 +501,14 @@ def run_memory(L, synth, torch, np):
             rows.append(row)
             log(f"n={n:6d} k={k}: Linformer {lin_item / 2**20:9.2f} MiB/item "
                 f"(max batch {row['linformer_max_batch']}), standard {std_item / 2**20:10.2f} MiB/item "
-                f"(max batch {row['standard_max_batch']}), bytes ratio "
-                f"{row['bytes_per_item_ratio_vs_standard']}")
-    # measured peak of one forward call (n = 4096, k = 256, batch 16)
-    B, n, k = 16, 4096, 256
-    p = L.problem(B, H, n, d, k, synth.DT_BF16, synth.SHARE_LAYERWISE, 0.0)
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    torch.cuda.reset_peak_memory_stats()
-    base = torch.cuda.memory_allocated()
-    Q = torch.randn(B, H, n, d, device="cuda").to(torch.bfloat16)
-    K = torch.randn(B, H, n, d, device="cuda").to(torch.bfloat16)
-    V = torch.randn(B, H, n, d, device="cuda").to(torch.bfloat16)
-    E = (torch.randn(1, k, n, device="cuda") / 16).to(torch.bfloat16)
-    O = torch.empty_like(Q)
-    wsb = L.linformer_workspace_size(p)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    torch.cuda.reset_peak_memory_stats()
-    L.linformer_forward(p, Q, K, V, E, None, None, O, ws, wsb)
-    torch.cuda.synchronize()
-    peak = torch.cuda.max_memory_allocated() - base
-    expect = B * (4 * H * n * d * 2) + k * n * 2 + wsb
-    log(f"measured peak of a forward call at B={B} n={n} k={k}: {peak / 2**20:.1f} MiB "
-        f"(Q, K, V, O, E and workspace: {expect / 2**20:.1f} MiB)")
-    print(json.dumps({"memory": rows, "free_bytes": free, "total_bytes": total,
-                      "budget_bytes": budget,
-                      "measured": {"batch": B, "n": n, "k": k, "peak_bytes": int(peak),
-                                   "expected_bytes": int(expect)},
+                f"(max batch {row['standard_max_batch']}; {std_kind.split(':')[0]}), ratio "
+                f"{row['max_batch_ratio_vs_standard']}")
+    print(json.dumps({"memory": rows, "library_allocation_bytes": lib_alloc,
+                      "free_bytes": free, "total_bytes": total, "budget_bytes": budget,
                       "config": {"heads": H, "head_dim": d, "share": "layerwise",
-                                 "dtype": "bf16"}}), flush=True)
+                                 "dtype": "bf16"},
+                      "source_sha": source_hashes(),
+                      "command": "python bench.py " + " ".join(sys.argv[1:])}), flush=True)
 
 
 PEAK_F32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix-core peak (published)
@@ -431,6 +563,9 @@ def run_backward(args, L, synth, torch, np):
         "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_F32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_F32_MFMA_TFLOPS, 4), "traffic": None,
                      "kernel": "whole backward step", "algorithmic_flops": flops},
+        "time_basis": "HIP events around the timed back-to-back backward calls",
+        "source_sha": source_hashes(),
+        "command": "python bench.py " + " ".join(sys.argv[1:]),
         "device": torch.cuda.get_device_name(0)}), flush=True)
 
 
@@ -602,12 +737,17 @@ def main():
     dom = "attend"
     kd = kern[dom]
     traffic = traffic_bytes(dom, wl.name)
+    rp_us = rocprof_us(dom, wl.name)
     roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(kd["gbs"] / PEAK_HBM_GBS, 4),
                 "traffic": traffic, "kernel": "attend_bf16_kernel", "avg_us": round(kd["us"], 2),
                 "algorithmic_bytes": kd["bytes"],
                 "mfma_tflops": round(kd["tflops"], 1),
-                "mfma_frac": round(kd["tflops"] / PEAK_BF16_TFLOPS, 4)}
+                "mfma_frac": round(kd["tflops"] / PEAK_BF16_TFLOPS, 4),
+                # the same bytes over the committed profiler duration of this kernel source
+                "rocprof_us": None if rp_us is None else round(rp_us, 2),
+                "frac_rocprof": None if rp_us is None else
+                round(kd["bytes"] / (rp_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
     step_bytes = kern["project"]["bytes"] + kern["attend"]["bytes"]
     step_flops = kern["project"]["flops"] + kern["attend"]["flops"]
     roof_us = max(step_bytes / (PEAK_HBM_GBS * 1e9), step_flops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
@@ -679,6 +819,16 @@ def main():
                           "frac": round(roof_us / (ms * 1e3), 4)},
         "valid_work_roofline": valid,
         "kernels_us": {k: round(v["us"], 2) for k, v in kern.items()},
+        "bytes_basis": "padded: Q, K, V, O over the padded length n, each distinct E/F matrix "
+                       "once, Kbar and Vbar (bf16) once each way; the kernels skip rows past "
+                       "each length (valid_work_roofline counts only the valid rows)",
+        "time_basis": "ms_per_step: HIP events around the timed back-to-back forward calls on "
+                      "the launch stream; kernels_us / roofline.avg_us: HIP events around "
+                      "back-to-back launches of one half (includes the dispatch gap between "
+                      "launches); roofline.rocprof_us: average kernel duration in the committed "
+                      "rocprofv3 trace at this kernel source (profiles/kernel_times.txt)",
+        "source_sha": source_hashes(),
+        "command": "python bench.py " + " ".join(sys.argv[1:]),
         "dense_comparator": dense,
         "copy_ceiling_gbs": round(copy_gbs, 1),
         "cpu_baseline": cpu,
