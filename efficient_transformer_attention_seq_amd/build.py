@@ -18,8 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblinformer.so")
 
-HIP_SOURCES = ["proj_bf16.hip", "attend_bf16.hip", "f32_path.hip", "dense_bf16.hip",
-               "linear_bf16.hip", "conv_bf16.hip", "backward_f32.hip"]
+HIP_SOURCES = ["proj_bf16.hip", "attend_bf16.hip", "fused_bf16.hip", "f32_path.hip",
+               "dense_bf16.hip", "linear_bf16.hip", "conv_bf16.hip", "backward_f32.hip"]
 HOST_SOURCES = ["api.cpp"]  # host-only code, compiled as HIP for the runtime headers
 
 ARCH = "gfx950"

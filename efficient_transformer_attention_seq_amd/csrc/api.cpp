@@ -403,6 +403,14 @@ size_t forward_ws_bytes(const lf_problem* p, const lf::ProjGeom& g) {
            round_up(part_bytes(p, g), 256);
 }
 
+// The whole layer in one launch (fused_bf16.hip): bf16, short sequences, and one matrix
+// projecting both the keys and the values (LINFORMER_FUSED=0 turns it off, for measurements).
+bool use_fused(const lf_problem* p, const void* E, const void* F) {
+    if (p->dtype != LF_BF16 || F != E || !lf::fused_supported(p->n, p->k)) return false;
+    const char* v = std::getenv("LINFORMER_FUSED");
+    return !(v && v[0] == '0');
+}
+
 // Validation of a forward call, everything but the device; `own_ws`: the workspace is the
 // library's fixed scratch (not the caller's), so only its size is checked, by the caller.
 struct FwdPlan {
@@ -444,6 +452,22 @@ int forward_run(const lf_problem* p, const FwdPlan& pl, const void* Q, const voi
     void* Vbar = w + pl.kb;
     void* part = pl.pb ? (void*)(w + pl.kb + pl.vb) : nullptr;
     hipStream_t s = (hipStream_t)stream;
+    if (use_fused(p, E, pl.Fr)) {
+        lf::FusedBf16Args f{};
+        f.Q = (const uint16_t*)Q;
+        f.K = (const uint16_t*)K;
+        f.V = (const uint16_t*)V;
+        f.E = (const uint16_t*)E;
+        f.lengths = lengths;
+        f.O = (uint16_t*)O;
+        f.B = p->batch;
+        f.H = p->heads;
+        f.n = p->n;
+        f.k = p->k;
+        f.e_heads = p->share == LF_SHARE_NONE ? p->heads : 1;
+        f.c = eff_scale(p) * lf::kLog2e;
+        return launch_status(lf::launch_fused_bf16(f, s));
+    }
     int st = do_project(p, K, V, E, pl.Fr, lengths, Kbar, Vbar, part, pl.g, s);
     if (st) return st;
     return do_attend(p, Q, Kbar, Vbar, lengths, O, s);

@@ -1,0 +1,264 @@
+// Linformer attention for short sequences in one launch (n <= 1024, bf16, one projection matrix
+// for the keys and the values: key-value or layerwise sharing, or per-head E_h with F_h = E_h).
+// One workgroup per (b, h): it projects that head's keys and values along the sequence,
+// Kbar = E . K and Vbar = E . V over the valid positions (Linformer 요약 설명, section "Model"),
+// straight into LDS in the attention's operand layouts (attend_core.h), then attends every query
+// tile of the head there.  Kbar and Vbar never reach HBM, and nothing waits on a second launch:
+// at n = 512 the separate projection and attention pass of them would add a quarter to the
+// layer's HBM bytes (the regime of the n = 512 row of "Inference-time Efficiency Results").
+//
+// Projection (k slots x 128 columns: 64 of Kbar, 64 of Vbar, reduced over the positions): wave w
+// computes the 32 WM slots from 32 WM (w % 4) of Kbar (w < 4) or Vbar (w >= 4) with
+// v_mfma_f32_32x32x16_bf16, the K/V rows as the A operand (read transposed with
+// ds_read_b64_tr_b16) and E as the B operand.  Each 64-position step of E's k rows and of the
+// head's K and V rows is copied global -> LDS by direct-to-LDS buffer loads (1 KB per wave
+// instruction, whole 128-byte rows) in a ring of 3 (k = 256) or 4 (k = 128) stages; K/V
+// descriptors are sized to the valid
+// length, so positions past it read as zero.  The epilogue writes x = c Kbar (c = scale log2 e)
+// as the bf16 plane, its e4m3 residual with one power-of-two scale per row half, and Vbar in
+// bf16, into the head's planes, which reuse the ring's LDS.
+// Attention: the waves take the head's 32-query tiles in turn (tile_math / tile_store of
+// attend_core.h), the first tile's Q loaded before the projection starts and each next tile's Q
+// during the current one; the rows past the last valid tile are zero-filled with streaming
+// stores issued at the start, so they drain under the projection.
+#include "attend_core.h"
+
+namespace lf {
+namespace {
+
+using namespace attn;
+constexpr int kThreads = 512;   // 8 waves
+constexpr int kStep = 64;       // positions per projection stage
+
+__device__ __forceinline__ int swz_e(int r) { return (r ^ (r >> 3)) & 7; }
+
+template <int KB>
+struct FusedLayout {
+    using Ly = AttnLayout<KB>;
+    static constexpr int K = Ly::K;
+    static constexpr int E_STAGE = K * 128;       // E: k rows x 64 positions, bf16
+    static constexpr int X_TILE = kStep * 128;    // K or V: 64 positions x 64 columns, bf16
+    static constexpr int STAGE = E_STAGE + 2 * X_TILE;
+    static constexpr int NS = 144 * 1024 / STAGE > 4 ? 4 : 144 * 1024 / STAGE;   // ring depth
+    static constexpr int RING = NS * STAGE;
+    static constexpr int OFF_STG = Ly::BYTES;     // per-wave tile staging after the planes
+    static constexpr int ATT = OFF_STG + 8 * 32 * 128;
+    static constexpr int BYTES = RING > ATT ? RING : ATT;
+    // direct-to-LDS instructions per stage (E rows, then K rows, then V rows), per wave
+    static constexpr int NI = K / 8 + 16;
+    static constexpr int PER_WAVE = NI / 8;
+    static_assert(NI % 8 == 0, "whole instructions per wave");
+};
+
+template <int N>
+__device__ __forceinline__ void vmcnt_le() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int KB>
+__global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
+    using FL = FusedLayout<KB>;
+    using Ly = AttnLayout<KB>;
+    constexpr int K = Ly::K;
+    constexpr int WM = KB / 4;   // 32-slot blocks per wave: the k slots over 4 waves
+    __shared__ __attribute__((aligned(16))) uint8_t smem[FL::BYTES];
+    const uint32_t lds0 = lds_addr(smem);
+
+    const int bh = blockIdx.x;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int L = clamp_len(a.lengths, b, a.n);
+    const int ntiles = (L + kTileQ - 1) / kTileQ;
+    const size_t rowbase = (size_t)bh * a.n;
+
+    // ---- the first tile's Q, in flight during the projection
+    u32x4 qraw[4];
+    auto load_q = [&](int tile) {
+        const u32x4* src = (const u32x4*)(a.Q + (rowbase + (size_t)tile * kTileQ) * kHeadDim) + lane;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qraw[i] = src[64 * i];
+    };
+    if (wave < ntiles) load_q(wave);
+
+    // ---- zero the rows past the last valid tile (streaming stores, drained under the work)
+    {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        u32x4* blk = (u32x4*)(a.O + (rowbase + (size_t)ntiles * kTileQ) * kHeadDim);
+        const int nz = (a.n - ntiles * kTileQ) * 8;   // 16-byte chunks
+        for (int c = tid; c < nz; c += kThreads) __builtin_nontemporal_store(zero, &blk[c]);
+    }
+
+    // ---- projection
+    const uint16_t* Eh = a.E + (size_t)(a.e_heads > 1 ? h : 0) * K * a.n;
+    const i32x4 rsrc_e = make_rsrc(Eh, (uint32_t)K * a.n * 2);
+    const uint32_t xbytes = L > 0 ? (uint32_t)(((size_t)(L - 1) * kHeadDim + kHeadDim) * 2) : 0u;
+    const i32x4 rsrc_k = make_rsrc(a.K + rowbase * kHeadDim, xbytes);
+    const i32x4 rsrc_v = make_rsrc(a.V + rowbase * kHeadDim, xbytes);
+    const int lrow = lane >> 3, lpc = lane & 7;
+    const int nsteps = (L + kStep - 1) / kStep;
+    auto issue = [&](int step, int slot) {
+        const int t0 = step * kStep;
+        const uint32_t sbase = lds0 + (uint32_t)slot * FL::STAGE;
+#pragma unroll
+        for (int p = 0; p < FL::PER_WAVE; ++p) {
+            const int j = wave + 8 * p;   // instruction index, the same split in every stage
+            if (j < K / 8) {              // E rows 8 j .. 8 j + 7, chunks swizzled by swz_e(row)
+                const int r = j * 8 + lrow;
+                const int lc = lpc ^ swz_e(r);
+                dma16(rsrc_e, sbase + j * 1024, (uint32_t)((size_t)r * a.n + t0 + lc * 8) * 2);
+            } else {                      // K (then V) positions 8 q .. 8 q + 7, 32-byte blocks
+                const int jj = j - K / 8;  // swizzled by the position's low bits
+                const int q = jj & 7;
+                const int tl = q * 8 + lrow;
+                const int lc = 2 * ((lpc >> 1) ^ (tl & 3)) + (lpc & 1);
+                const uint32_t off = (uint32_t)(((t0 + tl) * kHeadDim + lc * 8) * 2);
+                const uint32_t dst = sbase + FL::E_STAGE + (jj >> 3) * FL::X_TILE + q * 1024;
+                dma16((jj >> 3) ? rsrc_v : rsrc_k, dst, off);
+            }
+        }
+    };
+    const int which = wave >> 2, sb = wave & 3;
+    f32x16 acc[2][WM];   // [ct][mt]: rows = 32 columns ct, columns = 32 slots mt
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[ct][mt][j] = 0.0f;
+    int e_off[WM], e_sw[WM];
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt) {
+        const int r = 32 * (sb * WM + mt) + l32;
+        e_off[mt] = r * 128;
+        e_sw[mt] = swz_e(r);
+    }
+    const int grp16 = lane >> 4, s16 = lane & 15;
+    const int tq = 8 * (grp16 >> 1) + (s16 >> 2);
+    const int cb = grp16 & 1;
+    const int cin = (s16 & 3) * 8;
+    constexpr int NS = FL::NS;
+    for (int i = 0; i < NS - 1 && i < nsteps; ++i) issue(i, i);
+    for (int i = 0; i < nsteps; ++i) {
+        // this wave's share of stage i has landed once at most the younger stages are in flight
+        if (i + NS - 2 < nsteps) vmcnt_le<(NS - 2) * FL::PER_WAVE>();
+        else vmcnt_le<0>();
+        __syncthreads();   // everyone's has, and step i - 1's reads of its slot are done
+        if (i + NS - 1 < nsteps) issue(i + NS - 1, (i + NS - 1) % NS);
+        const uint8_t* st = smem + (size_t)(i % NS) * FL::STAGE;
+        const uint8_t* xt = st + FL::E_STAGE + which * FL::X_TILE;
+        bf16x8 ev[2][WM], xo[2][2];
+        auto load_ops = [&](int ks, bf16x8 (&e)[WM], bf16x8 (&x)[2]) {
+#pragma unroll
+            for (int mt = 0; mt < WM; ++mt)
+                e[mt] = *(const bf16x8*)(st + e_off[mt] + (((2 * ks + hh) ^ e_sw[mt]) << 4));
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const int cblk = ct * 2 + cb;
+                s16x4 v[2];
+#pragma unroll
+                for (int rd = 0; rd < 2; ++rd) {
+                    const int t = ks * 16 + tq + 4 * rd;
+                    const uint8_t* p = xt + t * 128 + ((cblk ^ (t & 3)) << 5) + cin;
+                    v[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(uintptr_t)(
+                            (__attribute__((address_space(3))) const uint8_t*)p));
+                }
+                x[ct] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        };
+        load_ops(0, ev[0], xo[0]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) load_ops(ks + 1, ev[(ks + 1) & 1], xo[(ks + 1) & 1]);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int mt = 0; mt < WM; ++mt)
+                    acc[ct][mt] = mfma32(xo[ks & 1][ct], ev[ks & 1][mt], acc[ct][mt]);
+        }
+    }
+    __syncthreads();   // every wave is done with the ring: the head's planes take its place
+
+    // ---- epilogue: lane (l32, hh) holds, for slot r = 32 (sb WM + mt) + l32, the columns
+    // d = 32 ct + 8 q + 4 hh + (0..3)
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt) {
+        const int r = 32 * (sb * WM + mt) + l32;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const f32x16& x = acc[ct][mt];
+            if (which == 1) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x2 v = {pack_bf16x2(x[4 * q], x[4 * q + 1]), pack_bf16x2(x[4 * q + 2], x[4 * q + 3])};
+                    *(u32x2*)(smem + Ly::OFF_V + r * 128 + (((2 * ct + (q >> 1)) ^ (r & 3)) << 5) +
+                              16 * (q & 1) + 8 * hh) = v;
+                }
+            } else {
+                float lo[16];
+                float m = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x2 hv = {hi_pair(a.c * x[4 * q], a.c * x[4 * q + 1], lo[4 * q], lo[4 * q + 1]),
+                                      hi_pair(a.c * x[4 * q + 2], a.c * x[4 * q + 3], lo[4 * q + 2], lo[4 * q + 3])};
+                    *(u32x2*)(smem + r * 128 + (((4 * ct + q) ^ swz16(r)) << 4) + 8 * hh) = hv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(lo[4 * q + e]));
+                }
+                m = fmaxf(m, other_half(m, hh));   // the row half's 32 residuals
+                const int sh = lo_shift(m);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int pos = 32 * (q & 1) + 16 * ct + 8 * (q >> 1) + 4 * hh;   // lo_pos
+                    *(uint32_t*)(smem + Ly::OFF_L + r * 64 + (((pos >> 4) ^ ((r >> 1) & 3)) << 4) +
+                                 (pos & 15)) =
+                        lo_bytes(lo[4 * q], lo[4 * q + 1], lo[4 * q + 2], lo[4 * q + 3], sh);
+                }
+                if (hh == 0) smem[Ly::OFF_S + r * 2 + ct] = (uint8_t)(127 - sh);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- attention over the head's query tiles, tile j to wave j % 8
+    if (wave >= ntiles) return;
+    const Lanes ln = attn_lanes<KB>(lds0, lane);
+    int scl[2];
+    attn_scales<KB>(smem, lane, scl);
+    uint32_t coff[4];
+    stage_offsets(lane, coff);
+    const uint32_t stg = lds0 + FL::OFF_STG + wave * (kTileQ * 128);
+    f32x16 bias;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) bias[j] = 0.0f;
+    bool bias_dirty = false;
+    bf16x8 qop[4];
+    for (int tile = wave; tile < ntiles; tile += 8) {
+        stage_q(stg, coff, qraw, lane, qop);
+        f32x16 o0, o1;
+        float z;
+        tile_math<KB>(ln, qop, scl, hh, bias, bias_dirty, o0, o1, z, [&]() {
+            if (tile + 8 < ntiles) load_q(tile + 8);
+        });
+        tile_store(stg, coff, lane, o0, o1, z, a.O + (rowbase + (size_t)tile * kTileQ) * kHeadDim,
+                   tile * kTileQ, L);
+    }
+}
+
+}  // namespace
+
+bool fused_supported(int n, int k) { return n <= 1024 && (k == 128 || k == 256); }
+
+hipError_t launch_fused_bf16(const FusedBf16Args& a, hipStream_t stream) {
+    const dim3 grid(a.B * a.H), block(kThreads);
+    switch (a.k) {
+        case 128: hipLaunchKernelGGL(fused_bf16_kernel<4>, grid, block, 0, stream, a); break;
+        case 256: hipLaunchKernelGGL(fused_bf16_kernel<8>, grid, block, 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace lf

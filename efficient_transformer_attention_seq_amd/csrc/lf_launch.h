@@ -190,6 +190,22 @@ struct DenseBf16Args {
     float c;  // scale * log2(e)
 };
 
+// Fused short-sequence path (fused_bf16.hip): projection into LDS and attention in one launch,
+// one workgroup per (b, h); one projection matrix for keys and values.
+struct FusedBf16Args {
+    const uint16_t* Q;
+    const uint16_t* K;
+    const uint16_t* V;
+    const uint16_t* E;      // [e_heads, k, n], projects both the keys and the values
+    const int32_t* lengths;
+    uint16_t* O;
+    int B, H, n, k;
+    int e_heads;            // H (per-head E_h) or 1
+    float c;                // scale * log2(e)
+};
+bool fused_supported(int n, int k);
+hipError_t launch_fused_bf16(const FusedBf16Args& a, hipStream_t stream);
+
 // Projection geometry for a problem (deterministic; `split_override` > 0 forces S,
 // `cfg_override` names a tile configuration).  Returns false if the shape is unsupported.
 bool proj_geometry(int B, int H, int n, int k, int share, int split_override,
