@@ -191,6 +191,18 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
         const int L = s_len[p0.b];
         const size_t rowbase = (size_t)bh * a.n;
 
+        // this wave's first tile of the segment (tiles t .. t+7 are taken statically): its Q is
+        // loaded before the head's planes, so the two loads' latencies overlap
+        int tt = t + wave;
+        u32x4 qraw[4];   // the tile as loaded: row 8 i + lane / 8, chunk lane % 8, i = 0..3
+        auto load_q = [&](int tile) {
+            const int q0 = (p0.j + (tile - t)) * kTileQ;
+            const u32x4* src = (const u32x4*)(a.Q + (rowbase + q0) * kHeadDim) + lane;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qraw[i] = src[64 * i];
+        };
+        if (tt < seg_end) load_q(tt);
+
         // ---- fill LDS with this head's Kbar planes and Vbar
         __syncthreads();   // previous segment's readers are done with the LDS planes
         {
@@ -212,8 +224,8 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
                 dma16(rl, lds0 + OFF_L + I * 1024, (uint32_t)(r * 64 + ((ch ^ ((r >> 1) & 3)) << 4)));
             }
             if (wave == 0) dma16(rs, lds0 + OFF_S, (uint32_t)(lane * 16));   // past K*2: zeros
-            __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));   // vmcnt(0)
-            if (tid == 0) s_next = 8;   // tiles t .. t+7 are taken statically below
+            __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));   // vmcnt(0): Q too
+            if (tid == 0) s_next = 8;   // tiles t .. t+7 are taken statically
         }
         __syncthreads();
         int scl[2];
@@ -221,15 +233,7 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
 
         // ---- tiles of this segment, taken dynamically by the waves from an LDS counter (so waves
         // that finish early take more), Q of the next tile prefetched during the current one
-        int tt = t + wave;
         bf16x8 qop[4];   // operand layout: columns 16 ks + 8 hh + (0..7) of query q0 + l32
-        u32x4 qraw[4];   // the tile as loaded: row 8 i + lane / 8, chunk lane % 8, i = 0..3
-        auto load_q = [&](int tile) {
-            const int q0 = (p0.j + (tile - t)) * kTileQ;
-            const u32x4* src = (const u32x4*)(a.Q + (rowbase + q0) * kHeadDim) + lane;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) qraw[i] = src[64 * i];
-        };
         uint32_t coff[4];
         stage_offsets(lane, coff);
         const uint32_t stg = lds_addr(&s_stage[wave][0]);
@@ -244,7 +248,6 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
 #pragma unroll
         for (int j = 0; j < 16; ++j) bias[j] = 0.0f;
         bool bias_dirty = false;
-        if (tt < seg_end) load_q(tt);
         int tnext = t + __builtin_amdgcn_readfirstlane(grab_raw());
         int gv = 0;              // reply of the grab for the tile after tt, if `pending`
         bool pending = false;
