@@ -411,6 +411,17 @@ bool use_fused(const lf_problem* p, const void* E, const void* F) {
     return !(v && v[0] == '0');
 }
 
+// The stack layer's projected keys and values and its attention in one launch (fused_bf16.hip,
+// stack form): k of 128 or 256, and enough (b, h) pairs to occupy a quarter of the compute units
+// (LINFORMER_FUSED=0 turns it off, =force turns it on regardless of the pair count).
+bool stack_fused(const lf_stack* s) {
+    const char* v = std::getenv("LINFORMER_FUSED");
+    if (v && v[0] == '0') return false;
+    if (s->k != 128 && s->k != 256) return false;
+    if (v && std::strcmp(v, "force") == 0) return true;
+    return (long long)s->batch * s->heads >= 64;
+}
+
 // Validation of a forward call, everything but the device; `own_ws`: the workspace is the
 // library's fixed scratch (not the caller's), so only its size is checked, by the caller.
 struct FwdPlan {
@@ -735,6 +746,25 @@ int linformer_stack_forward(const lf_stack* s, const void* X, const void* Wqkv, 
         pa.g = g;
         st = launch_status(lf::launch_proj_bf16(pa, strm));
         if (st) return st;
+        if (stack_fused(s)) {
+            // Kbar, Vbar = Xbar_b [W_K; W_V]_h^T per (b, h) into LDS, then the attention, in one
+            // launch (fused_bf16.hip, stack form)
+            lf::FusedBf16Args f{};
+            f.Q = Qp;
+            f.K = Wl + dm * dm;   // W_K rows, then W_V rows
+            f.E = Xbar;
+            f.lengths = lengths;
+            f.O = O;
+            f.B = s->batch;
+            f.H = s->heads;
+            f.n = s->n;
+            f.k = s->k;
+            f.e_heads = 1;
+            f.c = c;
+            f.dm = D;
+            st = launch_status(lf::launch_fused_bf16(f, strm));
+            if (st) return st;
+        } else {
         // Kbar | Vbar = Xbar [W_K; W_V]^T, Kbar straight into the attention's format
         lf::LinearBf16Args kv{};
         kv.W = Wl + dm * dm;
@@ -756,6 +786,7 @@ int linformer_stack_forward(const lf_stack* s, const void* X, const void* Wqkv, 
         if (st) return st;
         st = do_attend(&p, Qp, Kbar, Vbar, lengths, O, strm);
         if (st) return st;
+        }
         // output projection of the concatenated heads
         lf::LinearBf16Args o{};
         o.W = Wol;

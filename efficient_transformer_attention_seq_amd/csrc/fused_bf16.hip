@@ -55,7 +55,7 @@ __device__ __forceinline__ void vmcnt_le() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int KB>
+template <int KB, bool STACK>
 __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
     using FL = FusedLayout<KB>;
     using Ly = AttnLayout<KB>;
@@ -90,24 +90,45 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
         for (int c = tid; c < nz; c += kThreads) __builtin_nontemporal_store(zero, &blk[c]);
     }
 
-    // ---- projection
-    const uint16_t* Eh = a.E + (size_t)(a.e_heads > 1 ? h : 0) * K * a.n;
-    const i32x4 rsrc_e = make_rsrc(Eh, (uint32_t)K * a.n * 2);
-    const uint32_t xbytes = L > 0 ? (uint32_t)(((size_t)(L - 1) * kHeadDim + kHeadDim) * 2) : 0u;
-    const i32x4 rsrc_k = make_rsrc(a.K + rowbase * kHeadDim, xbytes);
-    const i32x4 rsrc_v = make_rsrc(a.V + rowbase * kHeadDim, xbytes);
+    // ---- projection.  Sequence form: the slot rows are E's (positions contiguous), the columns
+    // the head's K, V rows (read transposed), 64 positions per stage, over the valid length.
+    // Stack form: the slot rows are the head's batch item's projected input Xbar_b (features
+    // contiguous; stage j is its head-planar block j, features 64 j .. 64 j + 63), the columns
+    // the rows 64 h .. 64 h + 63 of W_K and of W_V (features contiguous), over all d_model features.
     const int lrow = lane >> 3, lpc = lane & 7;
-    const int nsteps = (L + kStep - 1) / kStep;
+    i32x4 rsrc_e, rsrc_k, rsrc_v;
+    int nsteps;
+    if constexpr (STACK) {
+        rsrc_e = make_rsrc(a.E + (size_t)b * a.H * K * kHeadDim, (uint32_t)a.H * K * kHeadDim * 2);
+        rsrc_k = make_rsrc(a.K, (uint32_t)((size_t)2 * a.dm * a.dm * 2));   // W_K then W_V
+        rsrc_v = rsrc_k;
+        nsteps = a.dm / kStep;
+    } else {
+        const uint16_t* Eh = a.E + (size_t)(a.e_heads > 1 ? h : 0) * K * a.n;
+        rsrc_e = make_rsrc(Eh, (uint32_t)K * a.n * 2);
+        const uint32_t xbytes = L > 0 ? (uint32_t)(((size_t)(L - 1) * kHeadDim + kHeadDim) * 2) : 0u;
+        rsrc_k = make_rsrc(a.K + rowbase * kHeadDim, xbytes);
+        rsrc_v = make_rsrc(a.V + rowbase * kHeadDim, xbytes);
+        nsteps = (L + kStep - 1) / kStep;
+    }
     auto issue = [&](int step, int slot) {
         const int t0 = step * kStep;
         const uint32_t sbase = lds0 + (uint32_t)slot * FL::STAGE;
 #pragma unroll
         for (int p = 0; p < FL::PER_WAVE; ++p) {
             const int j = wave + 8 * p;   // instruction index, the same split in every stage
-            if (j < K / 8) {              // E rows 8 j .. 8 j + 7, chunks swizzled by swz_e(row)
+            if (j < K / 8) {              // slot rows 8 j .. 8 j + 7, chunks swizzled by swz_e(row)
                 const int r = j * 8 + lrow;
                 const int lc = lpc ^ swz_e(r);
-                dma16(rsrc_e, sbase + j * 1024, (uint32_t)((size_t)r * a.n + t0 + lc * 8) * 2);
+                const size_t e = STACK ? ((size_t)step * K + r) * kHeadDim + lc * 8
+                                       : (size_t)r * a.n + t0 + lc * 8;
+                dma16(rsrc_e, sbase + j * 1024, (uint32_t)(e * 2));
+            } else if constexpr (STACK) {   // W rows: 64 of W_K then 64 of W_V, as slot rows are
+                const int wr = (j - K / 8) * 8 + lrow;
+                const int lc = lpc ^ swz_e(wr);
+                const size_t grow = (size_t)(wr >> 6) * a.dm + 64 * h + (wr & 63);
+                dma16(rsrc_k, sbase + FL::E_STAGE + (j - K / 8) * 1024,
+                      (uint32_t)((grow * a.dm + t0 + lc * 8) * 2));
             } else {                      // K (then V) positions 8 q .. 8 q + 7, 32-byte blocks
                 const int jj = j - K / 8;  // swizzled by the position's low bits
                 const int q = jj & 7;
@@ -155,6 +176,11 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
                 e[mt] = *(const bf16x8*)(st + e_off[mt] + (((2 * ks + hh) ^ e_sw[mt]) << 4));
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
+                if constexpr (STACK) {   // W rows 64 which + 32 ct + l32, features contiguous
+                    const int wr = 64 * which + 32 * ct + l32;
+                    x[ct] = *(const bf16x8*)(st + FL::E_STAGE + wr * 128 + (((2 * ks + hh) ^ swz_e(wr)) << 4));
+                    continue;
+                }
                 const int cblk = ct * 2 + cb;
                 s16x4 v[2];
 #pragma unroll
@@ -253,9 +279,17 @@ bool fused_supported(int n, int k) { return n <= 1024 && (k == 128 || k == 256);
 
 hipError_t launch_fused_bf16(const FusedBf16Args& a, hipStream_t stream) {
     const dim3 grid(a.B * a.H), block(kThreads);
+    if (a.dm > 0 && (a.dm % kStep || a.dm != 64 * a.H)) return hipErrorInvalidValue;
+    const bool stack = a.dm > 0;
     switch (a.k) {
-        case 128: hipLaunchKernelGGL(fused_bf16_kernel<4>, grid, block, 0, stream, a); break;
-        case 256: hipLaunchKernelGGL(fused_bf16_kernel<8>, grid, block, 0, stream, a); break;
+        case 128:
+            if (stack) hipLaunchKernelGGL((fused_bf16_kernel<4, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((fused_bf16_kernel<4, false>), grid, block, 0, stream, a);
+            break;
+        case 256:
+            if (stack) hipLaunchKernelGGL((fused_bf16_kernel<8, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((fused_bf16_kernel<8, false>), grid, block, 0, stream, a);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -190,8 +190,11 @@ struct DenseBf16Args {
     float c;  // scale * log2(e)
 };
 
-// Fused short-sequence path (fused_bf16.hip): projection into LDS and attention in one launch,
-// one workgroup per (b, h); one projection matrix for keys and values.
+// Fused path (fused_bf16.hip): projection into LDS and attention in one launch, one workgroup per
+// (b, h).  Sequence form (dm = 0): Kbar = E_h K, Vbar = E_h V over the valid positions, one
+// projection matrix for keys and values.  Stack form (dm = d_model): Kbar = Xbar_b W_K,h^T,
+// Vbar = Xbar_b W_V,h^T over the d_model features, with E = Xbar ([B, H, k, 64], the layer input
+// projected along the sequence) and K = W (the layer's rows of W_K then W_V, [2 dm, dm]).
 struct FusedBf16Args {
     const uint16_t* Q;
     const uint16_t* K;
@@ -202,6 +205,7 @@ struct FusedBf16Args {
     int B, H, n, k;
     int e_heads;            // H (per-head E_h) or 1
     float c;                // scale * log2(e)
+    int dm;                 // 0, or d_model for the stack form
 };
 bool fused_supported(int n, int k);
 hipError_t launch_fused_bf16(const FusedBf16Args& a, hipStream_t stream);

@@ -75,6 +75,35 @@ def test_stack_parity(batch, n, d_model, k, layers):
     assert err <= END_TOL
 
 
+# The stack form of the fused kernel (projected keys and values of each (b, h) computed into LDS
+# from the layer's projected input and W_K, W_V, then the attention, in one launch) serves k of 128
+# or 256; forced here on small shapes, with padding, and compared with the two-launch path (the
+# projected-key GEMM, then the attention kernel).
+@pytest.mark.parametrize("batch,n,d_model,k,layers,lens", [
+    (2, 256, 384, 128, 2, None),
+    (1, 512, 768, 256, 2, None),
+    (3, 320, 192, 128, 2, [320, 77, 1]),
+])
+def test_stack_fused_parity(batch, n, d_model, k, layers, lens):
+    wl = _stack_wl(batch, n, d_model, k, layers, seed=5)
+    G.log(f"stack fused {wl.name} lengths {lens}")
+    si = synth.make_stack_inputs(wl, lengths=lens)
+    with G.env(LINFORMER_FUSED="force"):
+        Y, ok = G.run_stack(si, keep_layers=True, guard=True)
+    assert ok, "stray writes outside Y"
+    assert np.all(np.isfinite(Y))
+    _check_layers(si, Y)
+    if lens is not None:
+        for l in range(wl.layers):
+            for b, Lb in enumerate(lens):
+                assert np.all(Y[l][b, Lb:] == 0.0)
+    with G.env(LINFORMER_FUSED=0):
+        Y2, _ = G.run_stack(si, keep_layers=True)
+    diff = orc.slice_rel_err(Y[-1], Y2[-1])
+    G.log(f"  fused vs two-launch, last layer: {diff:.3e}")
+    assert diff <= 1e-2
+
+
 def test_stack_last_layer_only_matches_kept():
     wl = _stack_wl(2, 256, 384, 64, 3)
     si = synth.make_stack_inputs(wl)
