@@ -27,7 +27,11 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "efficient_transformer_attention_seq_amd", "csrc")
-KERNEL_SOURCES = {"attend": "attend_bf16.hip", "project": "proj_bf16.hip"}
+# the source files each kernel's code comes from (a recorded time or traffic is valid only while
+# their hash is unchanged)
+KERNEL_SOURCES = {"attend": ("attend_bf16.hip", "attend_core.h", "lf_device.h"),
+                  "project": ("proj_bf16.hip", "lf_device.h"),
+                  "fused": ("fused_bf16.hip", "attend_core.h", "lf_device.h")}
 
 
 def log(*a):
@@ -35,8 +39,31 @@ def log(*a):
 
 
 def source_hash(kernel: str) -> str:
-    with open(os.path.join(CSRC, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def uses_fused(wl, conv: bool) -> bool:
+    """Whether linformer_forward runs this workload as the one-launch fused kernel: the library's
+    rule (bf16, n <= 1024, k of 128 or 256, one matrix for keys and values)."""
+    return (not conv and wl.dtype == 1 and wl.n <= 1024 and wl.k in (128, 256)
+            and not wl.separate_f and os.environ.get("LINFORMER_FUSED", "1") != "0")
+
+
+def step_algorithmic(wl, conv: bool = False):
+    """(bytes, flops) of one forward step as the scope table counts the method's work: Q, K, V
+    read and O written once over the padded length, each distinct E/F matrix read once (the
+    window weights of the convolution compression are negligible); 8 n k d flops per (b, h).
+    The Kbar/Vbar intermediates are not counted."""
+    B, H, n, d, k = wl.batch, wl.heads, wl.n, wl.d, wl.k
+    eb = 2 if wl.dtype == 1 else 4
+    n_mats = wl.e_heads * (2 if wl.separate_f else 1)
+    byts = 4 * B * H * n * d * eb + (0 if conv else n_mats * k * n * eb)
+    flops = B * H * (4.0 * n * k * d + (4.0 * n * d if conv else 4.0 * n * k * d))
+    return byts, flops
 
 
 def source_hashes() -> dict:
@@ -723,24 +750,34 @@ def main():
         else:
             L.linformer_attend(p, r["Q"], Kbar, Vbar, lens, O, stream=stream)
 
-    run_half("project", 0)
+    fused = uses_fused(wl, conv)
     kern = {}
-    for kind in ("project", "attend"):
-        us = time_half(kind, args.kernel_iters)
-        byts, flops = algorithmic(wl, kind, conv)
-        kern[kind] = dict(us=us, bytes=byts, flops=flops, gbs=byts / (us * 1e-6) / 1e9,
-                          tflops=flops / (us * 1e-6) / 1e12)
-        log(f"{kind}: {us:.1f} us/launch, {kern[kind]['gbs']:.0f} GB/s algorithmic, "
-            f"{kern[kind]['tflops']:.1f} TFLOP/s")
-    # roofline of the dominant single kernel: the attention kernel (one launch per half; the
-    # projection half is two kernels, the projection GEMM and the split fixup, each shorter)
-    dom = "attend"
+    if fused:
+        # one launch per step: the fused kernel is the step
+        byts, flops = step_algorithmic(wl, conv)
+        us = ms * 1e3
+        kern["fused"] = dict(us=us, bytes=byts, flops=flops, gbs=byts / (us * 1e-6) / 1e9,
+                             tflops=flops / (us * 1e-6) / 1e12)
+        dom, dom_name = "fused", "fused_bf16_kernel"
+    else:
+        run_half("project", 0)
+        for kind in ("project", "attend"):
+            us = time_half(kind, args.kernel_iters)
+            byts, flops = algorithmic(wl, kind, conv)
+            kern[kind] = dict(us=us, bytes=byts, flops=flops, gbs=byts / (us * 1e-6) / 1e9,
+                              tflops=flops / (us * 1e-6) / 1e12)
+        # roofline of the dominant single kernel: the attention kernel (one launch per half; the
+        # projection half is two kernels, the projection GEMM and the split fixup, each shorter)
+        dom, dom_name = "attend", "attend_bf16_kernel"
+    for kind, kv in kern.items():
+        log(f"{kind}: {kv['us']:.1f} us/launch, {kv['gbs']:.0f} GB/s algorithmic, "
+            f"{kv['tflops']:.1f} TFLOP/s")
     kd = kern[dom]
     traffic = traffic_bytes(dom, wl.name)
     rp_us = rocprof_us(dom, wl.name)
     roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(kd["gbs"] / PEAK_HBM_GBS, 4),
-                "traffic": traffic, "kernel": "attend_bf16_kernel", "avg_us": round(kd["us"], 2),
+                "traffic": traffic, "kernel": dom_name, "avg_us": round(kd["us"], 2),
                 "algorithmic_bytes": kd["bytes"],
                 "mfma_tflops": round(kd["tflops"], 1),
                 "mfma_frac": round(kd["tflops"] / PEAK_BF16_TFLOPS, 4),
@@ -748,8 +785,7 @@ def main():
                 "rocprof_us": None if rp_us is None else round(rp_us, 2),
                 "frac_rocprof": None if rp_us is None else
                 round(kd["bytes"] / (rp_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-    step_bytes = kern["project"]["bytes"] + kern["attend"]["bytes"]
-    step_flops = kern["project"]["flops"] + kern["attend"]["flops"]
+    step_bytes, step_flops = step_algorithmic(wl, conv)
     roof_us = max(step_bytes / (PEAK_HBM_GBS * 1e9), step_flops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
 
     # the same roofline over the valid work only (rows past each length do no work: the
@@ -760,8 +796,7 @@ def main():
         n_mats = wl.e_heads * (2 if wl.separate_f else 1)
         eb = 2 if wl.dtype == synth.DT_BF16 else 4
         vtok = sum(Ls)
-        vbytes = (4 * wl.heads * wl.d * eb * vtok + (0 if conv else n_mats * wl.k * wl.n * eb) +
-                  2 * 2 * wl.batch * wl.heads * wl.k * wl.d * eb)
+        vbytes = 4 * wl.heads * wl.d * eb * vtok + (0 if conv else n_mats * wl.k * wl.n * eb)
         vflops = 8.0 * wl.heads * wl.k * wl.d * vtok
         vroof = max(vbytes / (PEAK_HBM_GBS * 1e9), vflops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
         valid = {"tokens": vtok, "tokens_per_s": round(vtok / (ms / 1e3), 1),
@@ -819,14 +854,17 @@ def main():
                           "frac": round(roof_us / (ms * 1e3), 4)},
         "valid_work_roofline": valid,
         "kernels_us": {k: round(v["us"], 2) for k, v in kern.items()},
-        "bytes_basis": "padded: Q, K, V, O over the padded length n, each distinct E/F matrix "
-                       "once, Kbar and Vbar (bf16) once each way; the kernels skip rows past "
-                       "each length (valid_work_roofline counts only the valid rows)",
+        "bytes_basis": "step_roofline: the scope table's count -- Q, K, V, O over the padded "
+                       "length n and each distinct E/F matrix once (Kbar/Vbar excluded); "
+                       "valid_work_roofline: the same over the valid rows only; roofline (one "
+                       "kernel): its own inputs and outputs over the padded length, Kbar and Vbar "
+                       "(bf16) included for the two-launch halves",
         "time_basis": "ms_per_step: HIP events around the timed back-to-back forward calls on "
                       "the launch stream; kernels_us / roofline.avg_us: HIP events around "
-                      "back-to-back launches of one half (includes the dispatch gap between "
-                      "launches); roofline.rocprof_us: average kernel duration in the committed "
-                      "rocprofv3 trace at this kernel source (profiles/kernel_times.txt)",
+                      "back-to-back launches of one half, or the step itself when one fused "
+                      "kernel is the step (includes the dispatch gap between launches); "
+                      "roofline.rocprof_us: average kernel duration in the committed rocprofv3 "
+                      "trace at this kernel source (profiles/kernel_times.txt)",
         "source_sha": source_hashes(),
         "command": "python bench.py " + " ".join(sys.argv[1:]),
         "dense_comparator": dense,
