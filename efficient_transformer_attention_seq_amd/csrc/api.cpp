@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -70,9 +71,34 @@ size_t kbar_bytes(const lf_problem* p) {
 size_t vbar_bytes(const lf_problem* p) {
     return (size_t)p->batch * p->heads * p->k * p->d * elem_size(p->dtype);
 }
+// A two-way split is paired inside the projection kernel: per workgroup tile one block of
+// fp32 sums (the tile's KS x UPT x 64 outputs) and one 8-byte counter.
+size_t pair_tiles(const lf::ProjGeom& g) {
+    return (size_t)g.groups * g.slot_tiles * g.tiles_per_group;
+}
+size_t pair_sums_bytes(const lf::ProjGeom& g) {
+    return round_up(pair_tiles(g) * (size_t)(g.k / g.slot_tiles) * g.upt * 64 * 4, 256);
+}
 size_t part_bytes(const lf_problem* p, const lf::ProjGeom& g) {
     if (p->dtype != LF_BF16 || g.S <= 1) return 0;
+    if (g.S == 2) return pair_sums_bytes(g) + pair_tiles(g) * 8;
     return (size_t)g.S * 2 * p->batch * p->heads * p->k * p->d * 4;
+}
+
+// Per-call tag of the paired split: unique within the process (and, salted by the start time,
+// unlikely to repeat across processes), in [1, 2^62).
+unsigned long long next_pair_epoch() {
+    static std::atomic<unsigned long long> next{[] {
+        unsigned long long x = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+        x ^= x >> 33;
+        x *= 0xff51afd7ed558ccdull;
+        x ^= x >> 33;
+        return x;
+    }()};
+    for (;;) {
+        const unsigned long long e = next.fetch_add(1) & ((1ull << 62) - 1);
+        if (e != 0) return e;
+    }
 }
 
 struct Range {
@@ -201,6 +227,10 @@ int do_project(const lf_problem* p, const void* K, const void* V, const void* E,
     a.part = (float*)part;
     a.c = eff_scale(p) * lf::kLog2e;
     a.g = g;
+    if (g.S == 2) {
+        a.pair_ctr = (unsigned long long*)((uint8_t*)part + pair_sums_bytes(g));
+        a.pair_epoch = next_pair_epoch();
+    }
     return launch_status(lf::launch_proj_bf16(a, stream));
 }
 

@@ -60,9 +60,18 @@ struct ProjBf16Args {
     uint8_t* Klo;           // [B, H, k, 64]
     uint8_t* Ksc;           // [B, H, k, 2]
     uint16_t* Vb;           // [B, H, k, 64]
-    float* part;            // [S, 2, B*H, k, 64] when S > 1
+    float* part;            // [S, 2, B*H, k, 64] when S > 1 (paired: per tile, see below)
     float c;                // scale * log2(e), applied to Kbar before it is stored
     ProjGeom g;
+    // Two splits paired in the kernel (S == 2 and pair_epoch != 0): of the two workgroups of a
+    // tile, the one that finishes its half of the reduction first leaves its sums in `part` (per
+    // tile, the workgroup's accumulators in register order: tile t's block starts at t * KS * UPT
+    // * 64 floats) and marks the tile's counter ready; the other adds them to its own sums and
+    // stores the result (no fixup launch).  pair_ctr[t] (one per tile) holds 0 or this call's tags
+    // 2 pair_epoch (one arrived) and 2 pair_epoch + 1 (sums ready) and is left at 0; pair_epoch is
+    // unique per call and below 2^62, so counters left over by an earlier call never match.
+    unsigned long long* pair_ctr;
+    unsigned long long pair_epoch;
 };
 
 struct AttendBf16Args {

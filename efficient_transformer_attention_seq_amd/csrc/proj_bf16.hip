@@ -342,12 +342,87 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
         }
     }
 
+    // ---- two splits paired in the kernel: the workgroup that gets here first leaves its sums
+    // and exits, the other adds them to its own and goes on to the unsplit epilogue.  The sums
+    // move with agent-coherent (sc1) stores and loads, so the pair need not share an L2; the
+    // summation a + b is exact in either order, so the result does not depend on which is first.
+    bool split_out = g.S > 1;
+    if (a.pair_epoch != 0) {
+        split_out = false;
+        const int tile = (grp * g.slot_tiles + stile) * g.tiles_per_group + utile;
+        unsigned long long* ctr = a.pair_ctr + tile;
+        const unsigned long long tag_in = a.pair_epoch << 1, tag_ready = tag_in | 1ull;
+        __shared__ int s_role;   // 0: first, 1: second (sums not ready yet), 2: second (ready)
+        if (tid == 0) {
+            const unsigned long long prev =
+                __hip_atomic_exchange(ctr, tag_in, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_role = prev == tag_ready ? 2 : (prev == tag_in ? 1 : 0);
+        }
+        __syncthreads();
+        const int role = s_role;
+        // this wave's accumulators, 16-byte chunk c of accumulator q at ((q 4 + c) 64 + lane) 16
+        // bytes from the wave's block (1 KB of contiguous bytes per instruction)
+        constexpr int NACC = WN * 2 * WM;
+        constexpr uint32_t kWaveBytes = NACC * 4 * 64 * 16;
+        const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+            a.part + ((size_t)tile * NW + wave) * (kWaveBytes / 4), 0, kWaveBytes, 0x00020000);
+        constexpr int kSC0 = 1, kSC1 = 16;   // cache-policy bits: agent-coherent access
+        if (role == 0) {
+#pragma unroll
+            for (int wn = 0; wn < WN; ++wn)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+                        for (int c4 = 0; c4 < 4; ++c4) {
+                            const int q = (wn * 2 + ct) * WM + mt;
+                            const f32x16& x = acc[wn][ct][mt];
+                            const f32x4 v = {x[4 * c4], x[4 * c4 + 1], x[4 * c4 + 2], x[4 * c4 + 3]};
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp,
+                                                                   ((q * 4 + c4) * 64 + lane) * 16, 0, kSC1);
+                        }
+            vmcnt_le<0>();     // this wave's sums have reached the coherence point
+            __syncthreads();   // everyone's
+            if (tid == 0)
+                __hip_atomic_store(ctr, tag_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        if (tid == 0) {
+            // the first workgroup is past its exchange and only has stores left, so this wait
+            // ends; the bound only guards against a counter that held this call's tag before it
+            for (int it = 0; role == 1 && it < (1 << 20) &&
+                             __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag_ready;
+                 ++it)
+                __builtin_amdgcn_s_sleep(2);
+            __hip_atomic_store(ctr, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int wn = 0; wn < WN; ++wn)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+                    for (int c4 = 0; c4 < 4; ++c4) {
+                        const int q = (wn * 2 + ct) * WM + mt;
+                        const f32x4 v = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, ((q * 4 + c4) * 64 + lane) * 16, 0,
+                                                                         kSC0 | kSC1));
+                        f32x16& x = acc[wn][ct][mt];
+                        x[4 * c4] += v[0];
+                        x[4 * c4 + 1] += v[1];
+                        x[4 * c4 + 2] += v[2];
+                        x[4 * c4 + 3] += v[3];
+                    }
+    }
+
     // ---- epilogue: stage each wave's tile through LDS (the ring is free once every wave has
     // left the loop) so global stores are whole rows, 16 bytes per lane.
     //   lane (l32, hh) holds, for slot (32 mt + l32) of the wave, columns 32 ct + 8 q + 4 hh + (0..3)
     __syncthreads();
     constexpr int RW = 32 * WM;                      // slot rows per wave tile
-    const bool split_out = g.S > 1;
     // per-wave staging region: RW rows x 64 columns, fp32 (row stride 272 B), or the bf16 plane
     // (row stride 136 B) followed by the fp8 lo plane (row stride 80 B); at most 17 KB per wave
     constexpr int kRowF = 64 * 4 + 16, kRowH = 64 * 2 + 8, kRowL = 80;
@@ -658,7 +733,7 @@ hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream) {
         case 6: e = launch_cfg<Cfg128x128w4>(a, stream); break;
         default: e = launch_cfg<Cfg32x512>(a, stream); break;
     }
-    if (e != hipSuccess || g.S == 1) return e;
+    if (e != hipSuccess || g.S == 1 || a.pair_epoch != 0) return e;
     const size_t half = (size_t)g.B * g.H * g.k * kHeadDim;
     // the single-matrix mode has only the values half
     const size_t e0 = g.share == kProjSingle ? half : 0;

@@ -124,8 +124,10 @@ int linformer_kv_sizes(const lf_problem* p, size_t* kbar_bytes, size_t* vbar_byt
 
 /* Sequence projection, Kbar = E_h . K_{b,h} and Vbar = F_h . V_{b,h} over the valid positions
  * (Linformer 요약 설명, section "Model").  K, V, E, F and lengths are read; Kbar, Vbar are
- * written in the layouts of linformer_kv_sizes(); ws is scratch (its contents on entry do not
- * matter).  F: per the sharing mode above (NULL allowed for NONE, meaning F = E). */
+ * written in the layouts of linformer_kv_sizes(); ws is scratch: its contents on entry do not
+ * matter (the per-tile arrival counters of a two-way position split carry a tag unique to each
+ * call and are left at zero), but calls that may run at the same time must not share one.
+ * F: per the sharing mode above (NULL allowed for NONE, meaning F = E). */
 int linformer_project_kv(const lf_problem* p, const void* K, const void* V, const void* E,
                          const void* F, const int32_t* lengths, void* Kbar, void* Vbar,
                          void* ws, size_t ws_bytes, void* stream);

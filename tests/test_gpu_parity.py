@@ -134,6 +134,45 @@ def test_project_split_workspace_contents_do_not_matter(split):
     assert orc.slice_rel_err(outs[0][1], rv) <= 4e-3
 
 
+@pytest.mark.parametrize("split", [2, 5])
+def test_project_split_other_inputs_on_one_workspace(split):
+    """Calls with different inputs, one after another on one workspace, each give bitwise the
+    output of a call on a fresh workspace: no call reads partial sums (or, with two splits, the
+    in-kernel pairing state) that an earlier call left behind.  Two splits are paired inside the
+    projection kernel; five go through the fixup pass."""
+    torch = G.torch_mod()
+    ins = [synth.random_inputs(3, 4, 1024, 64, 128, BF, NONE, seed=s, lengths=L_)
+           for s, L_ in ((31, [1024, 700, 65]), (32, [999, 1024, 300]))]
+    wl = ins[0].wl
+    p = G.prob(wl)
+    kbytes, _ = L.linformer_kv_sizes(p)
+
+    def call(inp, ws, wsb):
+        K, V, E, F = (G.dev(x, wl.dtype) for x in (inp.K, inp.V, inp.E, inp.F))
+        Kbar = torch.empty(kbytes, dtype=torch.uint8, device="cuda")
+        Vbar = G.empty((wl.batch, wl.heads, wl.k, wl.d), wl.dtype)
+        L.linformer_project_kv(p, K, V, E, F, G.lengths_dev(inp.lengths), Kbar, Vbar, ws, wsb)
+        torch.cuda.synchronize()
+        return Kbar.cpu().numpy(), G.host(Vbar)
+
+    with G.env(LINFORMER_PROJ_SPLIT=split):
+        wsb = L.linformer_workspace_size(p)
+        fresh = []
+        for inp in ins:
+            ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+            fresh.append(call(inp, ws, wsb))
+        shared = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+        order = [0, 1, 0, 1, 1, 0]
+        G.log(f"split {split}: calls in the order {order} on one workspace")
+        for i in order:
+            kb, vb = call(ins[i], shared, wsb)
+            assert np.array_equal(kb, fresh[i][0]) and np.array_equal(vb, fresh[i][1])
+    rk, rv = _ref_project(ins[1])
+    _, _, x = G.decode_kbar_bf16(fresh[1][0], (wl.batch, wl.heads, wl.k, wl.d))
+    assert orc.slice_rel_err(x / G.log2e_scale(wl), rk) <= KBAR_TOL
+    assert orc.slice_rel_err(fresh[1][1], rv) <= 4e-3
+
+
 @pytest.mark.parametrize("split", [1, 3])
 def test_kbar_storage_format(split):
     """The bf16 Kbar bytes follow the documented format, from both the single-split epilogue and
