@@ -31,7 +31,9 @@ CSRC = os.path.join(ROOT, "efficient_transformer_attention_seq_amd", "csrc")
 # their hash is unchanged)
 KERNEL_SOURCES = {"attend": ("attend_bf16.hip", "attend_core.h", "lf_device.h"),
                   "project": ("proj_bf16.hip", "lf_device.h"),
-                  "fused": ("fused_bf16.hip", "attend_core.h", "lf_device.h")}
+                  "fused": ("fused_bf16.hip", "attend_core.h", "lf_device.h"),
+                  "attend_f32": ("f32_path.hip", "lf_device.h")}
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 
 
 def log(*a):
@@ -126,7 +128,7 @@ def traffic_bytes(kernel: str, workload: str):
 
 def algorithmic(wl, kernel: str, conv: bool = False):
     """(bytes, flops) per launch as the method's work is counted in the scope table: over the
-    padded length n (tokens = B n), bf16 storage.
+    padded length n (tokens = B n), in the workload's storage type (bf16, or fp32).
 
     Per token and head: project reads K and V (2 d 2 B = 256 B) plus its share of each distinct
     E/F matrix (read once), and does 4 k d flops (Kbar and Vbar); attend reads Q and writes O
@@ -137,7 +139,7 @@ def algorithmic(wl, kernel: str, conv: bool = False):
     """
     B, H, n, d, k = wl.batch, wl.heads, wl.n, wl.d, wl.k
     bh = B * H
-    eb = 2  # bf16
+    eb = 2 if wl.dtype == 1 else 4
     kv = 2 * bh * k * d * eb
     flops = 4.0 * bh * n * k * d
     if kernel == "project":
@@ -767,26 +769,33 @@ def main():
             kern[kind] = dict(us=us, bytes=byts, flops=flops, gbs=byts / (us * 1e-6) / 1e9,
                               tflops=flops / (us * 1e-6) / 1e12)
         # roofline of the dominant single kernel: the attention kernel (one launch per half; the
-        # projection half is two kernels, the projection GEMM and the split fixup, each shorter)
-        dom, dom_name = "attend", "attend_bf16_kernel"
+        # projection half is one kernel, plus the split fixup for three or more splits)
+        if wl.dtype == 1:
+            dom, dom_name = "attend", "attend_bf16_kernel"
+        else:
+            dom, dom_name = "attend_f32", "attend_f32_kernel"
     for kind, kv in kern.items():
         log(f"{kind}: {kv['us']:.1f} us/launch, {kv['gbs']:.0f} GB/s algorithmic, "
             f"{kv['tflops']:.1f} TFLOP/s")
-    kd = kern[dom]
+    kd = kern["attend" if dom == "attend_f32" else dom]
     traffic = traffic_bytes(dom, wl.name)
     rp_us = rocprof_us(dom, wl.name)
     roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(kd["gbs"] / PEAK_HBM_GBS, 4),
                 "traffic": traffic, "kernel": dom_name, "avg_us": round(kd["us"], 2),
                 "algorithmic_bytes": kd["bytes"],
-                "mfma_tflops": round(kd["tflops"], 1),
-                "mfma_frac": round(kd["tflops"] / PEAK_BF16_TFLOPS, 4),
+                # matrix-core rate (bf16 kernels), or the fp32 vector rate (fp32 kernels)
+                "mfma_tflops": round(kd["tflops"], 1) if wl.dtype == 1 else None,
+                "mfma_frac": round(kd["tflops"] / PEAK_BF16_TFLOPS, 4) if wl.dtype == 1 else None,
+                "vector_f32_frac": None if wl.dtype == 1 else
+                round(kd["tflops"] / PEAK_F32_TFLOPS, 4),
                 # the same bytes over the committed profiler duration of this kernel source
                 "rocprof_us": None if rp_us is None else round(rp_us, 2),
                 "frac_rocprof": None if rp_us is None else
                 round(kd["bytes"] / (rp_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
     step_bytes, step_flops = step_algorithmic(wl, conv)
-    roof_us = max(step_bytes / (PEAK_HBM_GBS * 1e9), step_flops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
+    peak_flops = (PEAK_BF16_TFLOPS if wl.dtype == 1 else PEAK_F32_TFLOPS) * 1e12
+    roof_us = max(step_bytes / (PEAK_HBM_GBS * 1e9), step_flops / peak_flops) * 1e6
 
     # the same roofline over the valid work only (rows past each length do no work: the
     # projection skips them and the attention only zero-fills them)
@@ -798,7 +807,7 @@ def main():
         vtok = sum(Ls)
         vbytes = 4 * wl.heads * wl.d * eb * vtok + (0 if conv else n_mats * wl.k * wl.n * eb)
         vflops = 8.0 * wl.heads * wl.k * wl.d * vtok
-        vroof = max(vbytes / (PEAK_HBM_GBS * 1e9), vflops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
+        vroof = max(vbytes / (PEAK_HBM_GBS * 1e9), vflops / peak_flops) * 1e6
         valid = {"tokens": vtok, "tokens_per_s": round(vtok / (ms / 1e3), 1),
                  "algorithmic_bytes": vbytes, "flops": vflops, "roofline_us": round(vroof, 2),
                  "frac": round(vroof / (ms * 1e3), 4)}

@@ -484,6 +484,24 @@ int forward_validate(const lf_problem* p, const void* Q, const void* K, const vo
     return LF_OK;
 }
 
+// Work split of the fused kernel: the (b, h) units of the last, partial round of workgroups are
+// each taken by `parts` workgroups (all project the unit, each attends a contiguous share of its
+// query tiles), as many as fill the compute units that round would leave idle, with at least
+// eight query tiles (one per wave) per share at full length (LINFORMER_FUSED_SPLIT=0: none).
+void fused_split(lf::FusedBf16Args& f) {
+    const int units = f.B * f.H, G = cu_count();
+    f.whole = units;
+    f.parts = 1;
+    const char* e = std::getenv("LINFORMER_FUSED_SPLIT");
+    if ((e && e[0] == '0') || G <= 0) return;
+    const int rest = units % G;
+    if (rest == 0) return;
+    const int parts = std::min(G / rest, std::max(1, f.n / 32 / 8));
+    if (parts < 2) return;
+    f.whole = units - rest;
+    f.parts = parts;
+}
+
 // The projection into the workspace (Kbar | Vbar | partials), then the attention.
 int forward_run(const lf_problem* p, const FwdPlan& pl, const void* Q, const void* K,
                 const void* V, const void* E, const int32_t* lengths, void* O, void* ws,
@@ -507,6 +525,7 @@ int forward_run(const lf_problem* p, const FwdPlan& pl, const void* Q, const voi
         f.k = p->k;
         f.e_heads = p->share == LF_SHARE_NONE ? p->heads : 1;
         f.c = eff_scale(p) * lf::kLog2e;
+        fused_split(f);
         return launch_status(lf::launch_fused_bf16(f, s));
     }
     int st = do_project(p, K, V, E, pl.Fr, lengths, Kbar, Vbar, part, pl.g, s);
@@ -792,6 +811,7 @@ int linformer_stack_forward(const lf_stack* s, const void* X, const void* Wqkv, 
             f.e_heads = 1;
             f.c = c;
             f.dm = D;
+            fused_split(f);
             st = launch_status(lf::launch_fused_bf16(f, strm));
             if (st) return st;
         } else {

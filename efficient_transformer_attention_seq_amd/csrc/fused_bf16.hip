@@ -21,6 +21,10 @@
 // attend_core.h), the first tile's Q loaded before the projection starts and each next tile's Q
 // during the current one; the rows past the last valid tile are zero-filled with streaming
 // stores issued at the start, so they drain under the projection.
+// Work split: when the units do not fill whole rounds of workgroups, each unit of the last,
+// partial round is taken by several workgroups that all project it and attend contiguous shares
+// of its tiles, so that round fills the compute units (every output tile is still computed once,
+// by the same arithmetic).
 #include "attend_core.h"
 
 namespace lf {
@@ -64,13 +68,21 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[FL::BYTES];
     const uint32_t lds0 = lds_addr(smem);
 
-    const int bh = blockIdx.x;
+    // this workgroup's unit and its share of the unit's query tiles
+    int bh = blockIdx.x, part = 0, nparts = 1;
+    if (bh >= a.whole) {
+        const int r = bh - a.whole;
+        bh = a.whole + r / a.parts;
+        part = r % a.parts;
+        nparts = a.parts;
+    }
     const int b = bh / a.H, h = bh % a.H;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int L = clamp_len(a.lengths, b, a.n);
     const int ntiles = (L + kTileQ - 1) / kTileQ;
+    const int t0 = ntiles * part / nparts, t1 = ntiles * (part + 1) / nparts;
     const size_t rowbase = (size_t)bh * a.n;
 
     // ---- the first tile's Q, in flight during the projection
@@ -80,10 +92,10 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) qraw[i] = src[64 * i];
     };
-    if (wave < ntiles) load_q(wave);
+    if (t0 + wave < t1) load_q(t0 + wave);
 
     // ---- zero the rows past the last valid tile (streaming stores, drained under the work)
-    {
+    if (part == 0) {
         const u32x4 zero = {0u, 0u, 0u, 0u};
         u32x4* blk = (u32x4*)(a.O + (rowbase + (size_t)ntiles * kTileQ) * kHeadDim);
         const int nz = (a.n - ntiles * kTileQ) * 8;   // 16-byte chunks
@@ -248,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
     }
     __syncthreads();
 
-    // ---- attention over the head's query tiles, tile j to wave j % 8
-    if (wave >= ntiles) return;
+    // ---- attention over this workgroup's query tiles t0 .. t1 - 1, tile t0 + j to wave j % 8
+    if (t0 + wave >= t1) return;
     const Lanes ln = attn_lanes<KB>(lds0, lane);
     int scl[2];
     attn_scales<KB>(smem, lane, scl);
@@ -261,12 +273,12 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
     for (int j = 0; j < 16; ++j) bias[j] = 0.0f;
     bool bias_dirty = false;
     bf16x8 qop[4];
-    for (int tile = wave; tile < ntiles; tile += 8) {
+    for (int tile = t0 + wave; tile < t1; tile += 8) {
         stage_q(stg, coff, qraw, lane, qop);
         f32x16 o0, o1;
         float z;
         tile_math<KB>(ln, qop, scl, hh, bias, bias_dirty, o0, o1, z, [&]() {
-            if (tile + 8 < ntiles) load_q(tile + 8);
+            if (tile + 8 < t1) load_q(tile + 8);
         });
         tile_store(stg, coff, lane, o0, o1, z, a.O + (rowbase + (size_t)tile * kTileQ) * kHeadDim,
                    tile * kTileQ, L);
@@ -278,7 +290,9 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
 bool fused_supported(int n, int k) { return n <= 1024 && (k == 128 || k == 256); }
 
 hipError_t launch_fused_bf16(const FusedBf16Args& a, hipStream_t stream) {
-    const dim3 grid(a.B * a.H), block(kThreads);
+    const int units = a.B * a.H;
+    if (a.whole < 0 || a.whole > units || a.parts < 1) return hipErrorInvalidValue;
+    const dim3 grid(a.whole + (units - a.whole) * a.parts), block(kThreads);
     if (a.dm > 0 && (a.dm % kStep || a.dm != 64 * a.H)) return hipErrorInvalidValue;
     const bool stack = a.dm > 0;
     switch (a.k) {

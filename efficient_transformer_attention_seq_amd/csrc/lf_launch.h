@@ -215,6 +215,11 @@ struct FusedBf16Args {
     int e_heads;            // H (per-head E_h) or 1
     float c;                // scale * log2(e)
     int dm;                 // 0, or d_model for the stack form
+    // Work split: workgroups 0 .. whole - 1 take (b, h) = their index, all of its query tiles;
+    // the units after those are each taken by `parts` workgroups that all project the unit and
+    // attend contiguous shares of its tiles (a last round of fewer units than compute units)
+    int whole;
+    int parts;
 };
 bool fused_supported(int n, int k);
 hipError_t launch_fused_bf16(const FusedBf16Args& a, hipStream_t stream);

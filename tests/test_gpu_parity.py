@@ -486,6 +486,24 @@ def test_forward_fused_parity(case):
     assert orc.slice_rel_err(out, out2) <= 1e-2
 
 
+@pytest.mark.parametrize("case", [FUSED_CASES[0], FUSED_CASES[1], FUSED_CASES[4],
+                                  (3, 3, 1024, 256, LAYER, [1024, 40, 990])])
+def test_forward_fused_work_split_is_bitwise_the_same(case):
+    """The fused kernel's work split (the units of a last, partial round taken by several
+    workgroups, each projecting the unit and attending a share of its tiles; the small problems
+    here are all one partial round) writes bitwise what one workgroup per unit writes,
+    including rows past the lengths and units whose shares hold no tile."""
+    B, H, n, k, share, lens = case
+    inp = synth.random_inputs(B, H, n, 64, k, BF, share, seed=17 + n + k, lengths=lens)
+    G.log(f"fused work split case={case}")
+    out, ok = G.run_forward(inp, guard=True)
+    assert ok, "write outside the output tensor"
+    with G.env(LINFORMER_FUSED_SPLIT=0):
+        ref, _ = G.run_forward(inp)
+    assert np.array_equal(out, ref)
+    assert orc.slice_rel_err(out, _ref_forward(inp)) <= G.TOL[BF]
+
+
 def test_forward_without_lengths_equals_full_lengths():
     inp = synth.random_inputs(2, 2, 256, 64, 128, BF, KV, seed=22)
     a, _ = G.run_forward(inp)
