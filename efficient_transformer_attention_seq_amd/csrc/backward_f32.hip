@@ -6,34 +6,41 @@
 //   dP = dO Vbar^T,  dS = P o (dP - rowsum(P o dP)),  dQ = s dS Kbar        (bw_attend_kernel)
 //   dVbar = P^T dO,  dKbar = s dS^T Q                                        (bw_gemm_kernel)
 //   dE += dKbar K^T, dK = E^T dKbar, dF += dVbar V^T, dV = F^T dVbar         (bw_gemm_kernel)
-// Every contraction runs on the fp32 matrix cores: one strided, batched GEMM (split along the
-// reduction when its output is too small to fill the chip) and a fused kernel for P, the softmax
-// Jacobian and dQ with Kbar and Vbar resident in LDS.  Both read the inputs in their own dtype
-// (bf16 values widen exactly to fp32 as they are staged) and never read the masked rows.
+// Every contraction runs on the matrix cores with fp32 accumulation: one strided, batched GEMM
+// (split along the reduction when its output is too small to fill the chip) and a fused kernel for
+// P, the softmax Jacobian and dQ with Kbar and Vbar resident in LDS.  Both read the inputs in
+// their own dtype and never read the masked rows.
+//
+// The GEMM multiplies fp32 operands as split bf16 pairs (the "bf16x3" scheme of Henry, Tang and
+// Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype For Higher-Precision
+// Computations", ARITH 2019): v = hi + lo with hi = bf16(v), lo = bf16(v - hi), so hi + lo holds v
+// to within 2^-16 |v|, and a b = ah bh + ah bl + al bh with the al bl term (below 2^-16 |a b|)
+// dropped, three v_mfma_f32_32x32x16_bf16 in place of 8 v_mfma_f32_32x32x2_f32 per 16-deep step.
+// A bf16 operand (Q, K, V, E, F, dO in bf16) is its own hi part, so its products take two.  The
+// fused kernel keeps the fp32 matrix cores (v_mfma_f32_16x16x4_f32).
+#include <type_traits>
+
 #include "lf_device.h"
 #include "lf_launch.h"
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 namespace lf {
 namespace {
 
 // ---- C = alpha A B + beta C over a batch z, operands addressed through strides (BwGemm in
-// lf_launch.h), on the fp32 matrix cores (v_mfma_f32_32x32x2_f32).  Workgroup tile 128 x TN
-// (TN = 64 NI), four waves in a 2 x 2 grid, each wave 64 x 32 NI as 2 x NI blocks of 32 x 32;
-// 32-deep reduction steps staged through LDS, the next step's operands loaded into registers
-// while the current one is multiplied.  Operand tiles are read with consecutive threads along
-// the operand's contiguous direction (the reduction index when its stride is 1, else the row or
-// column index), so global reads coalesce either way.
+// lf_launch.h), as split bf16 products (above) on v_mfma_f32_32x32x16_bf16.  Workgroup tile
+// 128 x TN (TN = 64 NI), four waves in a 2 x 2 grid, each wave 64 x 32 NI as 2 x NI blocks of
+// 32 x 32; 32-deep reduction steps staged through LDS as bf16 hi (and, for fp32 operands, lo)
+// planes, the next step's tiles loaded into registers while the current one is multiplied.
+// Operand tiles are read with consecutive threads along the operand's contiguous direction (the
+// reduction index when its stride is 1, else the row or column index), so global reads coalesce
+// either way; the planes keep that direction contiguous ([x][kk] rows of 80 bytes, read 16 bytes
+// per lane, or [kk][x] rows with 32-byte blocks XOR-swizzled by kk & 3, read with the transposing
+// ds_read_b64_tr_b16), so staging is 8- or 16-byte writes either way.
 constexpr int kGM = 128, kGK = 32;
-// LDS row padding (floats) of an operand tile: 1 when it is staged down columns (vectors along
-// the reduction index: consecutive rows land in consecutive banks), 4 when it is staged along
-// rows (16-byte aligned rows, so each vector is one 16-byte write)
-template <bool kf>
-constexpr int kGPad = kf ? 1 : 4;
 // Strides and bases must keep every 16-byte vector aligned: launch_bw_gemm checks them.
 
-__device__ __forceinline__ f32x16 mfma_f32_32(float a, float b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4 mfma_f32_16(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -105,20 +112,45 @@ struct TileLoader {
             }
         }
     }
-    template <int LD>
-    __device__ void stage(float (*S)[LD]) const {
+    // byte offset of (kk, x) in a [kk][x] plane (TX bf16 per row, 32-byte blocks swizzled by kk & 3)
+    __device__ static int tr_off(int kk, int x) {
+        return kk * TX * 2 + ((((x >> 4) ^ (kk & 3))) << 5) + (x & 15) * 2;
+    }
+    // The tile as bf16 planes, [x][kk] (reduction index contiguous) when kf, else [kk][x]
+    // (read back transposed): hi = bf16(v) and, for fp32
+    // operands, lo = bf16(v - hi), so hi + lo carries v to within 2^-16 of |v|
+    template <int LDK, bool LO>
+    __device__ void stage_split(uint16_t (*Sh)[LDK], uint16_t (*Sl)[LDK]) const {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const int kk = kk0 + v * dkk, x = x0 + v * dx;
-            float d[VEC];
-            unpack(raw[v], d, T{});
-            if constexpr (kf) {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) S[kk + e][x] = d[e];
+            if constexpr (!LO) {   // bf16 operand: its bits are the hi plane
+                if constexpr (kf) {
+                    *(u32x4*)&Sh[x][kk] = raw[v];
+                } else {   // [kk][x] rows, 32-byte blocks swizzled by kk & 3
+                    *(u32x4*)((uint8_t*)Sh + tr_off(kk, x)) = raw[v];
+                }
             } else {
+                float d[VEC];
+                unpack(raw[v], d, T{});
+                uint16_t hv[VEC], lv[VEC];
 #pragma unroll
-                for (int e = 0; e < VEC; e += 4)
-                    *(f32x4*)&S[kk][x + e] = f32x4{d[e], d[e + 1], d[e + 2], d[e + 3]};
+                for (int e = 0; e < VEC; ++e) {
+                    hv[e] = f32_to_bf16(d[e]);
+                    lv[e] = f32_to_bf16(d[e] - bf16_to_f32(hv[e]));
+                }
+                if constexpr (kf) {
+#pragma unroll
+                    for (int e = 0; e < VEC; e += 2) {
+                        *(uint32_t*)&Sh[x][kk + e] = (uint32_t)hv[e] | ((uint32_t)hv[e + 1] << 16);
+                        *(uint32_t*)&Sl[x][kk + e] = (uint32_t)lv[e] | ((uint32_t)lv[e + 1] << 16);
+                    }
+                } else {   // [kk][x] rows: VEC (4) consecutive x, 8 bytes in one 32-byte block
+                    *(u32x2*)((uint8_t*)Sh + tr_off(kk, x)) =
+                        u32x2{(uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
+                    *(u32x2*)((uint8_t*)Sl + tr_off(kk, x)) =
+                        u32x2{(uint32_t)lv[0] | ((uint32_t)lv[1] << 16), (uint32_t)lv[2] | ((uint32_t)lv[3] << 16)};
+                }
             }
         }
     }
@@ -128,11 +160,39 @@ struct TileLoader {
 template <int NI, typename TA, bool AKF, typename TB, bool BKF>
 __global__ __launch_bounds__(256) void bw_gemm_kernel(BwGemm g) {
     constexpr int TN = 64 * NI;
-    __shared__ __attribute__((aligned(16))) float As[kGK][kGM + kGPad<AKF>];
-    __shared__ __attribute__((aligned(16))) float Bs[kGK][TN + kGPad<BKF>];
+    constexpr bool LOA = !std::is_same<TA, uint16_t>::value, LOB = !std::is_same<TB, uint16_t>::value;
+    // kf operands: [x][kk] planes with 80-byte rows (the 16-byte operand reads of 8 rows cover
+    // all banks); the others: [kk][x] planes (same bytes), read with ds_read_b64_tr_b16
+    constexpr int LDK = kGK + 8;
+    static_assert(kGK * kGM <= kGM * LDK && kGK * TN <= TN * LDK, "planes fit");
+    __shared__ __attribute__((aligned(16))) uint16_t Ash[kGM][LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Asl[LOA ? kGM : 1][LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bsh[TN][LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bsl[LOB ? TN : 1][LDK];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l = lane & 31, h = lane >> 5;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * (TN / 2);
+    // operand of columns c0 .. c0 + 31 (c0 % 32 == 0), reduction 16 ks + 8 h .. + 7, from a plane
+    auto read_op = [&](const uint16_t (*S)[LDK], bool kfo, int TXo, int c0, int ks) {
+        if (kfo) return *(const bf16x8*)&S[c0 + l][16 * ks + 8 * h];
+        // transposed read: each 16-lane group takes a 4 x 16 block of [kk][x] (the operand order
+        // of lane (l, h) = column c0 + l, reduction 16 ks + 8 h + (0..7))
+        const int grp16 = lane >> 4, s16 = lane & 15;
+        const int tq = 8 * (grp16 >> 1) + (s16 >> 2);
+        const int cblk = 2 * (c0 >> 5) + (grp16 & 1);
+        const int cin = (s16 & 3) * 8;
+        s16x4 v[2];
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+            const int t = 16 * ks + tq + 4 * rd;
+            const uint8_t* p = (const uint8_t*)S + t * TXo * 2 + ((cblk ^ (t & 3)) << 5) + cin;
+            v[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(uintptr_t)(
+                    (__attribute__((address_space(3))) const uint8_t*)p));
+        }
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
     const int i0 = blockIdx.y * kGM, j0 = blockIdx.x * TN;
     const int z = blockIdx.z / g.splits, sp = blockIdx.z % g.splits;
     const long long z1 = z / g.zdiv, z2 = z % g.zdiv;
@@ -161,28 +221,33 @@ __global__ __launch_bounds__(256) void bw_gemm_kernel(BwGemm g) {
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
     if (kbeg < kend) fetch(kbeg);
     for (int k0 = kbeg; k0 < kend; k0 += kGK) {
-        la.stage(As);
-        lb.stage(Bs);
+        la.template stage_split<LDK, LOA>(Ash, Asl);
+        lb.template stage_split<LDK, LOB>(Bsh, Bsl);
         __syncthreads();
         if (k0 + kGK < kend) fetch(k0 + kGK);
-        // operands of pair kp + 2 are read while the products of pair kp run
-        float av[2][2], bv[2][NI];
-        auto read_ops = [&](int kp, float (&a2)[2], float (&b2)[NI]) {
+        // two 16-deep sub-steps: a b = ah bh + ah bl + al bh (the al bl term, below 2^-16 of |a b|,
+        // is dropped), v_mfma_f32_32x32x16_bf16 with fp32 accumulation
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) a2[mi] = As[kp + h][wm + 32 * mi + l];
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 ah[2], al[2], bh[NI], bl[NI];
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) b2[ni] = Bs[kp + h][wn + 32 * ni + l];
-        };
-        read_ops(0, av[0], bv[0]);
+            for (int mi = 0; mi < 2; ++mi) {
+                ah[mi] = read_op(Ash, AKF, kGM, wm + 32 * mi, ks);
+                if constexpr (LOA) al[mi] = read_op(Asl, AKF, kGM, wm + 32 * mi, ks);
+            }
 #pragma unroll
-        for (int kp = 0; kp < kGK; kp += 2) {
-            const int cur = (kp >> 1) & 1;
-            if (kp + 2 < kGK) read_ops(kp + 2, av[cur ^ 1], bv[cur ^ 1]);
+            for (int ni = 0; ni < NI; ++ni) {
+                bh[ni] = read_op(Bsh, BKF, TN, wn + 32 * ni, ks);
+                if constexpr (LOB) bl[ni] = read_op(Bsl, BKF, TN, wn + 32 * ni, ks);
+            }
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
-                    acc[mi][ni] = mfma_f32_32(av[cur][mi], bv[cur][ni], acc[mi][ni]);
+                for (int ni = 0; ni < NI; ++ni) {
+                    if constexpr (LOA) acc[mi][ni] = mfma32(al[mi], bh[ni], acc[mi][ni]);
+                    if constexpr (LOB) acc[mi][ni] = mfma32(ah[mi], bl[ni], acc[mi][ni]);
+                    acc[mi][ni] = mfma32(ah[mi], bh[ni], acc[mi][ni]);
+                }
         }
         __syncthreads();
     }

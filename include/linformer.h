@@ -196,7 +196,9 @@ int linformer_forward_conv(const lf_problem* p, const void* Q, const void* K, co
  * K, V rows and of the E, F columns past the length are zero.  Inputs in p->dtype and the forward layouts; gradients fp32:
  * dQ, dK, dV [B, H, n, d]; dE [H_E, k, n]; dF like dE when F is a separate matrix (headwise, or
  * unshared with F given and != E), else dF must be NULL and dE holds both projections' parts.
- * All arithmetic fp32 (Kbar, Vbar recomputed in fp32; bf16 inputs widen exactly).  ws:
+ * fp32 accumulation throughout (Kbar, Vbar recomputed in fp32); the GEMMs multiply fp32 operands
+ * as split bf16 pairs (hi + lo, within 2^-16 of the value: the bf16x3 scheme), and the results
+ * meet the 1e-4 relative bar of an fp32 computation (tested).  ws:
  * linformer_backward_workspace_size() bytes of scratch (16-byte aligned). */
 int linformer_backward_workspace_size(const lf_problem* p, size_t* bytes);
 int linformer_backward(const lf_problem* p, const void* Q, const void* K, const void* V,
