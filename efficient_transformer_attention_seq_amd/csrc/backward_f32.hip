@@ -17,7 +17,7 @@
 // to within 2^-16 |v|, and a b = ah bh + ah bl + al bh with the al bl term (below 2^-16 |a b|)
 // dropped, three v_mfma_f32_32x32x16_bf16 in place of 8 v_mfma_f32_32x32x2_f32 per 16-deep step.
 // A bf16 operand (Q, K, V, E, F, dO in bf16) is its own hi part, so its products take two.  The
-// fused kernel keeps the fp32 matrix cores (v_mfma_f32_16x16x4_f32).
+// fused kernel multiplies the same way on v_mfma_f32_16x16x32_bf16.
 #include <type_traits>
 
 #include "lf_device.h"
@@ -304,55 +304,114 @@ __global__ __launch_bounds__(256) void bw_gemm_reduce_kernel(BwGemm g) {
     }
 }
 
-// ---- per (b, h) and a range of 128-query blocks: P and dS ([n, k]) and dQ, on the fp32 matrix
-// cores (v_mfma_f32_16x16x4_f32).  Kbar and Vbar sit in LDS (row stride 68 floats) for the whole
-// range.  Each wave owns 16 query rows q0 + l of a block and works on transposed products, so
-// that lane (g, l) holds the values of query l:
-//   S^T = Kbar Q^T, dP^T = Vbar dO^T   (k x 16: lane holds rows r = 16 rb + 4 g + e, e < 4)
+// ---- per (b, h) and a range of 128-query blocks: P and dS ([n, k]) and dQ, as split bf16
+// products (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Kbar and Vbar sit in LDS for the whole
+// range as bf16 hi and lo planes ([k][64], 16-byte chunks XOR-swizzled by (r ^ r >> 3) & 7).  Each
+// wave owns 16 query rows q0 + l of a block and works on transposed products, so that lane (g, l)
+// holds the values of query l:
+//   S^T = Kbar Q^T, dP^T = Vbar dO^T   (k x 16: lane holds rows 16 rb + 4 g + e, e < 4), the
+//        query's Q / dO slices at d = 32 kc + 8 g .. + 7 (kc = 0, 1) as the B operands, the
+//        planes' rows 16 rb + l as the A operands (hi and lo: Kbar = hi + lo within 2^-16)
 //   softmax and the Jacobian down each column (within the lane, then across the four lanes g)
-//   dQ^T = Kbar^T dS^T                  (64 x 16), its B operand taken straight from the dS^T
-//                                       accumulators by matching the reduction order
-// In the first two products the reduction index c runs over 16 g + t for lane group g, so the
-// lane's B operand is its own query row's slice Q[q][16 g .. 16 g + 15] held in registers; the
-// next block's slices are loaded into the same registers before this block's dQ products.  A wave whose 16 rows all lie at or past the item's length only writes
-// zero dQ rows: its P and dS rows are left unwritten (the reductions over queries stop at the
-// length) and its gradients are zero.
-constexpr int kKS = 68;   // LDS row stride of Kbar / Vbar (floats)
+//   dQ^T = Kbar^T dS^T                  (64 x 16): per 32 slots the B operand is the lane's dS^T
+//        values of rows 32 j + 4 g + e and 32 j + 16 + 4 g + e straight from the accumulators
+//        (split into hi and lo), and the A operand Kbar^T is read at exactly those slots with the
+//        transposing ds_read_b64_tr_b16 (lane i of a 16-lane group receives element i % 4 of
+//        source lanes 4 r + i / 4: source lane s reads the 4 columns 16 cb + 4 (s % 4) of row
+//        32 j + 4 g + s / 4, so lane i gets column 16 cb + i of those rows)
+// The next block's Q, dO slices are loaded into registers before this block's dQ products.  A
+// wave whose 16 rows all lie at or past the item's length only writes zero dQ rows: its P and dS
+// rows are left unwritten (the reductions over queries stop at the length) and its gradients are
+// zero.
 constexpr int kAttWaves = 8, kAttRows = 16 * kAttWaves;
 
-// 16 consecutive elements (16-element aligned) as four f32x4
-__device__ __forceinline__ void load16(const float* p, f32x4 (&v)[4]) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *(const f32x4*)(p + 4 * u);
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ void load16(const uint16_t* p, f32x4 (&v)[4]) {
+// byte offset of element (r, d) of a [k][64] bf16 plane (d % 4 == 0: 8 bytes in one chunk)
+__device__ __forceinline__ int kv_off(int r, int d) {
+    return r * 128 + (((d >> 3) ^ ((r ^ (r >> 3)) & 7)) << 4) + (d & 7) * 2;
+}
+// hi = bf16(v), lo = bf16(v - hi) of four values, as packed pairs
+__device__ __forceinline__ void split4(f32x4 v, u32x2& hi, u32x2& lo) {
+    uint16_t h[4], o[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const u32x4 w = *(const u32x4*)(p + 8 * h);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t x = w[2 * i], y = w[2 * i + 1];
-            v[2 * h + i] = f32x4{__uint_as_float(x << 16), __uint_as_float(x & 0xFFFF0000u),
-                                 __uint_as_float(y << 16), __uint_as_float(y & 0xFFFF0000u)};
-        }
+    for (int e = 0; e < 4; ++e) {
+        h[e] = f32_to_bf16(v[e]);
+        o[e] = f32_to_bf16(v[e] - bf16_to_f32(h[e]));
     }
+    hi = u32x2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+    lo = u32x2{(uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+}
+__device__ __forceinline__ bf16x8 pair8(u32x2 a, u32x2 b) {
+    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+__device__ __forceinline__ bf16x8 lds16(const uint8_t* base, int off) {
+    return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(
+        (const __attribute__((address_space(3))) uint8_t*)(base + off));
+}
+__device__ __forceinline__ s16x4 lds_tr(const uint8_t* base, int off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(uintptr_t)(
+            (__attribute__((address_space(3))) const uint8_t*)(base + off)));
 }
 
-template <int KB, typename TQ>   // KB = k / 16 row blocks; TQ: float or uint16_t (bf16) Q, dO
+// The query row's slices d = 32 kc + 8 g .. + 7 (kc = 0, 1) of Q or dO, as loaded (zero at or
+// past the length: raw zeros), and as bf16 operands hi (and lo for fp32 inputs)
+template <typename TQ>
+struct RowOps {
+    u32x4 raw[2][sizeof(TQ) / 2];   // 16 bytes (bf16) or 32 bytes (fp32) per slice
+    __device__ void load(const TQ* row, int g) {
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int w = 0; w < (int)(sizeof(TQ) / 2); ++w)
+                raw[kc][w] = *(const u32x4*)(row + 32 * kc + 8 * g + 4 * w);   // w > 0: fp32 only
+    }
+    __device__ void zero() {
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int w = 0; w < (int)(sizeof(TQ) / 2); ++w) raw[kc][w] = u32x4{0u, 0u, 0u, 0u};
+    }
+    __device__ void ops(int kc, bf16x8& hi, bf16x8& lo) const {
+        if constexpr (sizeof(TQ) == 2) {
+            hi = __builtin_bit_cast(bf16x8, raw[kc][0]);
+        } else {
+            u32x2 h0, l0, h1, l1;
+            split4(__builtin_bit_cast(f32x4, raw[kc][0]), h0, l0);
+            split4(__builtin_bit_cast(f32x4, raw[kc][1]), h1, l1);
+            hi = pair8(h0, h1);
+            lo = pair8(l0, l1);
+        }
+    }
+};
+
+template <int KB, typename TQ>   // KB = k / 16 row blocks (even); TQ: float or uint16_t (bf16) Q, dO
 __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs a) {
     constexpr int K = KB * 16;
-    extern __shared__ float lds[];
-    float* kb = lds;              // [K][68]
-    float* vb = kb + K * kKS;     // [K][68]
+    constexpr int PL = K * 128;   // bytes of one [k][64] bf16 plane
+    constexpr bool QLO = sizeof(TQ) == 4;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
+    const uint8_t* kh = lds8;
+    const uint8_t* kl = lds8 + PL;
+    const uint8_t* vh = lds8 + 2 * PL;
+    const uint8_t* vl = lds8 + 3 * PL;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l = lane & 15;
     const int bh = blockIdx.y;
     const float* kg = a.Kb + (size_t)bh * K * 64;
     const float* vg = a.Vb + (size_t)bh * K * 64;
-    for (int e = tid; e < K * 16; e += 64 * kAttWaves) {   // 16-byte pieces
-        const int r = e >> 4, c4 = e & 15;
-        *(f32x4*)(kb + r * kKS + 4 * c4) = *(const f32x4*)(kg + 4 * e);
-        *(f32x4*)(vb + r * kKS + 4 * c4) = *(const f32x4*)(vg + 4 * e);
+    for (int e = tid; e < K * 16; e += 64 * kAttWaves) {   // 4 values (16 bytes) each
+        const int r = e >> 4, d = 4 * (e & 15);
+        const int off = kv_off(r, d);
+        u32x2 hi, lo;
+        split4(*(const f32x4*)(kg + 4 * e), hi, lo);
+        *(u32x2*)(lds8 + off) = hi;
+        *(u32x2*)(lds8 + PL + off) = lo;
+        split4(*(const f32x4*)(vg + 4 * e), hi, lo);
+        *(u32x2*)(lds8 + 2 * PL + off) = hi;
+        *(u32x2*)(lds8 + 3 * PL + off) = lo;
     }
     __syncthreads();   // the only barrier
     const int L = clamp_len(a.lengths, bh / a.H, a.n);
@@ -360,16 +419,15 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
     const float c = a.scale * 1.4426950408889634f;   // scores to base-2 exponents
     const int nblk = (a.n + kAttRows - 1) / kAttRows;
     const int blk0 = blockIdx.x * a.qb, blk1 = min(nblk, blk0 + a.qb);
-    // the row's slice [16 g, 16 g + 16) of Q and of dO (zero at or past the length)
-    auto load_rows = [&](int q, f32x4 (&qr)[4], f32x4 (&gr)[4]) {
-        load16((const TQ*)a.Q + head + (size_t)q * 64 + 16 * g, qr);
-        load16((const TQ*)a.dO + head + (size_t)q * 64 + 16 * g, gr);
-        if (q >= L) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) gr[u] = f32x4{};
-        }
+    RowOps<TQ> qr, gr;
+    auto load_rows = [&](int q) {
+        qr.load((const TQ*)a.Q + head + (size_t)q * 64, g);
+        if (q < L) gr.load((const TQ*)a.dO + head + (size_t)q * 64, g);
+        else gr.zero();
     };
-    f32x4 qr[4], gr[4];
+    // per-lane LDS offsets of the transposed Kbar^T reads: source lane s = l of group g reads
+    // columns 16 cb + 4 (l % 4) of rows 32 j + 4 g + l / 4 (+ 16)
+    const int tr_row = 4 * g + (l >> 2), tr_col = 4 * (l & 3);
     bool loaded = false;
     for (int blk = blk0; blk < blk1; ++blk) {
         const int q0 = blk * kAttRows + wave * 16;
@@ -381,7 +439,7 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
                 *(f32x4*)(a.dQ + head + (size_t)q * 64 + 16 * cb + 4 * g) = f32x4{};
             continue;
         }
-        if (!loaded) load_rows(q, qr, gr);
+        if (!loaded) load_rows(q);
         f32x4 st[KB], dp[KB];
 #pragma unroll
         for (int r = 0; r < KB; ++r) {
@@ -389,20 +447,23 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
             dp[r] = f32x4{};
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int kc = 0; kc < 2; ++kc) {
+            bf16x8 qh, ql, gh, gl;
+            qr.ops(kc, qh, ql);
+            gr.ops(kc, gh, gl);
 #pragma unroll
-            for (int r = 0; r < KB; r += 2) {
-                const f32x4 k0 = *(const f32x4*)(kb + (16 * r + l) * kKS + 16 * g + 4 * u);
-                const f32x4 k1 = *(const f32x4*)(kb + (16 * r + 16 + l) * kKS + 16 * g + 4 * u);
-                const f32x4 v0 = *(const f32x4*)(vb + (16 * r + l) * kKS + 16 * g + 4 * u);
-                const f32x4 v1 = *(const f32x4*)(vb + (16 * r + 16 + l) * kKS + 16 * g + 4 * u);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    st[r] = mfma_f32_16(k0[t], qr[u][t], st[r]);
-                    st[r + 1] = mfma_f32_16(k1[t], qr[u][t], st[r + 1]);
-                    dp[r] = mfma_f32_16(v0[t], gr[u][t], dp[r]);
-                    dp[r + 1] = mfma_f32_16(v1[t], gr[u][t], dp[r + 1]);
+            for (int r = 0; r < KB; ++r) {
+                const int off = kv_off(16 * r + l, 32 * kc + 8 * g);
+                const bf16x8 k0 = lds16(kh, off), k1 = lds16(kl, off);
+                const bf16x8 v0 = lds16(vh, off), v1 = lds16(vl, off);
+                st[r] = mfma16(k1, qh, st[r]);
+                dp[r] = mfma16(v1, gh, dp[r]);
+                if constexpr (QLO) {
+                    st[r] = mfma16(k0, ql, st[r]);
+                    dp[r] = mfma16(v0, gl, dp[r]);
                 }
+                st[r] = mfma16(k0, qh, st[r]);
+                dp[r] = mfma16(v0, gh, dp[r]);
             }
         }
         float mx = st[0][0];
@@ -445,19 +506,30 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
         // next block's rows into the same registers; they arrive during the dQ products
         loaded = false;
         if (blk + 1 < blk1 && q0 + kAttRows < min(a.n, L)) {
-            load_rows(q + kAttRows, qr, gr);
+            load_rows(q + kAttRows);
             loaded = true;
         }
-        // dQ^T = Kbar^T dS^T: reduction step (r, e) takes row 16 r + 4 g + e in lane group g
+        // dQ^T = Kbar^T dS^T over 32 slots at a time
         f32x4 dq[4] = {};
 #pragma unroll
-        for (int r = 0; r < KB; ++r)
+        for (int j = 0; j < KB / 2; ++j) {
+            u32x2 h0, l0, h1, l1;
+            split4(dp[2 * j], h0, l0);
+            split4(dp[2 * j + 1], h1, l1);
+            const bf16x8 bhi = pair8(h0, h1), blo = pair8(l0, l1);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float* krow = kb + (16 * r + 4 * g + e) * kKS + l;
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb) dq[cb] = mfma_f32_16(krow[16 * cb], dp[r][e], dq[cb]);
+            for (int cb = 0; cb < 4; ++cb) {
+                const int o0 = kv_off(32 * j + tr_row, 16 * cb + tr_col);
+                const int o1 = kv_off(32 * j + 16 + tr_row, 16 * cb + tr_col);
+                const bf16x8 ah = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lds_tr(kh, o0), lds_tr(kh, o1), 0, 1, 2, 3, 4, 5, 6, 7));
+                const bf16x8 al = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lds_tr(kl, o0), lds_tr(kl, o1), 0, 1, 2, 3, 4, 5, 6, 7));
+                dq[cb] = mfma16(al, bhi, dq[cb]);
+                dq[cb] = mfma16(ah, blo, dq[cb]);
+                dq[cb] = mfma16(ah, bhi, dq[cb]);
             }
+        }
         // dq[cb] element e of lane (g, l): dQ[q][16 cb + 4 g + e]
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
@@ -544,7 +616,7 @@ hipError_t launch_bw_gemm(const BwGemm& g, hipStream_t stream) {
 
 template <int KB, typename TQ>
 static hipError_t launch_attend_kb(const BwAttendArgs& a, hipStream_t stream) {
-    const size_t lds = (size_t)2 * KB * 16 * kKS * sizeof(float);
+    const size_t lds = (size_t)4 * KB * 16 * 128;   // Kbar, Vbar: hi and lo bf16 planes
     auto kern = bw_attend_kernel<KB, TQ>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
