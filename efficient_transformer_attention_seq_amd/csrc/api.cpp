@@ -79,8 +79,25 @@ size_t pair_tiles(const lf::ProjGeom& g) {
 size_t pair_sums_bytes(const lf::ProjGeom& g) {
     return round_up(pair_tiles(g) * (size_t)(g.k / g.slot_tiles) * g.upt * 64 * 4, 256);
 }
+// fp32 projection (one BwGemm launch for Kbar and Vbar, z = (which, b, h)): the reduction over
+// the positions is split into chunks of at least 32 until about 512 workgroups run, summed in
+// chunk order by the GEMM's second kernel.
+void f32_proj_plan(const lf_problem* p, int* splits, int* kchunk) {
+    const long long tiles = 2LL * p->batch * p->heads * ((p->k + 127) / 128);
+    long long s = 512 / std::max(1LL, tiles);
+    s = std::max(1LL, std::min<long long>(s, std::min(p->n / 32, 64)));
+    const int chunk = (int)((p->n + s - 1) / s + 31) / 32 * 32;
+    *kchunk = chunk;
+    *splits = (p->n + chunk - 1) / chunk;
+}
+
 size_t part_bytes(const lf_problem* p, const lf::ProjGeom& g) {
-    if (p->dtype != LF_BF16 || g.S <= 1) return 0;
+    if (p->dtype == LF_F32) {
+        int s, c;
+        f32_proj_plan(p, &s, &c);
+        return s > 1 ? (size_t)s * 2 * p->batch * p->heads * p->k * 64 * 4 : 0;   // Kbar and Vbar
+    }
+    if (g.S <= 1) return 0;
     if (g.S == 2) return pair_sums_bytes(g) + pair_tiles(g) * 8;
     return (size_t)g.S * 2 * p->batch * p->heads * p->k * p->d * 4;
 }
@@ -197,21 +214,25 @@ int do_project(const lf_problem* p, const void* K, const void* V, const void* E,
                const int32_t* lengths, void* Kbar, void* Vbar, void* part,
                const lf::ProjGeom& g, hipStream_t stream) {
     if (p->dtype == LF_F32) {
-        lf::F32Args a{};
-        a.K = (const float*)K;
-        a.V = (const float*)V;
-        a.E = (const float*)E;
-        a.F = (const float*)F;
-        a.lengths = lengths;
-        a.Kbar = (float*)Kbar;
-        a.Vbar = (float*)Vbar;
-        a.B = p->batch;
-        a.H = p->heads;
-        a.n = p->n;
-        a.k = p->k;
-        a.share = p->share;
-        a.scale = eff_scale(p);
-        return launch_status(lf::launch_proj_f32(a, stream));
+        // Kbar = E_h K, Vbar = F_h V on the split-bf16 batched GEMM (backward_f32.hip), one
+        // reduction per output tile: z = (b, h), M = k, N = 64, reduction over the positions
+        // before the length
+        const int B = p->batch, H = p->heads, n = p->n, k = p->k;
+        const long long kn = (long long)k * n, hn64 = (long long)n * 64, hk64 = (long long)k * 64;
+        // one launch for both: batch entries (b, h) then (b, h) again with F, V, Vbar
+        lf::BwGemm g{};
+        g.A = E; g.B = K; g.C = (float*)Kbar;
+        g.A2 = F; g.B2 = V; g.C2 = (float*)Vbar;
+        g.zhalf = B * H;
+        g.alpha = 1.0f;
+        g.M = k; g.N = 64; g.K = n; g.Z = 2 * B * H; g.zdiv = H; g.kblk = n;
+        g.k_len = lengths;
+        g.a_z2 = p->share == LF_SHARE_NONE ? kn : 0; g.a_i = n; g.a_kc = 1;
+        g.b_z1 = H * hn64; g.b_z2 = hn64; g.b_kc = 64; g.b_j = 1;
+        g.c_z1 = H * hk64; g.c_z2 = hk64; g.c_i = 64; g.c_j = 1;
+        f32_proj_plan(p, &g.splits, &g.kchunk);
+        g.part = (float*)part;
+        return launch_status(lf::launch_bw_gemm(g, stream));
     }
     lf::ProjBf16Args a{};
     a.K = (const uint16_t*)K;
@@ -239,15 +260,14 @@ int do_attend(const lf_problem* p, const void* Q, const void* Kbar, const void* 
     if (p->dtype == LF_F32) {
         lf::F32Args a{};
         a.Q = (const float*)Q;
-        a.Kbar = (float*)Kbar;
-        a.Vbar = (float*)Vbar;
+        a.Kbar = (const float*)Kbar;
+        a.Vbar = (const float*)Vbar;
         a.O = (float*)O;
         a.lengths = lengths;
         a.B = p->batch;
         a.H = p->heads;
         a.n = p->n;
         a.k = p->k;
-        a.share = p->share;
         a.scale = eff_scale(p);
         return launch_status(lf::launch_attend_f32(a, stream));
     }

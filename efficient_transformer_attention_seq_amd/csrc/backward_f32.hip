@@ -22,8 +22,7 @@
 
 #include "lf_device.h"
 #include "lf_launch.h"
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+#include "split_bf16.h"
 
 namespace lf {
 namespace {
@@ -195,14 +194,17 @@ __global__ __launch_bounds__(256) void bw_gemm_kernel(BwGemm g) {
 
     const int i0 = blockIdx.y * kGM, j0 = blockIdx.x * TN;
     const int z = blockIdx.z / g.splits, sp = blockIdx.z % g.splits;
-    const long long z1 = z / g.zdiv, z2 = z % g.zdiv;
+    // second operand set for the upper half of the batch (zhalf > 0)
+    const bool hi2 = g.zhalf > 0 && z >= g.zhalf;
+    const int zo = hi2 ? z - g.zhalf : z;
+    const long long z1 = zo / g.zdiv, z2 = zo % g.zdiv;
     const int row_end = g.row_len ? clamp_len(g.row_len, (int)z1, g.M) : g.M;
     const int kbeg = sp * g.kchunk;
     int kend = min(g.K, kbeg + g.kchunk);
     if (g.k_len) kend = min(kend, clamp_len(g.k_len, (int)z1, g.K));   // terms past it are zero
     if (i0 >= row_end) kend = kbeg;                                      // rows written as zero
-    const TA* A = (const TA*)g.A + z1 * g.a_z1 + z2 * g.a_z2 + (long long)i0 * g.a_i;
-    const TB* Bm = (const TB*)g.B + z1 * g.b_z1 + z2 * g.b_z2 + (long long)j0 * g.b_j;
+    const TA* A = (const TA*)(hi2 ? g.A2 : g.A) + z1 * g.a_z1 + z2 * g.a_z2 + (long long)i0 * g.a_i;
+    const TB* Bm = (const TB*)(hi2 ? g.B2 : g.B) + z1 * g.b_z1 + z2 * g.b_z2 + (long long)j0 * g.b_j;
     TileLoader<TA, kGM, AKF> la;
     TileLoader<TB, TN, BKF> lb;
     la.init(tid, g.a_i, g.a_kc);
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(256) void bw_gemm_kernel(BwGemm g) {
         __syncthreads();
     }
     // C tile element j of lane (h, l): row 8 (j / 4) + 4 h + j % 4, column l
-    float* C = g.C + z1 * g.c_z1 + z2 * g.c_z2;
+    float* C = (hi2 ? g.C2 : g.C) + z1 * g.c_z1 + z2 * g.c_z2;
     float* part = g.splits > 1 ? g.part + ((size_t)sp * g.Z + z) * g.M * g.N : nullptr;
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
@@ -294,9 +296,11 @@ __global__ __launch_bounds__(256) void bw_gemm_reduce_kernel(BwGemm g) {
     }
     const int z = (int)(idx / mn);
     const int i = (int)((idx % mn) / g.N), j = (int)(idx % g.N);
-    const long long z1 = z / g.zdiv, z2 = z % g.zdiv;
+    const bool hi2 = g.zhalf > 0 && z >= g.zhalf;
+    const int zo = hi2 ? z - g.zhalf : z;
+    const long long z1 = zo / g.zdiv, z2 = zo % g.zdiv;
     const bool keep = !g.row_len || i < clamp_len(g.row_len, (int)z1, g.M);
-    float* c = g.C + z1 * g.c_z1 + z2 * g.c_z2 + (long long)i * g.c_i + (long long)j * g.c_j;
+    float* c = (hi2 ? g.C2 : g.C) + z1 * g.c_z1 + z2 * g.c_z2 + (long long)i * g.c_i + (long long)j * g.c_j;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         const float v = g.alpha * s[e] + (g.beta != 0.0f ? g.beta * c[e] : 0.0f);
@@ -324,68 +328,6 @@ __global__ __launch_bounds__(256) void bw_gemm_reduce_kernel(BwGemm g) {
 // rows are left unwritten (the reductions over queries stop at the length) and its gradients are
 // zero.
 constexpr int kAttWaves = 8, kAttRows = 16 * kAttWaves;
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// byte offset of element (r, d) of a [k][64] bf16 plane (d % 4 == 0: 8 bytes in one chunk)
-__device__ __forceinline__ int kv_off(int r, int d) {
-    return r * 128 + (((d >> 3) ^ ((r ^ (r >> 3)) & 7)) << 4) + (d & 7) * 2;
-}
-// hi = bf16(v), lo = bf16(v - hi) of four values, as packed pairs
-__device__ __forceinline__ void split4(f32x4 v, u32x2& hi, u32x2& lo) {
-    uint16_t h[4], o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        h[e] = f32_to_bf16(v[e]);
-        o[e] = f32_to_bf16(v[e] - bf16_to_f32(h[e]));
-    }
-    hi = u32x2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-    lo = u32x2{(uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
-}
-__device__ __forceinline__ bf16x8 pair8(u32x2 a, u32x2 b) {
-    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
-}
-__device__ __forceinline__ bf16x8 lds16(const uint8_t* base, int off) {
-    return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(
-        (const __attribute__((address_space(3))) uint8_t*)(base + off));
-}
-__device__ __forceinline__ s16x4 lds_tr(const uint8_t* base, int off) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(uintptr_t)(
-            (__attribute__((address_space(3))) const uint8_t*)(base + off)));
-}
-
-// The query row's slices d = 32 kc + 8 g .. + 7 (kc = 0, 1) of Q or dO, as loaded (zero at or
-// past the length: raw zeros), and as bf16 operands hi (and lo for fp32 inputs)
-template <typename TQ>
-struct RowOps {
-    u32x4 raw[2][sizeof(TQ) / 2];   // 16 bytes (bf16) or 32 bytes (fp32) per slice
-    __device__ void load(const TQ* row, int g) {
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int w = 0; w < (int)(sizeof(TQ) / 2); ++w)
-                raw[kc][w] = *(const u32x4*)(row + 32 * kc + 8 * g + 4 * w);   // w > 0: fp32 only
-    }
-    __device__ void zero() {
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int w = 0; w < (int)(sizeof(TQ) / 2); ++w) raw[kc][w] = u32x4{0u, 0u, 0u, 0u};
-    }
-    __device__ void ops(int kc, bf16x8& hi, bf16x8& lo) const {
-        if constexpr (sizeof(TQ) == 2) {
-            hi = __builtin_bit_cast(bf16x8, raw[kc][0]);
-        } else {
-            u32x2 h0, l0, h1, l1;
-            split4(__builtin_bit_cast(f32x4, raw[kc][0]), h0, l0);
-            split4(__builtin_bit_cast(f32x4, raw[kc][1]), h1, l1);
-            hi = pair8(h0, h1);
-            lo = pair8(l0, l1);
-        }
-    }
-};
 
 template <int KB, typename TQ>   // KB = k / 16 row blocks (even); TQ: float or uint16_t (bf16) Q, dO
 __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs a) {
@@ -552,7 +494,8 @@ static bool vec_aligned(const BwGemm& g) {
                                : ok(g.a_i, g.a_kc, g.a_z1, g.a_z2, g.a_kb, va);
     const bool b = g.b_kc == 1 ? ok(g.b_kc, g.b_j, g.b_z1, g.b_z2, g.b_kb, vb)
                                : ok(g.b_j, g.b_kc, g.b_z1, g.b_z2, g.b_kb, vb);
-    return a && b && ((uintptr_t)g.A & 15) == 0 && ((uintptr_t)g.B & 15) == 0;
+    return a && b && ((uintptr_t)g.A & 15) == 0 && ((uintptr_t)g.B & 15) == 0 &&
+           (g.zhalf == 0 || (((uintptr_t)g.A2 & 15) == 0 && ((uintptr_t)g.B2 & 15) == 0));
 }
 
 void bw_gemm_plan(BwGemm& g) {

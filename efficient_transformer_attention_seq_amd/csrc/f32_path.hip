@@ -1,136 +1,179 @@
-// fp32 path: the same Linformer layer computed in fp32 with vector FMAs (Linformer 요약 설명,
-// section "Model").  It serves fp32 accuracy on small workloads (the single-head n = 512 case is
-// 34 MFLOP): what bounds it is latency and the number of workgroups, so both kernels spread the
-// work over many short workgroups rather than feeding the matrix cores.
+// fp32 path: the same Linformer layer to fp32 accuracy (Linformer 요약 설명, section "Model":
+// n x k scores, softmax over the k projected slots of each query, weighted sum of Vbar).  The
+// projection Kbar = E K, Vbar = F V runs on the strided batched GEMM of backward_f32.hip; the
+// attention below.  Both multiply on the bf16 matrix cores as split bf16 pairs with fp32
+// accumulation (split_bf16.h: every operand carried to within 2^-16), which holds the fp32 path's
+// 1e-4 bar with room to spare (tested: 1e-5 on Kbar, 1e-4 on O).
+//
+// attend_f32_kernel: one 8-wave workgroup per (b, h) and range of 128-query blocks, Kbar and Vbar
+// resident in LDS as hi and lo bf16 planes.  Each wave owns 16 query rows q0 + l of a block and
+// works on transposed products so that lane (g, l) holds the values of query l (as the backward's
+// fused kernel does):
+//   S^T = Kbar Q^T   (k x 16: lane holds rows 16 rb + 4 g + e), Q split into hi and lo in
+//                    registers (slices d = 32 kc + 8 g .. + 7), the planes' rows as A operands
+//   the exact softmax down each column (within the lane, then across the four lanes g), in base 2
+//   O^T = Vbar^T P^T (64 x 16): per 32 slots the B operand is the lane's unnormalised weights of
+//                    rows 32 j + 4 g + e and 32 j + 16 + 4 g + e straight from the accumulators
+//                    (split into hi and lo), the A operand Vbar^T read at exactly those slots
+//                    with the transposing ds_read_b64_tr_b16; each column divided by its weight
+//                    sum at the end
+// Rows at or past the length are written as zeros.
 #include "lf_device.h"
 #include "lf_launch.h"
+#include "split_bf16.h"
 
 namespace lf {
 namespace {
 
-__device__ __forceinline__ const float* f32_matrix(const F32Args& a, int which, int h) {
-    if (a.share == 0) return (which ? a.F : a.E) + (size_t)h * a.k * a.n;
-    if (a.share == 1) return which ? a.F : a.E;
-    return a.E;
-}
+constexpr int kAttWaves = 8, kAttRows = 16 * kAttWaves;
 
-// Kbar[b,h][r][c] = sum_{t < L_b} E_h[r][t] K[b,h][t][c]  (and Vbar with F, V).
-// Block (4 waves): 8 slots x 64 columns of one (which, b, h); lane = column, wave w sums the
-// positions of the w-th contiguous quarter of [0, L) in ascending order (8 independent
-// accumulators; the 8 E entries of a position are the same for the whole wave, so they come in
-// through scalar loads), then wave 0 adds the four quarters in order.
-constexpr int kProjSlots = 8;
-__global__ __launch_bounds__(256) void proj_f32_kernel(F32Args a) {
-    __shared__ float part[4][kProjSlots][64];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r0 = blockIdx.x * kProjSlots;
-    const int BH = a.B * a.H;
-    const int which = blockIdx.y / BH;
-    const int bh = blockIdx.y % BH;
-    const int b = bh / a.H, h = bh % a.H;
-    const int L = clamp_len(a.lengths, b, a.n);
-    const float* A = f32_matrix(a, which, h) + (size_t)r0 * a.n;
-    const float* X = (which ? a.V : a.K) + (size_t)bh * a.n * kHeadDim + lane;
-    const int t0 = (int)((long long)L * wave / 4), t1 = (int)((long long)L * (wave + 1) / 4);
-    float acc[kProjSlots];
-#pragma unroll
-    for (int i = 0; i < kProjSlots; ++i) acc[i] = 0.0f;
-#pragma unroll 4
-    for (int t = t0; t < t1; ++t) {
-        const float x = X[(size_t)t * kHeadDim];
-#pragma unroll
-        for (int i = 0; i < kProjSlots; ++i) acc[i] = __builtin_fmaf(A[(size_t)i * a.n + t], x, acc[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < kProjSlots; ++i) part[wave][i][lane] = acc[i];
-    __syncthreads();
-    if (wave != 0) return;
-    float* out = (which ? a.Vbar : a.Kbar) + ((size_t)bh * a.k + r0) * kHeadDim + lane;
-#pragma unroll
-    for (int i = 0; i < kProjSlots; ++i)
-        out[(size_t)i * kHeadDim] = ((part[0][i][lane] + part[1][i][lane]) + part[2][i][lane]) + part[3][i][lane];
-}
-
-// One query per wave (4 per block), the head's Kbar and Vbar resident in LDS.  Scores: lane = slot
-// (k / 64 passes), the query's 64 values in every lane's registers; softmax over the k slots with
-// wave reductions; weighted sum: lane = output column, the weights read back from LDS.
-constexpr int kMaxK = 256;
-__global__ __launch_bounds__(256) void attend_f32_kernel(F32Args a) {
-    __shared__ float sK[kMaxK * 65];   // row stride 65: lane r reads row r conflict-free
-    __shared__ float sV[kMaxK * 64];
-    __shared__ float sw[4][kMaxK];
+template <int KB>   // KB = k / 16 row blocks (even)
+__global__ __launch_bounds__(64 * kAttWaves) void attend_f32_kernel(F32Args a, int qb) {
+    constexpr int K = KB * 16;
+    constexpr int PL = K * 128;   // bytes of one [k][64] bf16 plane
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
+    const uint8_t* kh = lds8;
+    const uint8_t* kl = lds8 + PL;
+    const uint8_t* vh = lds8 + 2 * PL;
+    const uint8_t* vl = lds8 + 3 * PL;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, l = lane & 15;
     const int bh = blockIdx.y;
-    const int b = bh / a.H;
-    const int L = clamp_len(a.lengths, b, a.n);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const float* gK = a.Kbar + (size_t)bh * a.k * kHeadDim;
-    const float* gV = a.Vbar + (size_t)bh * a.k * kHeadDim;
-    for (int i = tid; i < a.k * kHeadDim; i += 256) {
-        sK[(i >> 6) * 65 + (i & 63)] = gK[i];
-        sV[i] = gV[i];
+    const float* kg = a.Kbar + (size_t)bh * K * 64;
+    const float* vg = a.Vbar + (size_t)bh * K * 64;
+    for (int e = tid; e < K * 16; e += 64 * kAttWaves) {   // 4 values (16 bytes) each
+        const int r = e >> 4, d = 4 * (e & 15);
+        const int off = kv_off(r, d);
+        u32x2 hi, lo;
+        split4(*(const f32x4*)(kg + 4 * e), hi, lo);
+        *(u32x2*)(lds8 + off) = hi;
+        *(u32x2*)(lds8 + PL + off) = lo;
+        split4(*(const f32x4*)(vg + 4 * e), hi, lo);
+        *(u32x2*)(lds8 + 2 * PL + off) = hi;
+        *(u32x2*)(lds8 + 3 * PL + off) = lo;
     }
-    __syncthreads();
-    const int q = blockIdx.x * 4 + wave;
-    if (q >= a.n) return;
-    float* orow = a.O + ((size_t)bh * a.n + q) * kHeadDim;
-    if (q >= L) {
-        orow[lane] = 0.0f;
-        return;
-    }
-    float qv[64];
-    const f32x4* qrow = (const f32x4*)(a.Q + ((size_t)bh * a.n + q) * kHeadDim);
+    __syncthreads();   // the only barrier
+    const int L = clamp_len(a.lengths, bh / a.H, a.n);
+    const size_t head = (size_t)bh * a.n * 64;
+    const float c = a.scale * kLog2e;   // scores to base-2 exponents
+    const int nblk = (a.n + kAttRows - 1) / kAttRows;
+    const int blk0 = blockIdx.x * qb, blk1 = min(nblk, blk0 + qb);
+    // per-lane LDS offsets of the transposed Vbar^T reads: source lane s = l of group g reads
+    // columns 16 cb + 4 (l % 4) of rows 32 j + 4 g + l / 4 (+ 16)
+    const int tr_row = 4 * g + (l >> 2), tr_col = 4 * (l & 3);
+    RowOps<float> qr;
+    bool loaded = false;
+    for (int blk = blk0; blk < blk1; ++blk) {
+        const int q0 = blk * kAttRows + wave * 16;
+        if (q0 >= a.n) break;
+        const int q = q0 + l;
+        if (q0 >= L) {   // wholly past the length
 #pragma unroll
-    for (int c4 = 0; c4 < 16; ++c4) {
-        const f32x4 v = qrow[c4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qv[4 * c4 + e] = v[e];
-    }
-    float sc[kMaxK / 64];
-    float m = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < kMaxK / 64; ++p) {
-        const int r = 64 * p + lane;
-        float s = 0.0f;
-        if (r < a.k) {
-#pragma unroll
-            for (int c = 0; c < 64; ++c) s = __builtin_fmaf(qv[c], sK[r * 65 + c], s);
-            s *= a.scale;
-            m = fmaxf(m, s);
+            for (int cb = 0; cb < 4; ++cb)
+                *(f32x4*)(a.O + head + (size_t)q * 64 + 16 * cb + 4 * g) = f32x4{};
+            continue;
         }
-        sc[p] = s;
-    }
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    float z = 0.0f;
+        if (!loaded) qr.load(a.Q + head + (size_t)q * 64, g);
+        f32x4 st[KB];
 #pragma unroll
-    for (int p = 0; p < kMaxK / 64; ++p) {
-        const int r = 64 * p + lane;
-        if (r < a.k) {
-            const float w = expf(sc[p] - m);
-            sw[wave][r] = w;
-            z += w;
+        for (int r = 0; r < KB; ++r) st[r] = f32x4{};
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            bf16x8 qh, ql;
+            qr.ops(kc, qh, ql);
+#pragma unroll
+            for (int r = 0; r < KB; ++r) {
+                const int off = kv_off(16 * r + l, 32 * kc + 8 * g);
+                const bf16x8 k0 = lds16(kh, off), k1 = lds16(kl, off);
+                st[r] = mfma16(k1, qh, st[r]);
+                st[r] = mfma16(k0, ql, st[r]);
+                st[r] = mfma16(k0, qh, st[r]);
+            }
         }
+        // next block's Q slices into the same registers; they arrive during the products below
+        loaded = false;
+        if (blk + 1 < blk1 && q0 + kAttRows < min(a.n, L)) {
+            qr.load(a.Q + head + (size_t)(q + kAttRows) * 64, g);
+            loaded = true;
+        }
+        float mx = st[0][0];
+#pragma unroll
+        for (int r = 0; r < KB; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, st[r][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mc = mx * c;
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < KB; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                st[r][e] = __builtin_amdgcn_exp2f(fmaf(st[r][e], c, -mc));
+                sum += st[r][e];
+            }
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        // O^T = Vbar^T W^T over 32 slots at a time, then divided by the weight sum
+        f32x4 o[4] = {};
+#pragma unroll
+        for (int j = 0; j < KB / 2; ++j) {
+            u32x2 h0, l0, h1, l1;
+            split4(st[2 * j], h0, l0);
+            split4(st[2 * j + 1], h1, l1);
+            const bf16x8 bhi = pair8(h0, h1), blo = pair8(l0, l1);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const int o0 = kv_off(32 * j + tr_row, 16 * cb + tr_col);
+                const int o1 = kv_off(32 * j + 16 + tr_row, 16 * cb + tr_col);
+                const bf16x8 ah = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lds_tr(vh, o0), lds_tr(vh, o1), 0, 1, 2, 3, 4, 5, 6, 7));
+                const bf16x8 al = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lds_tr(vl, o0), lds_tr(vl, o1), 0, 1, 2, 3, 4, 5, 6, 7));
+                o[cb] = mfma16(al, bhi, o[cb]);
+                o[cb] = mfma16(ah, blo, o[cb]);
+                o[cb] = mfma16(ah, bhi, o[cb]);
+            }
+        }
+        // o[cb] element e of lane (g, l): O[q][16 cb + 4 g + e]
+        const float inv = 1.0f / sum;
+        const bool live = q < L;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+            *(f32x4*)(a.O + head + (size_t)q * 64 + 16 * cb + 4 * g) = live ? o[cb] * inv : f32x4{};
     }
-    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's weights are in LDS
-    __builtin_amdgcn_wave_barrier();
-    float acc = 0.0f;
-    for (int r = 0; r < a.k; ++r) acc = __builtin_fmaf(sw[wave][r], sV[r * 64 + lane], acc);
-    orow[lane] = acc / z;
+}
+
+template <int KB>
+hipError_t launch_kb(const F32Args& a, hipStream_t stream) {
+    const size_t lds = (size_t)4 * KB * 16 * 128;   // Kbar, Vbar: hi and lo bf16 planes
+    auto kern = attend_f32_kernel<KB>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    // about three rounds of one workgroup per compute unit (MI355X: 256)
+    const int nblk = (a.n + kAttRows - 1) / kAttRows;
+    const int qb = max(1, min(nblk, nblk * a.B * a.H / 768));
+    hipLaunchKernelGGL(kern, dim3((nblk + qb - 1) / qb, a.B * a.H), dim3(64 * kAttWaves), lds,
+                       stream, a, qb);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_proj_f32(const F32Args& a, hipStream_t stream) {
-    hipLaunchKernelGGL(proj_f32_kernel, dim3(a.k / kProjSlots, 2 * a.B * a.H), dim3(256), 0, stream,
-                       a);
-    return hipGetLastError();
-}
-
 hipError_t launch_attend_f32(const F32Args& a, hipStream_t stream) {
-    hipLaunchKernelGGL(attend_f32_kernel, dim3((a.n + 3) / 4, a.B * a.H), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    if (a.n % 16 || a.B * a.H > 65535) return hipErrorInvalidValue;
+    switch (a.k / 32) {   // k % 32 == 0, 32 .. 256
+        case 1: return launch_kb<2>(a, stream);
+        case 2: return launch_kb<4>(a, stream);
+        case 3: return launch_kb<6>(a, stream);
+        case 4: return launch_kb<8>(a, stream);
+        case 5: return launch_kb<10>(a, stream);
+        case 6: return launch_kb<12>(a, stream);
+        case 7: return launch_kb<14>(a, stream);
+        case 8: return launch_kb<16>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace lf

@@ -86,17 +86,14 @@ struct AttendBf16Args {
     int nlogical;  // persistent grid size (multiple of 8)
 };
 
+// fp32 attention (f32_path.hip); the fp32 projection is a BwGemm (below)
 struct F32Args {
-    const float* Q;
-    const float* K;
-    const float* V;
-    const float* E;
-    const float* F;
+    const float* Q;         // [B, H, n, 64]
     const int32_t* lengths;
-    float* Kbar;
-    float* Vbar;
+    const float* Kbar;      // [B, H, k, 64], unscaled
+    const float* Vbar;
     float* O;
-    int B, H, n, k, share;
+    int B, H, n, k;
     float scale;
 };
 
@@ -142,6 +139,12 @@ struct BwGemm {
     const int32_t* bj_len;    // optional: B(z, kk, j) reads as zero for j >= bj_len[kb / bj_div]
     int bj_div;
     int a_bf16, b_bf16;
+    // optional: batch entries z >= zhalf (> 0) use A2, B2, C2 with z - zhalf (two products of one
+    // shape in one launch: Z = 2 zhalf)
+    int zhalf;
+    const void* A2;
+    const void* B2;
+    float* C2;
 };
 
 // Chooses splits / kchunk for g's shape (enough workgroups to cover the chip).
@@ -231,7 +234,6 @@ bool proj_geometry(int B, int H, int n, int k, int share, int split_override,
 
 hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream);
 hipError_t launch_attend_bf16(const AttendBf16Args& a, hipStream_t stream);
-hipError_t launch_proj_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_attend_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_dense_bf16(const DenseBf16Args& a, hipStream_t stream);
 hipError_t launch_linear_bf16(const LinearBf16Args& a, hipStream_t stream);
