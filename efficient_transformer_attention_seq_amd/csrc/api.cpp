@@ -210,9 +210,10 @@ int check_project_args(const lf_problem* p, const void* K, const void* V, const 
     return LF_OK;
 }
 
+// Kbar, Vbar in the attention kernels' formats, or (f32_out, the backward pass) unscaled fp32
 int do_project(const lf_problem* p, const void* K, const void* V, const void* E, const void* F,
                const int32_t* lengths, void* Kbar, void* Vbar, void* part,
-               const lf::ProjGeom& g, hipStream_t stream) {
+               const lf::ProjGeom& g, hipStream_t stream, bool f32_out = false) {
     if (p->dtype == LF_F32) {
         // Kbar = E_h K, Vbar = F_h V on the split-bf16 batched GEMM (backward_f32.hip), one
         // reduction per output tile: z = (b, h), M = k, N = 64, reduction over the positions
@@ -245,6 +246,11 @@ int do_project(const lf_problem* p, const void* K, const void* V, const void* E,
     a.Klo = (uint8_t*)Kbar + 2 * e;
     a.Ksc = (uint8_t*)Kbar + 3 * e;
     a.Vb = (uint16_t*)Vbar;
+    if (f32_out) {
+        a.Khi = nullptr; a.Klo = nullptr; a.Ksc = nullptr; a.Vb = nullptr;
+        a.Kf = (float*)Kbar;
+        a.Vf = (float*)Vbar;
+    }
     a.part = (float*)part;
     a.c = eff_scale(p) * lf::kLog2e;
     a.g = g;
@@ -341,18 +347,17 @@ int do_conv(const lf_problem* p, const void* K, const void* V, const void* wE, c
 
 // ---- backward pass
 struct BwWs {
-    size_t kb, vb, p, ds, dkb, dvb, part, total;   // byte offsets
+    size_t kb, vb, stats, dkb, dvb, part, total;   // byte offsets
 };
 
 void bw_ws(const lf_problem* p, BwWs* w) {
     const size_t kv = (size_t)p->batch * p->heads * p->k * 64 * 4;
-    const size_t pk = (size_t)p->batch * p->heads * p->n * p->k * 4;
+    const size_t st = (size_t)p->batch * p->heads * p->n * 4 * 4;   // 4 floats per query
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o += round_up(bytes, 256); return at; };
     w->kb = take(kv);
     w->vb = take(kv);
-    w->p = take(pk);
-    w->ds = take(pk);
+    w->stats = take(st);
     w->dkb = take(kv);
     w->dvb = take(kv);
     // split-reduction partial sums, the largest any of the backward's GEMMs asks for
@@ -362,6 +367,8 @@ void bw_ws(const lf_problem* p, BwWs* w) {
     part = std::max(part, lf::bw_gemm_part_bytes(k, n, unshared ? B * 64 : B * H * 64,
                                                  unshared ? H : 1));                // dE, dF
     part = std::max(part, lf::bw_gemm_part_bytes(n, 64, k, B * H));                // dK, dV
+    lf::ProjGeom g;
+    if (geometry(p, &g)) part = std::max(part, part_bytes(p, g));                  // Kbar, Vbar
     w->part = take(part);
     w->total = o;
 }
@@ -962,8 +969,8 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
 
     hipStream_t strm = (hipStream_t)stream;
     uint8_t* b = (uint8_t*)ws;
-    float *Kb = (float*)(b + w.kb), *Vb = (float*)(b + w.vb), *P = (float*)(b + w.p);
-    float *dS = (float*)(b + w.ds), *dKb = (float*)(b + w.dkb), *dVb = (float*)(b + w.dvb);
+    float *Kb = (float*)(b + w.kb), *Vb = (float*)(b + w.vb), *stats = (float*)(b + w.stats);
+    float *dKb = (float*)(b + w.dkb), *dVb = (float*)(b + w.dvb);
     float* part = (float*)(b + w.part);
     auto run_gemm = [&](lf::BwGemm& g) {
         lf::bw_gemm_plan(g);
@@ -978,44 +985,29 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
     const bool unshared = p->share == LF_SHARE_NONE;
     hipError_t e = hipSuccess;
     const long long hn64 = (long long)n * 64, hk64 = (long long)k * 64, kn = (long long)k * n;
-    // Kbar = E_h K, Vbar = F_h V: z = (b, h), M = k, N = 64, reduction over the positions before
-    // the length (K, V rows past it are zero)
-    auto project = [&](const void* A, const void* X, float* out) {
-        lf::BwGemm g = gemm0();
-        g.A = A; g.B = X; g.C = out; g.a_bf16 = g.b_bf16 = bf;
-        g.M = k; g.N = 64; g.K = n; g.Z = B * H; g.zdiv = H; g.kblk = n;
-        g.k_len = lengths;
-        g.a_z2 = unshared ? kn : 0; g.a_i = n; g.a_kc = 1;
-        g.b_z1 = H * hn64; g.b_z2 = hn64; g.b_kc = 64; g.b_j = 1;
-        g.c_z1 = H * hk64; g.c_z2 = hk64; g.c_i = 64; g.c_j = 1;
-        return run_gemm(g);
-    };
-    e = project(E, K, Kb);
-    if (e == hipSuccess) e = project(Fr, V, Vb);
-    if (e != hipSuccess) return LF_ERR_LAUNCH;
+    // Kbar = E_h K, Vbar = F_h V in fp32, by the forward pass's projection (positions past the
+    // length contribute nothing)
+    {
+        lf::ProjGeom g;
+        if (!geometry(p, &g)) return LF_ERR_SHAPE;
+        st = do_project(p, K, V, E, Fr, lengths, Kb, Vb, part, g, strm, true);
+        if (st) return st;
+    }
     lf::BwAttendArgs at{};
-    at.Q = Q; at.dO = dO; at.in_bf16 = bf; at.Kb = Kb; at.Vb = Vb; at.P = P; at.dS = dS; at.dQ = dQ;
+    at.Q = Q; at.dO = dO; at.in_bf16 = bf; at.Kb = Kb; at.Vb = Vb; at.stats = stats; at.dQ = dQ;
     at.B = B; at.H = H; at.n = n; at.k = k; at.scale = s; at.lengths = lengths;
     {   // about three rounds of one workgroup per compute unit (MI355X: 256)
         const int nblk = (n + 127) / 128;
         at.qb = std::max(1, std::min(nblk, nblk * B * H / 768));
     }
     if (lf::launch_bw_attend(at, strm) != hipSuccess) return LF_ERR_LAUNCH;
-    // dVbar = P^T dO, dKbar = s dS^T Q: z = (b, h), M = k, N = 64, reduction over the queries
-    // before the length (P, dS rows past it are not written; dO and dS vanish there)
-    auto reduce_q = [&](const float* A, const void* X, float* out, float alpha) {
-        lf::BwGemm g = gemm0();
-        g.A = A; g.B = X; g.C = out; g.alpha = alpha; g.b_bf16 = bf;
-        g.M = k; g.N = 64; g.K = n; g.Z = B * H; g.zdiv = H; g.kblk = n;
-        g.k_len = lengths;
-        g.a_z1 = H * kn; g.a_z2 = kn; g.a_i = 1; g.a_kc = k;
-        g.b_z1 = H * hn64; g.b_z2 = hn64; g.b_kc = 64; g.b_j = 1;
-        g.c_z1 = H * hk64; g.c_z2 = hk64; g.c_i = 64; g.c_j = 1;
-        return run_gemm(g);
-    };
-    e = reduce_q(P, dO, dVb, 1.0f);
-    if (e == hipSuccess) e = reduce_q(dS, Q, dKb, s);
-    if (e != hipSuccess) return LF_ERR_LAUNCH;
+    // dVbar = P^T dO, dKbar = s dS^T Q, reductions over the queries before the length, P and dS
+    // recomputed from the statistics the kernel above stored
+    lf::BwKvArgs kv{};
+    kv.Q = Q; kv.dO = dO; kv.in_bf16 = bf; kv.Kb = Kb; kv.Vb = Vb; kv.stats = stats;
+    kv.lengths = lengths; kv.dKb = dKb; kv.dVb = dVb;
+    kv.B = B; kv.H = H; kv.n = n; kv.k = k; kv.scale = s;
+    if (lf::launch_bw_kv(kv, strm) != hipSuccess) return LF_ERR_LAUNCH;
     // dE (+)= dXbar X^T: M = k, N = n, reduction over (b, c) (unshared: z = h) or over (b, h, c);
     // positions at or past item b's length read as zero
     auto grad_mat = [&](const float* dXb, const void* X, float* out, float beta) {

@@ -4,12 +4,14 @@
 // positions contribute nothing, and rows of O past the length are fixed at zero):
 //   Kbar = E K, Vbar = F V (recomputed),  P = softmax(s Q Kbar^T)
 //   dP = dO Vbar^T,  dS = P o (dP - rowsum(P o dP)),  dQ = s dS Kbar        (bw_attend_kernel)
-//   dVbar = P^T dO,  dKbar = s dS^T Q                                        (bw_gemm_kernel)
+//   dVbar = P^T dO,  dKbar = s dS^T Q   (P, dS recomputed per slot block)   (bw_kv_kernel)
 //   dE += dKbar K^T, dK = E^T dKbar, dF += dVbar V^T, dV = F^T dVbar         (bw_gemm_kernel)
 // Every contraction runs on the matrix cores with fp32 accumulation: one strided, batched GEMM
-// (split along the reduction when its output is too small to fill the chip) and a fused kernel for
-// P, the softmax Jacobian and dQ with Kbar and Vbar resident in LDS.  Both read the inputs in
-// their own dtype and never read the masked rows.
+// (split along the reduction when its output is too small to fill the chip) and two fused kernels
+// with Kbar and Vbar resident on chip, one per query block (P, the softmax Jacobian, dQ and the
+// per-query softmax statistics) and one per slot block (P and dS again from those statistics, and
+// the reductions over the queries), so no n x k matrix is ever stored, as in FlashAttention-2's
+// backward.  All read the inputs in their own dtype and never read the masked rows.
 //
 // The GEMM multiplies fp32 operands as split bf16 pairs (the "bf16x3" scheme of Henry, Tang and
 // Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype For Higher-Precision
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(256) void bw_gemm_reduce_kernel(BwGemm g) {
     }
 }
 
-// ---- per (b, h) and a range of 128-query blocks: P and dS ([n, k]) and dQ, as split bf16
+// ---- per (b, h) and a range of 128-query blocks: the softmax statistics and dQ, as split bf16
 // products (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Kbar and Vbar sit in LDS for the whole
 // range as bf16 hi and lo planes ([k][64], 16-byte chunks XOR-swizzled by (r ^ r >> 3) & 7).  Each
 // wave owns 16 query rows q0 + l of a block and works on transposed products, so that lane (g, l)
@@ -323,10 +325,11 @@ __global__ __launch_bounds__(256) void bw_gemm_reduce_kernel(BwGemm g) {
 //        transposing ds_read_b64_tr_b16 (lane i of a 16-lane group receives element i % 4 of
 //        source lanes 4 r + i / 4: source lane s reads the 4 columns 16 cb + 4 (s % 4) of row
 //        32 j + 4 g + s / 4, so lane i gets column 16 cb + i of those rows)
-// The next block's Q, dO slices are loaded into registers before this block's dQ products.  A
-// wave whose 16 rows all lie at or past the item's length only writes zero dQ rows: its P and dS
-// rows are left unwritten (the reductions over queries stop at the length) and its gradients are
-// zero.
+// Per query it stores (c m, 1 / sum, D) (D = rowsum(P o dP)), from which bw_kv_kernel recomputes
+// P and dS for the reductions over the queries, so neither [n, k] matrix reaches memory.  The next
+// block's Q, dO slices are loaded into registers before this block's dQ products.  A wave whose 16
+// rows all lie at or past the item's length only writes zero dQ rows (its statistics are left
+// unwritten: bw_kv_kernel never uses queries past the length).
 constexpr int kAttWaves = 8, kAttRows = 16 * kAttWaves;
 
 template <int KB, typename TQ>   // KB = k / 16 row blocks (even); TQ: float or uint16_t (bf16) Q, dO
@@ -344,28 +347,20 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
     const int bh = blockIdx.y;
     const float* kg = a.Kb + (size_t)bh * K * 64;
     const float* vg = a.Vb + (size_t)bh * K * 64;
-    for (int e = tid; e < K * 16; e += 64 * kAttWaves) {   // 4 values (16 bytes) each
-        const int r = e >> 4, d = 4 * (e & 15);
-        const int off = kv_off(r, d);
-        u32x2 hi, lo;
-        split4(*(const f32x4*)(kg + 4 * e), hi, lo);
-        *(u32x2*)(lds8 + off) = hi;
-        *(u32x2*)(lds8 + PL + off) = lo;
-        split4(*(const f32x4*)(vg + 4 * e), hi, lo);
-        *(u32x2*)(lds8 + 2 * PL + off) = hi;
-        *(u32x2*)(lds8 + 3 * PL + off) = lo;
-    }
+    stage_kv<K, 64 * kAttWaves>(lds8, kg, vg, tid);
     __syncthreads();   // the only barrier
     const int L = clamp_len(a.lengths, bh / a.H, a.n);
     const size_t head = (size_t)bh * a.n * 64;
     const float c = a.scale * 1.4426950408889634f;   // scores to base-2 exponents
     const int nblk = (a.n + kAttRows - 1) / kAttRows;
     const int blk0 = blockIdx.x * a.qb, blk1 = min(nblk, blk0 + a.qb);
+    // Q and dO rows past the length read as zeros (their dQ rows come out zero)
+    const __amdgpu_buffer_rsrc_t rsq = row_rsrc((const TQ*)a.Q + head, L);
+    const __amdgpu_buffer_rsrc_t rsg = row_rsrc((const TQ*)a.dO + head, L);
     RowOps<TQ> qr, gr;
     auto load_rows = [&](int q) {
-        qr.load((const TQ*)a.Q + head + (size_t)q * 64, g);
-        if (q < L) gr.load((const TQ*)a.dO + head + (size_t)q * 64, g);
-        else gr.zero();
+        qr.load(rsq, q, g);
+        gr.load(rsg, q, g);
     };
     // per-lane LDS offsets of the transposed Kbar^T reads: source lane s = l of group g reads
     // columns 16 cb + 4 (l % 4) of rows 32 j + 4 g + l / 4 (+ 16)
@@ -437,14 +432,11 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
             }
         dsum += __shfl_xor(dsum, 16);
         dsum += __shfl_xor(dsum, 32);
-        float* prow = a.P + ((size_t)bh * a.n + q) * K + 4 * g;
-        float* drow = a.dS + ((size_t)bh * a.n + q) * K + 4 * g;
+        // the query's statistics, from which bw_kv_kernel recomputes P and dS
+        if (g == 0)
+            *(f32x4*)(a.stats + ((size_t)bh * a.n + q) * 4) = f32x4{mc, inv, dsum, 0.0f};
 #pragma unroll
-        for (int r = 0; r < KB; ++r) {
-            dp[r] = st[r] * (dp[r] - dsum);   // dS
-            *(f32x4*)(prow + 16 * r) = st[r];
-            *(f32x4*)(drow + 16 * r) = dp[r];
-        }
+        for (int r = 0; r < KB; ++r) dp[r] = st[r] * (dp[r] - dsum);   // dS
         // next block's rows into the same registers; they arrive during the dQ products
         loaded = false;
         if (blk + 1 < blk1 && q0 + kAttRows < min(a.n, L)) {
@@ -476,6 +468,191 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
             *(f32x4*)(a.dQ + head + (size_t)q * 64 + 16 * cb + 4 * g) = dq[cb] * a.scale;
+    }
+}
+
+// ---- dVbar = P^T dO and dKbar = scale dS^T Q per (b, h) and block of 128 slots, P and dS
+// recomputed from the fused kernel's per-query statistics (the reductions over the queries of
+// FlashAttention-2's backward, with the projected slots in the role of its keys).  Wave w owns the
+// 16 slots s0 = 128 blockIdx.x + 16 w: their Kbar and Vbar rows sit in registers as hi and lo
+// bf16 operands.  The workgroup streams the queries before the length through LDS in chunks of 32
+// (Q and dO as hi, and for fp32 inputs lo, planes [32][64] with the 16-byte chunk swizzle of
+// split_bf16.h, and the chunk's statistics), double-buffered: the next chunk is loaded into
+// registers while the current one is multiplied.  Per chunk and wave, with lane (g, l) holding
+// C[4 g + e][l] of a 16 x 16 block:
+//   S = Q Kbar^T, dP = dO Vbar^T   (32 queries x 16 slots: query rows as A operands from LDS,
+//                                   the slots' rows as B operands from registers)
+//   P = exp2(c s - c m) / sum, dS = P o (dP - D)   (queries at or past the length: 0)
+//   dVbar^T += dO^T P, dKbar^T += Q^T dS   (64 x 16: per 32 queries the B operand is the lane's
+//        P / dS of queries 4 g + e and 16 + 4 g + e straight from the accumulators, split into hi
+//        and lo, and the A operand dO^T / Q^T is read at exactly those queries with the
+//        transposing ds_read_b64_tr_b16)
+// and at the end each wave writes its 16 slots' rows of dKbar (times scale) and dVbar.
+template <typename TQ>
+__global__ __launch_bounds__(512) void bw_kv_kernel(BwKvArgs a) {
+    constexpr bool QLO = sizeof(TQ) == 4;
+    constexpr int CQ = 32;                  // queries per chunk
+    constexpr int PLB = CQ * 128;           // bytes of one [32][64] bf16 plane
+    constexpr int NPL = QLO ? 4 : 2;        // planes per chunk: Q hi (lo), dO hi (lo)
+    constexpr int BUF = NPL * PLB + CQ * 16; // planes, then the statistics
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, l = lane & 15;
+    const int bh = blockIdx.y;
+    const int s0 = 128 * blockIdx.x + 16 * wave;
+    const bool active = s0 < a.k;
+    const int L = clamp_len(a.lengths, bh / a.H, a.n);
+    const size_t head = (size_t)bh * a.n * 64;
+    const float c = a.scale * kLog2e;
+    // this wave's slots' rows as B operands: lane (g, l) holds row s0 + l, columns 32 kc + 8 g ..
+    bf16x8 kbh[2], kbl[2], vbh[2], vbl[2];
+    if (active) {
+        const float* kr = a.Kb + ((size_t)bh * a.k + s0 + l) * 64;
+        const float* vr = a.Vb + ((size_t)bh * a.k + s0 + l) * 64;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            u32x2 h0, l0, h1, l1;
+            split4(*(const f32x4*)(kr + 32 * kc + 8 * g), h0, l0);
+            split4(*(const f32x4*)(kr + 32 * kc + 8 * g + 4), h1, l1);
+            kbh[kc] = pair8(h0, h1);
+            kbl[kc] = pair8(l0, l1);
+            split4(*(const f32x4*)(vr + 32 * kc + 8 * g), h0, l0);
+            split4(*(const f32x4*)(vr + 32 * kc + 8 * g + 4), h1, l1);
+            vbh[kc] = pair8(h0, h1);
+            vbl[kc] = pair8(l0, l1);
+        }
+    }
+    // chunk loads: thread t takes 8 bytes of Q and of dO (bf16: 4 values; fp32: 16 bytes, split)
+    // at row t / 16, columns 4 (t % 16) .. + 3, and thread t < 32 the statistics of query t.
+    // Buffer descriptors sized to the rows before the length return zeros past it, so the loads
+    // need no branches (and none waits for another).
+    const uint32_t rows = (uint32_t)L * 64 * sizeof(TQ);
+    const __amdgpu_buffer_rsrc_t rsq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((const TQ*)a.Q + head), 0, rows, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsg =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((const TQ*)a.dO + head), 0, rows, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.stats + (size_t)bh * a.n * 4), 0, (uint32_t)L * 16, 0x00020000);
+    const int lr = tid >> 4, lc = 4 * (tid & 15);
+    u32x4 rq, rg;
+    f32x4 rs;
+    auto load_chunk = [&](int q0) {
+        const uint32_t off = (uint32_t)((q0 + lr) * 64 + lc) * sizeof(TQ);
+        if constexpr (QLO) {
+            rq = __builtin_amdgcn_raw_buffer_load_b128(rsq, off, 0, 0);
+            rg = __builtin_amdgcn_raw_buffer_load_b128(rsg, off, 0, 0);
+        } else {
+            const u32x2 zq = __builtin_amdgcn_raw_buffer_load_b64(rsq, off, 0, 0);
+            const u32x2 zg = __builtin_amdgcn_raw_buffer_load_b64(rsg, off, 0, 0);
+            rq = u32x4{zq[0], zq[1], 0u, 0u};
+            rg = u32x4{zg[0], zg[1], 0u, 0u};
+        }
+        rs = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rss, (uint32_t)(q0 + (tid & (CQ - 1))) * 16, 0, 0));
+    };
+    auto store_chunk = [&](uint8_t* buf) {
+        const int off = kv_off(lr, lc);
+        if constexpr (QLO) {
+            u32x2 h, o;
+            split4(__builtin_bit_cast(f32x4, rq), h, o);
+            *(u32x2*)(buf + off) = h;
+            *(u32x2*)(buf + PLB + off) = o;
+            split4(__builtin_bit_cast(f32x4, rg), h, o);
+            *(u32x2*)(buf + 2 * PLB + off) = h;
+            *(u32x2*)(buf + 3 * PLB + off) = o;
+        } else {
+            *(u32x2*)(buf + off) = u32x2{rq[0], rq[1]};
+            *(u32x2*)(buf + PLB + off) = u32x2{rg[0], rg[1]};
+        }
+        if (tid < CQ) *(f32x4*)(buf + NPL * PLB + tid * 16) = rs;
+    };
+    const int tr_row = 4 * g + (l >> 2), tr_col = 4 * (l & 3);
+    f32x4 dk[4] = {}, dv[4] = {};
+    const int nchunk = (L + CQ - 1) / CQ;
+    if (nchunk > 0) {
+        load_chunk(0);
+        store_chunk(lds);
+    }
+    __syncthreads();
+    for (int ch = 0; ch < nchunk; ++ch) {
+        uint8_t* buf = lds + (ch & 1) * BUF;
+        if (ch + 1 < nchunk) load_chunk((ch + 1) * CQ);
+        if (active) {
+            const uint8_t* qh = buf;
+            const uint8_t* ql = buf + PLB;
+            const uint8_t* gh = buf + (QLO ? 2 : 1) * PLB;
+            const uint8_t* gl = buf + 3 * PLB;
+            const float* st = (const float*)(buf + NPL * PLB);
+            f32x4 sc[2], dp[2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                sc[qb] = f32x4{};
+                dp[qb] = f32x4{};
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    const int off = kv_off(16 * qb + l, 32 * kc + 8 * g);
+                    const bf16x8 aq = lds16(qh, off), ag = lds16(gh, off);
+                    sc[qb] = mfma16(aq, kbl[kc], sc[qb]);
+                    dp[qb] = mfma16(ag, vbl[kc], dp[qb]);
+                    if constexpr (QLO) {
+                        sc[qb] = mfma16(lds16(ql, off), kbh[kc], sc[qb]);
+                        dp[qb] = mfma16(lds16(gl, off), vbh[kc], dp[qb]);
+                    }
+                    sc[qb] = mfma16(aq, kbh[kc], sc[qb]);
+                    dp[qb] = mfma16(ag, vbh[kc], dp[qb]);
+                }
+                // P and dS of queries 16 qb + 4 g + e (zero at or past the length)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int qi = 16 * qb + 4 * g + e;
+                    const f32x4 sq = *(const f32x4*)(st + 4 * qi);
+                    const bool in = ch * CQ + qi < L;
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(sc[qb][e], c, -sq[0])) * sq[1];
+                    const float P = in ? pv : 0.0f;
+                    sc[qb][e] = P;
+                    dp[qb][e] = in ? P * (dp[qb][e] - sq[2]) : 0.0f;
+                }
+            }
+            u32x2 ph0, pl0, ph1, pl1, dh0, dl0, dh1, dl1;
+            split4(sc[0], ph0, pl0);
+            split4(sc[1], ph1, pl1);
+            split4(dp[0], dh0, dl0);
+            split4(dp[1], dh1, dl1);
+            const bf16x8 bph = pair8(ph0, ph1), bpl = pair8(pl0, pl1);
+            const bf16x8 bdh = pair8(dh0, dh1), bdl = pair8(dl0, dl1);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const int o0 = kv_off(tr_row, 16 * cb + tr_col);
+                const int o1 = kv_off(16 + tr_row, 16 * cb + tr_col);
+                const bf16x8 agh = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lds_tr(gh, o0), lds_tr(gh, o1), 0, 1, 2, 3, 4, 5, 6, 7));
+                const bf16x8 aqh = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lds_tr(qh, o0), lds_tr(qh, o1), 0, 1, 2, 3, 4, 5, 6, 7));
+                dv[cb] = mfma16(agh, bpl, dv[cb]);
+                dk[cb] = mfma16(aqh, bdl, dk[cb]);
+                if constexpr (QLO) {
+                    const bf16x8 agl = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(lds_tr(gl, o0), lds_tr(gl, o1), 0, 1, 2, 3, 4, 5, 6, 7));
+                    const bf16x8 aql = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(lds_tr(ql, o0), lds_tr(ql, o1), 0, 1, 2, 3, 4, 5, 6, 7));
+                    dv[cb] = mfma16(agl, bph, dv[cb]);
+                    dk[cb] = mfma16(aql, bdh, dk[cb]);
+                }
+                dv[cb] = mfma16(agh, bph, dv[cb]);
+                dk[cb] = mfma16(aqh, bdh, dk[cb]);
+            }
+        }
+        if (ch + 1 < nchunk) store_chunk(lds + ((ch + 1) & 1) * BUF);
+        __syncthreads();
+    }
+    if (!active) return;
+    // dv[cb] element e of lane (g, l): dVbar[s0 + l][16 cb + 4 g + e]
+    float* dkr = a.dKb + ((size_t)bh * a.k + s0 + l) * 64;
+    float* dvr = a.dVb + ((size_t)bh * a.k + s0 + l) * 64;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        *(f32x4*)(dkr + 16 * cb + 4 * g) = dk[cb] * a.scale;
+        *(f32x4*)(dvr + 16 * cb + 4 * g) = dv[cb];
     }
 }
 
@@ -583,6 +760,14 @@ static hipError_t launch_attend_t(const BwAttendArgs& a, hipStream_t stream) {
         case 8: return launch_attend_kb<16, TQ>(a, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_bw_kv(const BwKvArgs& a, hipStream_t stream) {
+    if (a.k % 32 || a.k > 256 || a.B * a.H > 65535) return hipErrorInvalidValue;
+    const dim3 grid((a.k + 127) / 128, a.B * a.H);
+    if (a.in_bf16) hipLaunchKernelGGL(bw_kv_kernel<uint16_t>, grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL(bw_kv_kernel<float>, grid, dim3(512), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_bw_attend(const BwAttendArgs& a, hipStream_t stream) {

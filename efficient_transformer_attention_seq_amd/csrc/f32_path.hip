@@ -41,20 +41,11 @@ __global__ __launch_bounds__(64 * kAttWaves) void attend_f32_kernel(F32Args a, i
     const int bh = blockIdx.y;
     const float* kg = a.Kbar + (size_t)bh * K * 64;
     const float* vg = a.Vbar + (size_t)bh * K * 64;
-    for (int e = tid; e < K * 16; e += 64 * kAttWaves) {   // 4 values (16 bytes) each
-        const int r = e >> 4, d = 4 * (e & 15);
-        const int off = kv_off(r, d);
-        u32x2 hi, lo;
-        split4(*(const f32x4*)(kg + 4 * e), hi, lo);
-        *(u32x2*)(lds8 + off) = hi;
-        *(u32x2*)(lds8 + PL + off) = lo;
-        split4(*(const f32x4*)(vg + 4 * e), hi, lo);
-        *(u32x2*)(lds8 + 2 * PL + off) = hi;
-        *(u32x2*)(lds8 + 3 * PL + off) = lo;
-    }
+    stage_kv<K, 64 * kAttWaves>(lds8, kg, vg, tid);
     __syncthreads();   // the only barrier
     const int L = clamp_len(a.lengths, bh / a.H, a.n);
     const size_t head = (size_t)bh * a.n * 64;
+    const __amdgpu_buffer_rsrc_t rsq = row_rsrc(a.Q + head, L);   // rows past the length: zeros
     const float c = a.scale * kLog2e;   // scores to base-2 exponents
     const int nblk = (a.n + kAttRows - 1) / kAttRows;
     const int blk0 = blockIdx.x * qb, blk1 = min(nblk, blk0 + qb);
@@ -73,7 +64,7 @@ __global__ __launch_bounds__(64 * kAttWaves) void attend_f32_kernel(F32Args a, i
                 *(f32x4*)(a.O + head + (size_t)q * 64 + 16 * cb + 4 * g) = f32x4{};
             continue;
         }
-        if (!loaded) qr.load(a.Q + head + (size_t)q * 64, g);
+        if (!loaded) qr.load(rsq, q, g);
         f32x4 st[KB];
 #pragma unroll
         for (int r = 0; r < KB; ++r) st[r] = f32x4{};
@@ -93,7 +84,7 @@ __global__ __launch_bounds__(64 * kAttWaves) void attend_f32_kernel(F32Args a, i
         // next block's Q slices into the same registers; they arrive during the products below
         loaded = false;
         if (blk + 1 < blk1 && q0 + kAttRows < min(a.n, L)) {
-            qr.load(a.Q + head + (size_t)(q + kAttRows) * 64, g);
+            qr.load(rsq, q + kAttRows, g);
             loaded = true;
         }
         float mx = st[0][0];

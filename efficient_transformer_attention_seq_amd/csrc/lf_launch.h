@@ -60,6 +60,10 @@ struct ProjBf16Args {
     uint8_t* Klo;           // [B, H, k, 64]
     uint8_t* Ksc;           // [B, H, k, 2]
     uint16_t* Vb;           // [B, H, k, 64]
+    // fp32 outputs instead (the backward pass): when Kf is set, Kbar and Vbar are stored unscaled
+    // in fp32 at Kf and Vf ([B, H, k, 64] each) and Khi, Klo, Ksc, Vb and c are not used
+    float* Kf;
+    float* Vf;
     float* part;            // [S, 2, B*H, k, 64] when S > 1 (paired: per tile, see below)
     float c;                // scale * log2(e), applied to Kbar before it is stored
     ProjGeom g;
@@ -158,14 +162,32 @@ struct BwAttendArgs {
     const float* Kb;   // [B, H, k, 64]
     const float* Vb;
     const int32_t* lengths;   // optional per-item lengths
-    float* P;          // [B, H, n, k]; rows of 16-query groups wholly past the length unwritten
-    float* dS;         // [B, H, n, k]
+    float* stats;      // [B, H, n, 4]: per query (c m, 1 / sum, D, 0) with P = exp2(c s - c m) / sum
+                       // (c = scale log2 e) and D = rowsum(P o dP); rows of 16-query groups wholly
+                       // past the length unwritten
     float* dQ;         // [B, H, n, 64]
     int B, H, n, k;
     int qb;            // 128-query blocks per workgroup
     int in_bf16;
     float scale;
 };
+
+// dVbar = P^T dO and dKbar = scale dS^T Q (backward_f32.hip, bw_kv_kernel), P and dS recomputed
+// from Q, dO, Kbar, Vbar and the fused kernel's per-query statistics
+struct BwKvArgs {
+    const void* Q;     // as BwAttendArgs
+    const void* dO;
+    const float* Kb;
+    const float* Vb;
+    const float* stats;
+    const int32_t* lengths;
+    float* dKb;        // [B, H, k, 64]
+    float* dVb;
+    int B, H, n, k;
+    int in_bf16;
+    float scale;
+};
+hipError_t launch_bw_kv(const BwKvArgs& a, hipStream_t stream);
 
 // Dense projection Y = X . W^T of the encoder attention stack (linear_bf16.hip).
 struct LinearBf16Args {

@@ -24,6 +24,7 @@
 // bitwise reproducible) and casts.  With S == 1 the cast happens here.
 // Output: Kbar scaled by c = scale * log2(e) and stored as a bf16 plane plus an fp8 residual plane
 // with per-block power-of-two scales (format in lf_launch.h); Vbar -> bf16, round to nearest even.
+// The backward pass takes both unscaled in fp32 instead (Kf, Vf).
 // Unsplit Kbar / Vbar outputs are written with streaming (non-temporal) stores (RoBERTa-shaped
 // forward 59.8 -> 57.9 us on two boxes, -0.3 us on a third); split partials and the stack's E.X output use ordinary stores
 // (streaming measured flat for the former and 1.5% slower for the stack).
@@ -430,6 +431,7 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
     uint8_t* stg_lo = stg + RW * kRowH;
     const size_t bhk = (size_t)g.B * g.H * g.k;
     const float c = a.c;
+    const bool f32_out = a.Kf != nullptr;
 #pragma unroll
     for (int wn = 0; wn < WN; ++wn) {
         const int j = j0 + ug * WN + wn;
@@ -442,7 +444,7 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
             const int row = mt * 32 + l32;
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                if (split_out) {
+                if (split_out || f32_out) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int col = ct * 32 + q * 8 + 4 * hh;
@@ -490,8 +492,9 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
         __builtin_amdgcn_wave_barrier();
         if (live) {
             const size_t ubase = urow * kHeadDim;
-            if (split_out) {
-                float* dst = a.part + ((size_t)s * 2 + un.which) * bhk * kHeadDim + ubase;
+            if (split_out || f32_out) {
+                float* dst = split_out ? a.part + ((size_t)s * 2 + un.which) * bhk * kHeadDim + ubase
+                                       : (un.which == 0 ? a.Kf : a.Vf) + ubase;
                 // RW rows x 256 B: 16 lanes per row
 #pragma unroll
                 for (int it = 0; it < RW / 4; ++it) {
@@ -527,7 +530,7 @@ __global__ __launch_bounds__(C::NW * 64) void proj_bf16_kernel(ProjBf16Args a) {
 }
 
 // Adds the S fp32 partial sums of every Kbar/Vbar element and stores them in the bf16 formats
-// (Kbar: hi plane, fp8 lo plane and block scales, see lf_launch.h).  NG = 1: a thread adds all S
+// (Kbar: hi plane, fp8 lo plane and block scales, see lf_launch.h) or, given Kf, in fp32.  NG = 1: a thread adds all S
 // splits of 4 consecutive columns in split order (loads issued 4 ahead).  NG = 4 (many splits): a
 // block covers 64 such chunks and its 4 waves each add a contiguous quarter of the splits in
 // order, then wave 0 adds the quarter sums in order.  Either way the summation order is fixed,
@@ -537,7 +540,8 @@ template <int NG>
 __global__ __launch_bounds__(256) void proj_fixup_bf16_kernel(const float* part, int S,
                                                               size_t half, size_t e0, float c,
                                                               uint16_t* Khi, uint8_t* Klo,
-                                                              uint8_t* Ksc, uint16_t* Vb) {
+                                                              uint8_t* Ksc, uint16_t* Vb,
+                                                              float* Kf, float* Vf) {
     constexpr int CH = 256 / NG;   // four-column chunks per block
     __shared__ f32x4 quarter[NG > 1 ? NG : 1][CH];
     const int ci = threadIdx.x % CH, grp = threadIdx.x / CH;
@@ -568,7 +572,9 @@ __global__ __launch_bounds__(256) void proj_fixup_bf16_kernel(const float* part,
         for (int q = 1; q < NG; ++q) acc += quarter[q][ci];
     }
     if (!live) return;
-    if (e4 < half) {
+    if (Kf) {   // fp32 outputs
+        *(f32x4*)(e4 < half ? Kf + e4 : Vf + (e4 - half)) = acc;
+    } else if (e4 < half) {
         float r0, r1, r2, r3;
         const u32x2 hi = {hi_pair(c * acc[0], c * acc[1], r0, r1), hi_pair(c * acc[2], c * acc[3], r2, r3)};
         float m = fmaxf(fmaxf(fabsf(r0), fabsf(r1)), fmaxf(fabsf(r2), fabsf(r3)));
@@ -740,10 +746,10 @@ hipError_t launch_proj_bf16(const ProjBf16Args& a, hipStream_t stream) {
     const size_t chunks = (2 * half - e0) / 4;
     if (g.S >= 8) {   // many splits: spread each chunk's reduction over 4 waves
         hipLaunchKernelGGL(proj_fixup_bf16_kernel<4>, dim3((int)((chunks + 63) / 64)), dim3(256), 0,
-                           stream, a.part, g.S, half, e0, a.c, a.Khi, a.Klo, a.Ksc, a.Vb);
+                           stream, a.part, g.S, half, e0, a.c, a.Khi, a.Klo, a.Ksc, a.Vb, a.Kf, a.Vf);
     } else {
         hipLaunchKernelGGL(proj_fixup_bf16_kernel<1>, dim3((int)((chunks + 255) / 256)), dim3(256), 0,
-                           stream, a.part, g.S, half, e0, a.c, a.Khi, a.Klo, a.Ksc, a.Vb);
+                           stream, a.part, g.S, half, e0, a.c, a.Khi, a.Klo, a.Ksc, a.Vb, a.Kf, a.Vf);
     }
     return hipGetLastError();
 }

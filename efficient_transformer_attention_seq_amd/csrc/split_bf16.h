@@ -49,23 +49,53 @@ __device__ __forceinline__ s16x4 lds_tr(const uint8_t* base, int off) {
             (__attribute__((address_space(3))) const uint8_t*)(base + off)));
 }
 
-// The query row's slices d = 32 kc + 8 g .. + 7 (kc = 0, 1) of Q or dO, as loaded (zero at or
-// past the length: raw zeros), and as bf16 operands hi (and lo for fp32 inputs)
+// Kbar and Vbar ([K][64] fp32 each, at kg and vg) into LDS as hi and lo bf16 planes at lds,
+// lds + K 128, lds + 2 K 128, lds + 3 K 128 (bytes), by NT threads: every thread's loads are
+// issued before the first is split, so the staging costs one load latency, not one per step
+template <int K, int NT>
+__device__ __forceinline__ void stage_kv(uint8_t* lds, const float* kg, const float* vg, int tid) {
+    constexpr int PL = K * 128, NIT = K * 16 / NT;
+    static_assert(K * 16 % NT == 0, "whole steps");
+    f32x4 kx[NIT], vx[NIT];
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {   // 4 values (16 bytes) each
+        kx[i] = *(const f32x4*)(kg + 4 * (tid + i * NT));
+        vx[i] = *(const f32x4*)(vg + 4 * (tid + i * NT));
+    }
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+        const int e = tid + i * NT, r = e >> 4, d = 4 * (e & 15);
+        const int off = kv_off(r, d);
+        u32x2 hi, lo;
+        split4(kx[i], hi, lo);
+        *(u32x2*)(lds + off) = hi;
+        *(u32x2*)(lds + PL + off) = lo;
+        split4(vx[i], hi, lo);
+        *(u32x2*)(lds + 2 * PL + off) = hi;
+        *(u32x2*)(lds + 3 * PL + off) = lo;
+    }
+}
+
+// Buffer descriptor over `rows` rows of 64 values of TQ from `base`: loads at or past them return
+// zeros, so rows past a length need no branch around their loads.
+template <typename TQ>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const TQ* base, int rows) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (uint32_t)rows * 64 * sizeof(TQ),
+                                             0x00020000);
+}
+
+// The query row's slices d = 32 kc + 8 g .. + 7 (kc = 0, 1) of Q or dO, as loaded (rows past the
+// descriptor's end: zeros), and as bf16 operands hi (and lo for fp32 inputs)
 template <typename TQ>
 struct RowOps {
     u32x4 raw[2][sizeof(TQ) / 2];   // 16 bytes (bf16) or 32 bytes (fp32) per slice
-    __device__ void load(const TQ* row, int g) {
+    __device__ void load(__amdgpu_buffer_rsrc_t rs, int row, int g) {
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-            for (int w = 0; w < (int)(sizeof(TQ) / 2); ++w)
-                raw[kc][w] = *(const u32x4*)(row + 32 * kc + 8 * g + 4 * w);   // w > 0: fp32 only
-    }
-    __device__ void zero() {
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int w = 0; w < (int)(sizeof(TQ) / 2); ++w) raw[kc][w] = u32x4{0u, 0u, 0u, 0u};
+            for (int w = 0; w < (int)(sizeof(TQ) / 2); ++w)   // w > 0: fp32 only
+                raw[kc][w] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, (uint32_t)(row * 64 + 32 * kc + 8 * g) * sizeof(TQ) + 16 * w, 0, 0);
     }
     __device__ void ops(int kc, bf16x8& hi, bf16x8& lo) const {
         if constexpr (sizeof(TQ) == 2) {
