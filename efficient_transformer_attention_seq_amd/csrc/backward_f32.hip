@@ -534,49 +534,60 @@ __global__ __launch_bounds__(512) void bw_kv_kernel(BwKvArgs a) {
     const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.stats + (size_t)bh * a.n * 4), 0, (uint32_t)L * 16, 0x00020000);
     const int lr = tid >> 4, lc = 4 * (tid & 15);
-    u32x4 rq, rg;
-    f32x4 rs;
-    auto load_chunk = [&](int q0) {
+    // two register sets: chunk ch + 2 is loaded into set ch % 2 while chunk ch is multiplied and
+    // chunk ch + 1 (set (ch + 1) % 2) waits to be stored, so each load has two chunks' time to land
+    u32x4 rq[2], rg[2];
+    f32x4 rs[2];
+    auto load_chunk = [&](auto set, int q0) {
+        constexpr int S = decltype(set)::value;
         const uint32_t off = (uint32_t)((q0 + lr) * 64 + lc) * sizeof(TQ);
         if constexpr (QLO) {
-            rq = __builtin_amdgcn_raw_buffer_load_b128(rsq, off, 0, 0);
-            rg = __builtin_amdgcn_raw_buffer_load_b128(rsg, off, 0, 0);
+            rq[S] = __builtin_amdgcn_raw_buffer_load_b128(rsq, off, 0, 0);
+            rg[S] = __builtin_amdgcn_raw_buffer_load_b128(rsg, off, 0, 0);
         } else {
             const u32x2 zq = __builtin_amdgcn_raw_buffer_load_b64(rsq, off, 0, 0);
             const u32x2 zg = __builtin_amdgcn_raw_buffer_load_b64(rsg, off, 0, 0);
-            rq = u32x4{zq[0], zq[1], 0u, 0u};
-            rg = u32x4{zg[0], zg[1], 0u, 0u};
+            rq[S] = u32x4{zq[0], zq[1], 0u, 0u};
+            rg[S] = u32x4{zg[0], zg[1], 0u, 0u};
         }
-        rs = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rss, (uint32_t)(q0 + (tid & (CQ - 1))) * 16, 0, 0));
+        rs[S] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rss, (uint32_t)(q0 + (tid & (CQ - 1))) * 16, 0, 0));
     };
-    auto store_chunk = [&](uint8_t* buf) {
+    auto store_chunk = [&](auto set) {
+        constexpr int S = decltype(set)::value;
+        uint8_t* buf = lds + S * BUF;
         const int off = kv_off(lr, lc);
         if constexpr (QLO) {
             u32x2 h, o;
-            split4(__builtin_bit_cast(f32x4, rq), h, o);
+            split4(__builtin_bit_cast(f32x4, rq[S]), h, o);
             *(u32x2*)(buf + off) = h;
             *(u32x2*)(buf + PLB + off) = o;
-            split4(__builtin_bit_cast(f32x4, rg), h, o);
+            split4(__builtin_bit_cast(f32x4, rg[S]), h, o);
             *(u32x2*)(buf + 2 * PLB + off) = h;
             *(u32x2*)(buf + 3 * PLB + off) = o;
         } else {
-            *(u32x2*)(buf + off) = u32x2{rq[0], rq[1]};
-            *(u32x2*)(buf + PLB + off) = u32x2{rg[0], rg[1]};
+            *(u32x2*)(buf + off) = u32x2{rq[S][0], rq[S][1]};
+            *(u32x2*)(buf + PLB + off) = u32x2{rg[S][0], rg[S][1]};
         }
-        if (tid < CQ) *(f32x4*)(buf + NPL * PLB + tid * 16) = rs;
+        if (tid < CQ) *(f32x4*)(buf + NPL * PLB + tid * 16) = rs[S];
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
     const int tr_row = 4 * g + (l >> 2), tr_col = 4 * (l & 3);
     f32x4 dk[4] = {}, dv[4] = {};
     const int nchunk = (L + CQ - 1) / CQ;
     if (nchunk > 0) {
-        load_chunk(0);
-        store_chunk(lds);
+        load_chunk(I0{}, 0);
+        if (nchunk > 1) load_chunk(I1{}, CQ);
+        store_chunk(I0{});
     }
     __syncthreads();
-    for (int ch = 0; ch < nchunk; ++ch) {
-        uint8_t* buf = lds + (ch & 1) * BUF;
-        if (ch + 1 < nchunk) load_chunk((ch + 1) * CQ);
+    // one chunk; the buffer parity is a compile-time constant, so every LDS read is a per-lane
+    // offset (the same for both buffers) plus an immediate
+    auto chunk = [&](auto parity, int ch) {
+        constexpr int PAR = decltype(parity)::value;
+        const uint8_t* buf = lds + PAR * BUF;
+        if (ch + 2 < nchunk) load_chunk(parity, (ch + 2) * CQ);
         if (active) {
             const uint8_t* qh = buf;
             const uint8_t* ql = buf + PLB;
@@ -601,16 +612,14 @@ __global__ __launch_bounds__(512) void bw_kv_kernel(BwKvArgs a) {
                     sc[qb] = mfma16(aq, kbh[kc], sc[qb]);
                     dp[qb] = mfma16(ag, vbh[kc], dp[qb]);
                 }
-                // P and dS of queries 16 qb + 4 g + e (zero at or past the length)
+                // P and dS of queries 16 qb + 4 g + e.  Past the length Q, dO and the statistics
+                // all read as zero, so P = exp2(0) * 0 and dS = 0 there without a test.
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int qi = 16 * qb + 4 * g + e;
-                    const f32x4 sq = *(const f32x4*)(st + 4 * qi);
-                    const bool in = ch * CQ + qi < L;
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(sc[qb][e], c, -sq[0])) * sq[1];
-                    const float P = in ? pv : 0.0f;
+                    const f32x4 sq = *(const f32x4*)(st + 4 * (16 * qb + 4 * g + e));
+                    const float P = __builtin_amdgcn_exp2f(fmaf(sc[qb][e], c, -sq[0])) * sq[1];
                     sc[qb][e] = P;
-                    dp[qb][e] = in ? P * (dp[qb][e] - sq[2]) : 0.0f;
+                    dp[qb][e] = P * (dp[qb][e] - sq[2]);
                 }
             }
             u32x2 ph0, pl0, ph1, pl1, dh0, dl0, dh1, dl1;
@@ -642,8 +651,12 @@ __global__ __launch_bounds__(512) void bw_kv_kernel(BwKvArgs a) {
                 dk[cb] = mfma16(aqh, bdh, dk[cb]);
             }
         }
-        if (ch + 1 < nchunk) store_chunk(lds + ((ch + 1) & 1) * BUF);
+        if (ch + 1 < nchunk) store_chunk(std::integral_constant<int, 1 - PAR>{});
         __syncthreads();
+    };
+    for (int ch = 0; ch < nchunk; ch += 2) {
+        chunk(I0{}, ch);
+        if (ch + 1 < nchunk) chunk(I1{}, ch + 1);
     }
     if (!active) return;
     // dv[cb] element e of lane (g, l): dVbar[s0 + l][16 cb + 4 g + e]
