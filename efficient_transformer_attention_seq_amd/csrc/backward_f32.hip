@@ -286,8 +286,7 @@ __global__ __launch_bounds__(256) void bw_gemm_reduce_kernel(BwGemm g) {
     const size_t idx = ((size_t)blockIdx.x * 256 + threadIdx.x) * V;
     if (idx >= total) return;
     float s[V] = {};
-    for (int sp = 0; sp < g.splits; ++sp) {
-        const float* q = g.part + (size_t)sp * total + idx;
+    auto add = [&](const float* q) {
         if constexpr (V == 4) {
             const f32x4 w = *(const f32x4*)q;
 #pragma unroll
@@ -295,7 +294,28 @@ __global__ __launch_bounds__(256) void bw_gemm_reduce_kernel(BwGemm g) {
         } else {
             s[0] += *q;
         }
+    };
+    // eight splits' loads in flight at a time (the adds stay in split order)
+    int sp = 0;
+    for (; sp + 8 <= g.splits; sp += 8) {
+        float w[8][V];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float* q = g.part + (size_t)(sp + u) * total + idx;
+            if constexpr (V == 4) {
+                const f32x4 x = *(const f32x4*)q;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[u][e] = x[e];
+            } else {
+                w[u][0] = *q;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int e = 0; e < V; ++e) s[e] += w[u][e];
     }
+    for (; sp < g.splits; ++sp) add(g.part + (size_t)sp * total + idx);
     const int z = (int)(idx / mn);
     const int i = (int)((idx % mn) / g.N), j = (int)(idx % g.N);
     const bool hi2 = g.zhalf > 0 && z >= g.zhalf;
