@@ -367,8 +367,6 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
     const int bh = blockIdx.y;
     const float* kg = a.Kb + (size_t)bh * K * 64;
     const float* vg = a.Vb + (size_t)bh * K * 64;
-    stage_kv<K, 64 * kAttWaves>(lds8, kg, vg, tid);
-    __syncthreads();   // the only barrier
     const int L = clamp_len(a.lengths, bh / a.H, a.n);
     const size_t head = (size_t)bh * a.n * 64;
     const float c = a.scale * 1.4426950408889634f;   // scores to base-2 exponents
@@ -385,7 +383,37 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
     // per-lane LDS offsets of the transposed Kbar^T reads: source lane s = l of group g reads
     // columns 16 cb + 4 (l % 4) of rows 32 j + 4 g + l / 4 (+ 16)
     const int tr_row = 4 * g + (l >> 2), tr_col = 4 * (l & 3);
+    // the first block's rows are in flight while Kbar and Vbar are staged
     bool loaded = false;
+    if (blk0 < blk1 && blk0 * kAttRows + wave * 16 < min(a.n, L)) {
+        load_rows(blk0 * kAttRows + wave * 16 + l);
+        loaded = true;
+    }
+    stage_kv<K, 64 * kAttWaves>(lds8, kg, vg, tid);
+    __syncthreads();   // the only barrier
+    // per-lane LDS bases.  Row reads of rows 16 r + l: the chunk swizzle repeats every 4 blocks
+    // (it sees (2 r) mod 8), so block r reads base[kc][r % 4] + (r / 4) 8192 (+ PL for the lo
+    // plane), the Vbar planes from their own bases.  Transposed reads of rows 32 j (+ 16) + tr_row:
+    // the swizzle repeats every 2 blocks, so tb[j % 2][half][cb] + (j / 2) 8192.
+    uint32_t kbase[2][4], vbase[2][4], tb[2][2][4];
+    {
+        const uint32_t l0 = lds_u32(lds8);
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                kbase[kc][rr] = opaque_u32(l0 + kv_off(16 * rr + l, 32 * kc + 8 * g));
+                vbase[kc][rr] = opaque_u32(l0 + 2 * PL + kv_off(16 * rr + l, 32 * kc + 8 * g));
+            }
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+                    tb[par][hf][cb] = opaque_u32(
+                        l0 + kv_off(32 * par + 16 * hf + 4 * g + (l >> 2), 16 * cb + 4 * (l & 3)));
+    }
     for (int blk = blk0; blk < blk1; ++blk) {
         const int q0 = blk * kAttRows + wave * 16;
         if (q0 >= a.n) break;
@@ -410,9 +438,9 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
             gr.ops(kc, gh, gl);
 #pragma unroll
             for (int r = 0; r < KB; ++r) {
-                const int off = kv_off(16 * r + l, 32 * kc + 8 * g);
-                const bf16x8 k0 = lds16(kh, off), k1 = lds16(kl, off);
-                const bf16x8 v0 = lds16(vh, off), v1 = lds16(vl, off);
+                const uint32_t ro = (r >> 2) * 8192;
+                const bf16x8 k0 = lds16a(kbase[kc][r & 3] + ro), k1 = lds16a(kbase[kc][r & 3] + PL + ro);
+                const bf16x8 v0 = lds16a(vbase[kc][r & 3] + ro), v1 = lds16a(vbase[kc][r & 3] + PL + ro);
                 st[r] = mfma16(k1, qh, st[r]);
                 dp[r] = mfma16(v1, gh, dp[r]);
                 if constexpr (QLO) {
@@ -473,12 +501,12 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
             const bf16x8 bhi = pair8(h0, h1), blo = pair8(l0, l1);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
-                const int o0 = kv_off(32 * j + tr_row, 16 * cb + tr_col);
-                const int o1 = kv_off(32 * j + 16 + tr_row, 16 * cb + tr_col);
+                const uint32_t a0 = tb[j & 1][0][cb] + (j >> 1) * 8192;
+                const uint32_t a1 = tb[j & 1][1][cb] + (j >> 1) * 8192;
                 const bf16x8 ah = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(lds_tr(kh, o0), lds_tr(kh, o1), 0, 1, 2, 3, 4, 5, 6, 7));
+                    bf16x8, __builtin_shufflevector(lds_tra(a0), lds_tra(a1), 0, 1, 2, 3, 4, 5, 6, 7));
                 const bf16x8 al = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(lds_tr(kl, o0), lds_tr(kl, o1), 0, 1, 2, 3, 4, 5, 6, 7));
+                    bf16x8, __builtin_shufflevector(lds_tra(a0 + PL), lds_tra(a1 + PL), 0, 1, 2, 3, 4, 5, 6, 7));
                 dq[cb] = mfma16(al, bhi, dq[cb]);
                 dq[cb] = mfma16(ah, blo, dq[cb]);
                 dq[cb] = mfma16(ah, bhi, dq[cb]);

@@ -49,6 +49,23 @@ __device__ __forceinline__ s16x4 lds_tr(const uint8_t* base, int off) {
             (__attribute__((address_space(3))) const uint8_t*)(base + off)));
 }
 
+// LDS loads at an absolute LDS byte address, and an address hidden from constant folding (so a
+// loop-invariant per-lane base stays in one register and the constant parts of the offsets go
+// into the instructions' offset fields)
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+__device__ __forceinline__ bf16x8 lds16a(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
+}
+__device__ __forceinline__ s16x4 lds_tra(uint32_t addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr);
+}
+
 // Kbar and Vbar ([K][64] fp32 each, at kg and vg) into LDS as hi and lo bf16 planes at lds,
 // lds + K 128, lds + 2 K 128, lds + 3 K 128 (bytes), by NT threads: every thread's loads are
 // issued before the first is split, so the staging costs one load latency, not one per step
