@@ -363,10 +363,9 @@ void bw_ws(const lf_problem* p, BwWs* w) {
     // split-reduction partial sums, the largest any of the backward's GEMMs asks for
     const int B = p->batch, H = p->heads, n = p->n, k = p->k;
     const bool unshared = p->share == LF_SHARE_NONE;
-    size_t part = lf::bw_gemm_part_bytes(k, 64, n, B * H);                         // Kbar, dXbar
-    part = std::max(part, lf::bw_gemm_part_bytes(k, n, unshared ? B * 64 : B * H * 64,
-                                                 unshared ? H : 1));                // dE, dF
-    part = std::max(part, lf::bw_gemm_part_bytes(n, 64, k, B * H));                // dK, dV
+    size_t part = lf::bw_gemm_part_bytes(k, n, unshared ? B * 64 : B * H * 64,
+                                         2 * (unshared ? H : 1));                   // dE (+ dF)
+    part = std::max(part, lf::bw_gemm_part_bytes(n, 64, k, 2 * B * H));            // dK and dV
     lf::ProjGeom g;
     if (geometry(p, &g)) part = std::max(part, part_bytes(p, g));                  // Kbar, Vbar
     w->part = take(part);
@@ -1010,7 +1009,8 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
     if (lf::launch_bw_kv(kv, strm) != hipSuccess) return LF_ERR_LAUNCH;
     // dE (+)= dXbar X^T: M = k, N = n, reduction over (b, c) (unshared: z = h) or over (b, h, c);
     // positions at or past item b's length read as zero
-    auto grad_mat = [&](const float* dXb, const void* X, float* out, float beta) {
+    // (dF given: dE and dF in one launch, batch entries z >= zhalf taking dVbar, V, dF)
+    auto grad_mat = [&](const float* dXb, const void* X, float* out, float beta, bool both) {
         lf::BwGemm g = gemm0();
         g.A = dXb; g.B = X; g.C = out; g.beta = beta; g.b_bf16 = bf;
         g.M = k; g.N = n; g.kblk = 64;
@@ -1028,24 +1028,33 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
         g.a_i = 64; g.a_kc = 1;
         g.b_kc = 1; g.b_j = 64;
         g.c_i = n; g.c_j = 1;
+        if (both) {
+            g.A2 = dVb; g.B2 = V; g.C2 = dF;
+            g.zhalf = g.Z;
+            g.Z *= 2;
+        }
         return run_gemm(g);
     };
-    e = grad_mat(dKb, K, dE, 0.0f);
-    if (e == hipSuccess) e = separate ? grad_mat(dVb, V, dF, 0.0f) : grad_mat(dVb, V, dE, 1.0f);
+    if (separate) {
+        e = grad_mat(dKb, K, dE, 0.0f, true);
+    } else {   // one matrix: dE = dKbar K^T + dVbar V^T
+        e = grad_mat(dKb, K, dE, 0.0f, false);
+        if (e == hipSuccess) e = grad_mat(dVb, V, dE, 1.0f, false);
+    }
     if (e != hipSuccess) return LF_ERR_LAUNCH;
-    // dK = E_h^T dKbar, dV = F_h^T dVbar: z = (b, h), M = n, N = 64, reduction over k
-    auto back = [&](const void* A, const float* dXb, float* out) {
+    // dK = E_h^T dKbar, dV = F_h^T dVbar in one launch: z = (b, h) for dK, then again for dV
+    // (batch entries z >= zhalf take F, dVbar, dV), M = n, N = 64, reduction over k
+    {
         lf::BwGemm g = gemm0();
-        g.A = A; g.B = dXb; g.C = out; g.a_bf16 = bf;
-        g.M = n; g.N = 64; g.K = k; g.Z = B * H; g.zdiv = H; g.kblk = k;
+        g.A = E; g.B = dKb; g.C = dK; g.a_bf16 = bf;
+        g.A2 = Fr; g.B2 = dVb; g.C2 = dV; g.zhalf = B * H;
+        g.M = n; g.N = 64; g.K = k; g.Z = 2 * B * H; g.zdiv = H; g.kblk = k;
         g.a_z2 = unshared ? kn : 0; g.a_i = 1; g.a_kc = n;
         g.b_z1 = H * hk64; g.b_z2 = hk64; g.b_kc = 64; g.b_j = 1;
         g.c_z1 = H * hn64; g.c_z2 = hn64; g.c_i = 64; g.c_j = 1;
         g.row_len = lengths;   // positions past the length get zero gradients
-        return run_gemm(g);
-    };
-    e = back(E, dKb, dK);
-    if (e == hipSuccess) e = back(Fr, dVb, dV);
+        e = run_gemm(g);
+    }
     return launch_status(e);
 }
 
