@@ -547,9 +547,10 @@ def run_backward(args, L, synth, torch, np):
     """linformer_backward on a workload's inputs with a random upstream gradient: gradients of Q,
     K, V, E, F (fp32 accumulation; every product on the bf16 matrix cores as split pairs).
     Algorithmic work per (b, h): 22 n k d flops, eleven products of 2 n k d (Kbar, Vbar
-    recomputed; scores, dP, dQ; dVbar, dKbar; dE, dF; dK, dV).  Executed matrix-core work: a
-    product takes 1 + (one per fp32 operand) bf16 products (hi.hi, lo.hi, hi.lo), the roofline's
-    basis against the bf16 peak."""
+    recomputed; scores, dP, dQ; dVbar, dKbar; dE, dF; dK, dV).  Executed matrix-core work: the
+    slot-block kernel computes the scores and dP a second time (so no n x k matrix is stored),
+    thirteen products in all, and a product takes 1 + (one per fp32 operand) bf16 products
+    (hi.hi, lo.hi, hi.lo), the roofline's basis against the bf16 peak."""
     wl = synth.WORKLOADS[args.workload]
     inp = synth.make_inputs(wl)
     td = torch.bfloat16 if wl.dtype == synth.DT_BF16 else torch.float32
@@ -584,13 +585,14 @@ def run_backward(args, L, synth, torch, np):
     ms = a.elapsed_time(b) / args.steps
     flops = 22.0 * wl.batch * wl.heads * wl.n * wl.k * wl.d
     tf = flops / (ms * 1e-3) / 1e12
-    # operands of the eleven products, True where fp32 (inputs in x, the computed intermediates
-    # Kbar, Vbar, P, dS, dKbar, dVbar in fp32): Kbar = E K, Vbar = F V, S = Q Kbar^T,
-    # dP = dO Vbar^T, dQ = dS Kbar, dVbar = P^T dO, dKbar = dS^T Q, dE = dKbar K^T, dF = dVbar V^T,
+    # operands of the thirteen executed products, True where fp32 (inputs in x, the computed
+    # intermediates Kbar, Vbar, P, dS, dKbar, dVbar in fp32): Kbar = E K, Vbar = F V,
+    # S = Q Kbar^T, dP = dO Vbar^T, dQ = dS Kbar (query-block kernel), S and dP again,
+    # dVbar = P^T dO, dKbar = dS^T Q (slot-block kernel), dE = dKbar K^T, dF = dVbar V^T,
     # dK = E^T dKbar, dV = F^T dVbar
     x = wl.dtype != synth.DT_BF16
-    ops = [(x, x), (x, x), (x, True), (x, True), (True, True), (True, x), (True, x),
-           (True, x), (True, x), (x, True), (x, True)]
+    ops = [(x, x), (x, x), (x, True), (x, True), (True, True), (x, True), (x, True),
+           (True, x), (True, x), (True, x), (True, x), (x, True), (x, True)]
     mult = sum(1 + int(a) + int(b) for a, b in ops)
     executed = 2.0 * mult * wl.batch * wl.heads * wl.n * wl.k * wl.d
     etf = executed / (ms * 1e-3) / 1e12

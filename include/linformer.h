@@ -199,7 +199,9 @@ int linformer_forward_conv(const lf_problem* p, const void* Q, const void* K, co
  * fp32 accumulation throughout (Kbar, Vbar recomputed in fp32); the GEMMs multiply fp32 operands
  * as split bf16 pairs (hi + lo, within 2^-16 of the value: the bf16x3 scheme), and the results
  * meet the 1e-4 relative bar of an fp32 computation (tested).  ws:
- * linformer_backward_workspace_size() bytes of scratch (16-byte aligned). */
+ * linformer_backward_workspace_size() bytes of scratch (16-byte aligned): fp32 Kbar, Vbar, dKbar,
+ * dVbar, four floats of softmax statistics per query and split partial sums, O(B H (k d + n))
+ * bytes; no n x k matrix is stored (P and dS are recomputed where they are reduced). */
 int linformer_backward_workspace_size(const lf_problem* p, size_t* bytes);
 int linformer_backward(const lf_problem* p, const void* Q, const void* K, const void* V,
                        const void* E, const void* F, const int32_t* lengths, const void* dO,
