@@ -360,7 +360,7 @@ void bw_ws(const lf_problem* p, BwWs* w) {
     w->stats = take(st);
     w->dkb = take(kv);
     w->dvb = take(kv);
-    // split-reduction partial sums, the largest any of the backward's GEMMs asks for
+    // split-reduction partial sums, the largest any of the backward's kernels asks for
     const int B = p->batch, H = p->heads, n = p->n, k = p->k;
     const bool unshared = p->share == LF_SHARE_NONE;
     size_t part = lf::bw_gemm_part_bytes(k, n, unshared ? B * 64 : B * H * 64,
@@ -368,6 +368,7 @@ void bw_ws(const lf_problem* p, BwWs* w) {
     part = std::max(part, lf::bw_gemm_part_bytes(n, 64, k, 2 * B * H));            // dK and dV
     lf::ProjGeom g;
     if (geometry(p, &g)) part = std::max(part, part_bytes(p, g));                  // Kbar, Vbar
+    part = std::max(part, lf::kv_part_bytes(B, H, k));                              // dKbar, dVbar
     w->part = take(part);
     w->total = o;
 }
@@ -1006,6 +1007,12 @@ int linformer_backward(const lf_problem* p, const void* Q, const void* K, const 
     kv.Q = Q; kv.dO = dO; kv.in_bf16 = bf; kv.Kb = Kb; kv.Vb = Vb; kv.stats = stats;
     kv.lengths = lengths; kv.dKb = dKb; kv.dVb = dVb;
     kv.B = B; kv.H = H; kv.n = n; kv.k = k; kv.scale = s;
+    kv.qparts = lf::kv_qparts(B, H, k);
+    if (kv.qparts == 2) {
+        kv.part = part;
+        kv.pair_ctr = (unsigned long long*)((uint8_t*)part + lf::kv_sums_bytes(B, H, k));
+        kv.pair_epoch = next_pair_epoch();
+    }
     if (lf::launch_bw_kv(kv, strm) != hipSuccess) return LF_ERR_LAUNCH;
     // dE (+)= dXbar X^T: M = k, N = n, reduction over (b, c) (unshared: z = h) or over (b, h, c);
     // positions at or past item b's length read as zero

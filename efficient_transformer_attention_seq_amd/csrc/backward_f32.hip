@@ -519,15 +519,15 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
     }
 }
 
-// ---- dVbar = P^T dO and dKbar = scale dS^T Q per (b, h) and block of 128 slots, P and dS
-// recomputed from the fused kernel's per-query statistics (the reductions over the queries of
-// FlashAttention-2's backward, with the projected slots in the role of its keys).  Wave w owns the
-// 16 slots s0 = 128 blockIdx.x + 16 w: their Kbar and Vbar rows sit in registers as hi and lo
-// bf16 operands.  The workgroup streams the queries before the length through LDS in chunks of 32
-// (Q and dO as hi, and for fp32 inputs lo, planes [32][64] with the 16-byte chunk swizzle of
-// split_bf16.h, and the chunk's statistics), double-buffered: the next chunk is loaded into
-// registers while the current one is multiplied.  Per chunk and wave, with lane (g, l) holding
-// C[4 g + e][l] of a 16 x 16 block:
+// ---- dVbar = P^T dO and dKbar = scale dS^T Q per (b, h), block of 64 slots and half of the valid
+// queries (or all of them), P and dS recomputed from the fused kernel's per-query statistics (the
+// reductions over the queries of FlashAttention-2's backward, with the projected slots in the role
+// of its keys).  Four waves; wave w owns the 16 slots s0 = 64 blockIdx.x + 16 w: their Kbar and
+// Vbar rows sit in registers as hi and lo bf16 operands.  The workgroup streams its queries
+// through LDS in chunks of 32 (Q and dO as hi, and for fp32 inputs lo, planes [32][64] with the
+// 16-byte chunk swizzle of split_bf16.h, and the chunk's statistics), double-buffered, the
+// next-but-one chunk in registers.  Per chunk and wave, with lane (g, l) holding C[4 g + e][l] of a
+// 16 x 16 block:
 //   S = Q Kbar^T, dP = dO Vbar^T   (32 queries x 16 slots: query rows as A operands from LDS,
 //                                   the slots' rows as B operands from registers)
 //   P = exp2(c s - c m) / sum, dS = P o (dP - D)   (queries at or past the length: 0)
@@ -535,9 +535,14 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
 //        P / dS of queries 4 g + e and 16 + 4 g + e straight from the accumulators, split into hi
 //        and lo, and the A operand dO^T / Q^T is read at exactly those queries with the
 //        transposing ds_read_b64_tr_b16)
-// and at the end each wave writes its 16 slots' rows of dKbar (times scale) and dVbar.
+// and at the end each wave writes its 16 slots' rows of dKbar (times scale) and dVbar, after
+// adding the other query half's sums when the queries are split (BwKvArgs).  Small workgroups
+// and the query split fill the chip: three workgroups share a compute unit, and B H ceil(k / 64)
+// tiles below two per compute unit are doubled by the split.
+constexpr int kKvWaves = 4, kKvSlots = 16 * kKvWaves;
+
 template <typename TQ>
-__global__ __launch_bounds__(512) void bw_kv_kernel(BwKvArgs a) {
+__global__ __launch_bounds__(64 * kKvWaves) void bw_kv_kernel(BwKvArgs a) {
     constexpr bool QLO = sizeof(TQ) == 4;
     constexpr int CQ = 32;                  // queries per chunk
     constexpr int PLB = CQ * 128;           // bytes of one [32][64] bf16 plane
@@ -546,8 +551,8 @@ __global__ __launch_bounds__(512) void bw_kv_kernel(BwKvArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l = lane & 15;
-    const int bh = blockIdx.y;
-    const int s0 = 128 * blockIdx.x + 16 * wave;
+    const int bh = blockIdx.z, qpart = blockIdx.y;
+    const int s0 = kKvSlots * blockIdx.x + 16 * wave;
     const bool active = s0 < a.k;
     const int L = clamp_len(a.lengths, bh / a.H, a.n);
     const size_t head = (size_t)bh * a.n * 64;
@@ -570,8 +575,8 @@ __global__ __launch_bounds__(512) void bw_kv_kernel(BwKvArgs a) {
             vbl[kc] = pair8(l0, l1);
         }
     }
-    // chunk loads: thread t takes 8 bytes of Q and of dO (bf16: 4 values; fp32: 16 bytes, split)
-    // at row t / 16, columns 4 (t % 16) .. + 3, and thread t < 32 the statistics of query t.
+    // chunk loads: thread t takes 8 values of Q and of dO (bf16: 16 bytes; fp32: 32 bytes, split)
+    // at row t / 8, columns 8 (t % 8) .. + 7, and thread t < 32 the statistics of query t.
     // Buffer descriptors sized to the rows before the length return zeros past it, so the loads
     // need no branches (and none waits for another).
     const uint32_t rows = (uint32_t)L * 64 * sizeof(TQ);
@@ -581,22 +586,19 @@ __global__ __launch_bounds__(512) void bw_kv_kernel(BwKvArgs a) {
         __builtin_amdgcn_make_buffer_rsrc((void*)((const TQ*)a.dO + head), 0, rows, 0x00020000);
     const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.stats + (size_t)bh * a.n * 4), 0, (uint32_t)L * 16, 0x00020000);
-    const int lr = tid >> 4, lc = 4 * (tid & 15);
+    const int lr = tid >> 3, lc = 8 * (tid & 7);
     // two register sets: chunk ch + 2 is loaded into set ch % 2 while chunk ch is multiplied and
     // chunk ch + 1 (set (ch + 1) % 2) waits to be stored, so each load has two chunks' time to land
-    u32x4 rq[2], rg[2];
+    constexpr int QW = sizeof(TQ) / 2;   // 16-byte pieces per thread and matrix
+    u32x4 rq[2][QW], rg[2][QW];
     f32x4 rs[2];
     auto load_chunk = [&](auto set, int q0) {
         constexpr int S = decltype(set)::value;
         const uint32_t off = (uint32_t)((q0 + lr) * 64 + lc) * sizeof(TQ);
-        if constexpr (QLO) {
-            rq[S] = __builtin_amdgcn_raw_buffer_load_b128(rsq, off, 0, 0);
-            rg[S] = __builtin_amdgcn_raw_buffer_load_b128(rsg, off, 0, 0);
-        } else {
-            const u32x2 zq = __builtin_amdgcn_raw_buffer_load_b64(rsq, off, 0, 0);
-            const u32x2 zg = __builtin_amdgcn_raw_buffer_load_b64(rsg, off, 0, 0);
-            rq[S] = u32x4{zq[0], zq[1], 0u, 0u};
-            rg[S] = u32x4{zg[0], zg[1], 0u, 0u};
+#pragma unroll
+        for (int w = 0; w < QW; ++w) {
+            rq[S][w] = __builtin_amdgcn_raw_buffer_load_b128(rsq, off + 16 * w, 0, 0);
+            rg[S][w] = __builtin_amdgcn_raw_buffer_load_b128(rsg, off + 16 * w, 0, 0);
         }
         rs[S] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                               rss, (uint32_t)(q0 + (tid & (CQ - 1))) * 16, 0, 0));
@@ -604,18 +606,20 @@ __global__ __launch_bounds__(512) void bw_kv_kernel(BwKvArgs a) {
     auto store_chunk = [&](auto set) {
         constexpr int S = decltype(set)::value;
         uint8_t* buf = lds + S * BUF;
-        const int off = kv_off(lr, lc);
+        const int off = kv_off(lr, lc);   // one whole 16-byte chunk of the row
         if constexpr (QLO) {
-            u32x2 h, o;
-            split4(__builtin_bit_cast(f32x4, rq[S]), h, o);
-            *(u32x2*)(buf + off) = h;
-            *(u32x2*)(buf + PLB + off) = o;
-            split4(__builtin_bit_cast(f32x4, rg[S]), h, o);
-            *(u32x2*)(buf + 2 * PLB + off) = h;
-            *(u32x2*)(buf + 3 * PLB + off) = o;
+            u32x2 h0, o0, h1, o1;
+            split4(__builtin_bit_cast(f32x4, rq[S][0]), h0, o0);
+            split4(__builtin_bit_cast(f32x4, rq[S][1]), h1, o1);
+            *(bf16x8*)(buf + off) = pair8(h0, h1);
+            *(bf16x8*)(buf + PLB + off) = pair8(o0, o1);
+            split4(__builtin_bit_cast(f32x4, rg[S][0]), h0, o0);
+            split4(__builtin_bit_cast(f32x4, rg[S][1]), h1, o1);
+            *(bf16x8*)(buf + 2 * PLB + off) = pair8(h0, h1);
+            *(bf16x8*)(buf + 3 * PLB + off) = pair8(o0, o1);
         } else {
-            *(u32x2*)(buf + off) = u32x2{rq[S][0], rq[S][1]};
-            *(u32x2*)(buf + PLB + off) = u32x2{rg[S][0], rg[S][1]};
+            *(u32x4*)(buf + off) = rq[S][0];
+            *(u32x4*)(buf + PLB + off) = rg[S][0];
         }
         if (tid < CQ) *(f32x4*)(buf + NPL * PLB + tid * 16) = rs[S];
     };
@@ -623,10 +627,13 @@ __global__ __launch_bounds__(512) void bw_kv_kernel(BwKvArgs a) {
     using I1 = std::integral_constant<int, 1>;
     const int tr_row = 4 * g + (l >> 2), tr_col = 4 * (l & 3);
     f32x4 dk[4] = {}, dv[4] = {};
-    const int nchunk = (L + CQ - 1) / CQ;
+    // this workgroup's chunks: all of them, or one of two halves of the valid ones
+    const int ntot = (L + CQ - 1) / CQ;
+    const int cbeg = ntot * qpart / a.qparts, nchunk = ntot * (qpart + 1) / a.qparts - cbeg;
+    const int qbase = cbeg * CQ;
     if (nchunk > 0) {
-        load_chunk(I0{}, 0);
-        if (nchunk > 1) load_chunk(I1{}, CQ);
+        load_chunk(I0{}, qbase);
+        if (nchunk > 1) load_chunk(I1{}, qbase + CQ);
         store_chunk(I0{});
     }
     __syncthreads();
@@ -635,7 +642,7 @@ __global__ __launch_bounds__(512) void bw_kv_kernel(BwKvArgs a) {
     auto chunk = [&](auto parity, int ch) {
         constexpr int PAR = decltype(parity)::value;
         const uint8_t* buf = lds + PAR * BUF;
-        if (ch + 2 < nchunk) load_chunk(parity, (ch + 2) * CQ);
+        if (ch + 2 < nchunk) load_chunk(parity, qbase + (ch + 2) * CQ);
         if (active) {
             const uint8_t* qh = buf;
             const uint8_t* ql = buf + PLB;
@@ -705,6 +712,57 @@ __global__ __launch_bounds__(512) void bw_kv_kernel(BwKvArgs a) {
     for (int ch = 0; ch < nchunk; ch += 2) {
         chunk(I0{}, ch);
         if (ch + 1 < nchunk) chunk(I1{}, ch + 1);
+    }
+    if (a.qparts == 2) {
+        // the two query halves of a tile: the first to get here leaves its sums (agent-coherent
+        // stores, 1 KB of contiguous bytes per instruction) and exits, the other adds them
+        const int tile = bh * gridDim.x + blockIdx.x;
+        unsigned long long* ctr = a.pair_ctr + tile;
+        const unsigned long long tag_in = a.pair_epoch << 1, tag_ready = tag_in | 1ull;
+        __shared__ int s_role;   // 0: first, 1: second (sums not ready yet), 2: second (ready)
+        if (tid == 0) {
+            const unsigned long long prev =
+                __hip_atomic_exchange(ctr, tag_in, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_role = prev == tag_ready ? 2 : (prev == tag_in ? 1 : 0);
+        }
+        __syncthreads();
+        const int role = s_role;
+        constexpr uint32_t kWaveBytes = 8 * 64 * 16;   // dk[4], dv[4] of every lane
+        const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+            a.part + ((size_t)tile * kKvWaves + wave) * (kWaveBytes / 4), 0, kWaveBytes, 0x00020000);
+        constexpr int kSC0 = 1, kSC1 = 16;   // cache-policy bits: agent-coherent access
+        if (role == 0) {
+            if (active) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4, q < 4 ? dk[q] : dv[q - 4]), rp, (q * 64 + lane) * 16, 0, kSC1);
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's sums are out
+            __syncthreads();                      // everyone's
+            if (tid == 0)
+                __hip_atomic_store(ctr, tag_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        if (tid == 0) {
+            // the first workgroup is past its exchange with only stores left, so this wait ends;
+            // the bound only guards against a counter that held this call's tag before it
+            for (int it = 0; role == 1 && it < (1 << 20) &&
+                             __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag_ready;
+                 ++it)
+                __builtin_amdgcn_s_sleep(2);
+            __hip_atomic_store(ctr, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (active) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const f32x4 v = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, (q * 64 + lane) * 16, 0, kSC0 | kSC1));
+                if (q < 4) dk[q] += v;
+                else dv[q - 4] += v;
+            }
+        }
     }
     if (!active) return;
     // dv[cb] element e of lane (g, l): dVbar[s0 + l][16 cb + 4 g + e]
@@ -823,11 +881,27 @@ static hipError_t launch_attend_t(const BwAttendArgs& a, hipStream_t stream) {
     }
 }
 
+int kv_qparts(int B, int H, int k) {
+    // fewer than two tiles per compute unit (MI355X: 256): split each tile's queries in two
+    const long long tiles = (long long)B * H * ((k + kKvSlots - 1) / kKvSlots);
+    return tiles < 512 ? 2 : 1;
+}
+
+size_t kv_sums_bytes(int B, int H, int k) {
+    return (size_t)B * H * ((k + kKvSlots - 1) / kKvSlots) * kKvWaves * 8 * 64 * 16;
+}
+
+size_t kv_part_bytes(int B, int H, int k) {   // the sums, then one counter per tile
+    return kv_sums_bytes(B, H, k) + (size_t)B * H * ((k + kKvSlots - 1) / kKvSlots) * 8;
+}
+
 hipError_t launch_bw_kv(const BwKvArgs& a, hipStream_t stream) {
-    if (a.k % 32 || a.k > 256 || a.B * a.H > 65535) return hipErrorInvalidValue;
-    const dim3 grid((a.k + 127) / 128, a.B * a.H);
-    if (a.in_bf16) hipLaunchKernelGGL(bw_kv_kernel<uint16_t>, grid, dim3(512), 0, stream, a);
-    else hipLaunchKernelGGL(bw_kv_kernel<float>, grid, dim3(512), 0, stream, a);
+    if (a.k % 32 || a.k > 256 || a.B * a.H > 65535 || (a.qparts != 1 && a.qparts != 2) ||
+        (a.qparts == 2 && (!a.part || !a.pair_ctr || a.pair_epoch == 0)))
+        return hipErrorInvalidValue;
+    const dim3 grid((a.k + kKvSlots - 1) / kKvSlots, a.qparts, a.B * a.H);
+    if (a.in_bf16) hipLaunchKernelGGL(bw_kv_kernel<uint16_t>, grid, dim3(64 * kKvWaves), 0, stream, a);
+    else hipLaunchKernelGGL(bw_kv_kernel<float>, grid, dim3(64 * kKvWaves), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -186,8 +186,23 @@ struct BwKvArgs {
     int B, H, n, k;
     int in_bf16;
     float scale;
+    // qparts = 2: the valid queries of each (b, h) are split in two halves, one workgroup each; of
+    // the two, the one that finishes first leaves its partial sums in `part` (kv_part_bytes()
+    // bytes, per 64-slot tile and wave 8 KB in register order) and marks the tile's counter
+    // pair_ctr[tile] (B H ceil(k / 64) counters) with 2 pair_epoch + 1; the other adds them (a + b,
+    // the same bits in either order) and stores.  Counters hold 0 or this call's tags and are left
+    // at 0; pair_epoch is unique per call and below 2^62.
+    int qparts;
+    float* part;
+    unsigned long long* pair_ctr;
+    unsigned long long pair_epoch;
 };
 hipError_t launch_bw_kv(const BwKvArgs& a, hipStream_t stream);
+// query halves per (b, h) the slot-block kernel uses; the bytes of its partial sums, and of the
+// sums followed by the tiles' counters
+int kv_qparts(int B, int H, int k);
+size_t kv_sums_bytes(int B, int H, int k);
+size_t kv_part_bytes(int B, int H, int k);
 
 // Dense projection Y = X . W^T of the encoder attention stack (linear_bf16.hip).
 struct LinearBf16Args {
