@@ -358,10 +358,6 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
     constexpr int PL = K * 128;   // bytes of one [k][64] bf16 plane
     constexpr bool QLO = sizeof(TQ) == 4;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
-    const uint8_t* kh = lds8;
-    const uint8_t* kl = lds8 + PL;
-    const uint8_t* vh = lds8 + 2 * PL;
-    const uint8_t* vl = lds8 + 3 * PL;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l = lane & 15;
     const int bh = blockIdx.y;
@@ -520,7 +516,7 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
 }
 
 // ---- dVbar = P^T dO and dKbar = scale dS^T Q per (b, h), block of 64 slots and half of the valid
-// queries (or all of them), P and dS recomputed from the fused kernel's per-query statistics (the
+// queries (or all of them), P and dS recomputed from bw_attend_kernel's per-query statistics (the
 // reductions over the queries of FlashAttention-2's backward, with the projected slots in the role
 // of its keys).  Four waves; wave w owns the 16 slots s0 = 64 blockIdx.x + 16 w: their Kbar and
 // Vbar rows sit in registers as hi and lo bf16 operands.  The workgroup streams its queries
