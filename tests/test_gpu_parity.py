@@ -357,6 +357,40 @@ def test_forward_parity_small(case, dtype):
     assert err <= G.TOL[dtype]
 
 
+def _random_case(seed):
+    """A seeded shape drawn over the supported space: batch and heads 1-4, n a multiple of 64 up
+    to 1536, k a multiple of 32 up to 256 (128 or 256, the one-launch kernel's, drawn more
+    often), any sharing mode, bf16 (three in four) or fp32, lengths drawn from 1, n - 1, n and
+    random values, with one item of every multi-item batch empty."""
+    rng = np.random.default_rng(7000 + seed)
+    B, H = int(rng.integers(1, 5)), int(rng.integers(1, 5))
+    n = 64 * int(rng.integers(1, 25))
+    k = 32 * int(rng.integers(1, 9)) if rng.random() < 0.6 else int(rng.choice([128, 256]))
+    share = [NONE, HEAD, KV, LAYER][int(rng.integers(0, 4))]
+    dtype = F32 if rng.random() < 0.25 else BF
+    pool = [1, n, n - 1, int(rng.integers(1, n + 1)), int(rng.integers(1, n + 1))]
+    lens = [pool[int(rng.integers(0, len(pool)))] for _ in range(B)]
+    if B > 1:
+        lens[int(rng.integers(0, B))] = 0
+    return B, H, n, k, share, dtype, lens
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_forward_random_shapes(seed):
+    """Seeded shapes across the whole supported space (both paths: the one-launch short-sequence
+    kernel where it applies, projection + attention elsewhere), in full against the oracle, with
+    guard bands around the output."""
+    B, H, n, k, share, dtype, lens = _random_case(seed)
+    inp = synth.random_inputs(B, H, n, 64, k, dtype, share, seed=900 + seed, lengths=lens)
+    G.log(f"random forward seed={seed} B={B} H={H} n={n} k={k} share={share} dtype={dtype} "
+          f"lengths={lens}")
+    out, ok = G.run_forward(inp, guard=True)
+    err = orc.slice_rel_err(out, _ref_forward(inp))
+    G.log(f"  err {err:.3e}")
+    assert ok, "write outside the output tensor"
+    assert err <= G.TOL[dtype]
+
+
 def test_forward_single_head_f32_full():
     """Single-head fp32 workload: B1 H1 n512 k128, separate E, F, seed 0 (full comparison)."""
     inp = synth.make_inputs(synth.C1)
