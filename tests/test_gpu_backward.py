@@ -68,6 +68,30 @@ def test_backward_parity(B, H, n, k, dtype, share, lengths):
             assert np.all(got[1][b, :, L:] == 0) and np.all(got[2][b, :, L:] == 0)
 
 
+def _random_case(seed):
+    """A seeded shape over the supported space: batch and heads 1-4, n a multiple of 64 up to
+    1024, k a multiple of 32 up to 256, any sharing mode and input dtype, lengths of at least a
+    quarter of n (or 0 for one item of a multi-item batch).  Items of one or a few tokens are
+    left to the normwise test below: their gradient slices cancel to far below the terms they
+    sum."""
+    rng = np.random.default_rng(8100 + seed)
+    B, H = int(rng.integers(1, 5)), int(rng.integers(1, 5))
+    n = 64 * int(rng.integers(1, 17))
+    k = 32 * int(rng.integers(1, 9))
+    share = [NONE, HEAD, KV, LAYER][int(rng.integers(0, 4))]
+    dtype = F32 if rng.random() < 0.4 else BF
+    lens = [int(rng.integers(max(2, n // 4), n + 1)) for _ in range(B)]
+    if B > 1:
+        lens[int(rng.integers(0, B))] = 0
+    return B, H, n, k, dtype, share, lens
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_backward_random_shapes(seed):
+    B, H, n, k, dtype, share, lengths = _random_case(seed)
+    test_backward_parity(B, H, n, k, dtype, share, lengths)
+
+
 def test_backward_one_token_item_is_normwise_accurate():
     """A one-token item's gradients are covariances under the softmax weights over the k slots
     (dS sums to zero), so a head's dQ, dK, dV slice can come out orders of magnitude below the
