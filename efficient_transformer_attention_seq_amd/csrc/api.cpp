@@ -455,9 +455,16 @@ int do_linear(const lf::LinearBf16Args& base, hipStream_t stream) {
 }
 
 // Workspace of one forward call: Kbar | Vbar | split partial sums, each 256-byte aligned.
+// Flags of the fused kernel's hand-off (one 8-byte tag per (b, h)), after the partials; only
+// shapes the fused kernel takes have them.
+size_t flag_bytes(const lf_problem* p) {
+    return p->dtype == LF_BF16 && lf::fused_supported(p->n, p->k)
+               ? round_up((size_t)8 * p->batch * p->heads, 256) : 0;
+}
+
 size_t forward_ws_bytes(const lf_problem* p, const lf::ProjGeom& g) {
     return round_up(kbar_bytes(p), 256) + round_up(vbar_bytes(p), 256) +
-           round_up(part_bytes(p, g), 256);
+           round_up(part_bytes(p, g), 256) + flag_bytes(p);
 }
 
 // The whole layer in one launch (fused_bf16.hip): bf16, short sequences, and one matrix
@@ -511,16 +518,35 @@ int forward_validate(const lf_problem* p, const void* Q, const void* K, const vo
     return LF_OK;
 }
 
-// Work split of the fused kernel: the (b, h) units of the last, partial round of workgroups are
-// each taken by `parts` workgroups (all project the unit, each attends a contiguous share of its
-// query tiles), as many as fill the compute units that round would leave idle, with at least
-// eight query tiles (one per wave) per share at full length (LINFORMER_FUSED_SPLIT=0: none).
-void fused_split(lf::FusedBf16Args& f) {
+// Work split of the fused kernel (one workgroup per compute unit at a time; G compute units, U
+// = B H units).  With G < U <= 3G/2 and a flag region (the forward's workspace), mode 2: G
+// workgroups, each of the U - G extra units projected by one workgroup and attended by its
+// neighbour after their own units.  Otherwise the (b, h) units of the last, partial round of
+// workgroups are each taken by `parts` workgroups (all project the unit, each attends a
+// contiguous share of its query tiles), as many as fill the compute units that round would leave
+// idle, with at least eight query tiles (one per wave) per share at full length.
+// LINFORMER_FUSED_SPLIT=0: no split at all; LINFORMER_FUSED_HANDOFF=0: no mode 2.
+void fused_split(lf::FusedBf16Args& f, uint8_t* Kbar = nullptr, uint16_t* Vbar = nullptr,
+                 unsigned long long* flags = nullptr) {
     const int units = f.B * f.H, G = cu_count();
     f.whole = units;
     f.parts = 1;
+    f.mode = 0;
+    f.grid = G;
     const char* e = std::getenv("LINFORMER_FUSED_SPLIT");
     if ((e && e[0] == '0') || G <= 0) return;
+    const char* ho = std::getenv("LINFORMER_FUSED_HANDOFF");
+    if (flags && f.dm == 0 && !(ho && ho[0] == '0') && units > G && 2 * (units - G) <= G) {
+        const size_t el = (size_t)units * f.k * 64;
+        f.mode = 2;
+        f.Khi = (uint16_t*)Kbar;
+        f.Klo = Kbar + 2 * el;
+        f.Ksc = Kbar + 3 * el;
+        f.Vb = Vbar;
+        f.flags = flags;
+        f.epoch = next_pair_epoch();
+        return;
+    }
     const int rest = units % G;
     if (rest == 0) return;
     const int parts = std::min(G / rest, std::max(1, f.n / 32 / 8));
@@ -552,7 +578,8 @@ int forward_run(const lf_problem* p, const FwdPlan& pl, const void* Q, const voi
         f.k = p->k;
         f.e_heads = p->share == LF_SHARE_NONE ? p->heads : 1;
         f.c = eff_scale(p) * lf::kLog2e;
-        fused_split(f);
+        fused_split(f, (uint8_t*)Kbar, (uint16_t*)Vbar,
+                    (unsigned long long*)(w + pl.kb + pl.vb + round_up(pl.pb, 256)));
         return launch_status(lf::launch_fused_bf16(f, s));
     }
     int st = do_project(p, K, V, E, pl.Fr, lengths, Kbar, Vbar, part, pl.g, s);

@@ -24,7 +24,13 @@
 // Work split: when the units do not fill whole rounds of workgroups, each unit of the last,
 // partial round is taken by several workgroups that all project it and attend contiguous shares
 // of its tiles, so that round fills the compute units (every output tile is still computed once,
-// by the same arithmetic).
+// by the same arithmetic).  Hand-off (HANDOFF, between one and one and a half units per compute
+// unit): one round of workgroups; workgroup 2 j first projects the extra unit grid + j and
+// copies its planes, un-swizzled, to the workspace in the attention kernel's format with
+// agent-coherent stores, then sets the unit's flag to the call's tag; workgroup 2 j + 1, after
+// its own unit, waits for that flag (set by a workgroup of lower index, which is already
+// running), loads the planes with agent-coherent loads and attends all of the unit's tiles.  The
+// planes are the same bytes either way, so the output is bitwise that of the plain split.
 #include "attend_core.h"
 
 namespace lf {
@@ -59,31 +65,56 @@ __device__ __forceinline__ void vmcnt_le() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int KB, bool STACK>
+// dma16 with the descriptor read from lane 0 (so that it sits in scalar registers even where
+// the compiler cannot prove it wave-uniform).
+__device__ __forceinline__ void dma16u(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+    i32x4 rs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+    dma16(rs, lds_base, voff);
+}
+
+// dma16 with agent-coherent loads (sc0 sc1): data another workgroup stored with agent-coherent
+// stores, possibly on another XCD, is read from the coherence point, not from a stale L2 line.
+__device__ __forceinline__ void dma16_coherent(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+    i32x4 rs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen sc0 sc1 lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rs)
+                 : "memory");
+}
+
+template <int KB, bool STACK, bool HANDOFF>
 __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
     using FL = FusedLayout<KB>;
     using Ly = AttnLayout<KB>;
     constexpr int K = Ly::K;
     constexpr int WM = KB / 4;   // 32-slot blocks per wave: the k slots over 4 waves
     __shared__ __attribute__((aligned(16))) uint8_t smem[FL::BYTES];
-    const uint32_t lds0 = lds_addr(smem);
+    constexpr int kSC1 = 16;   // cache-policy bit: agent-coherent stores
 
-    // this workgroup's unit and its share of the unit's query tiles
-    int bh = blockIdx.x, part = 0, nparts = 1;
-    if (bh >= a.whole) {
-        const int r = bh - a.whole;
-        bh = a.whole + r / a.parts;
-        part = r % a.parts;
-        nparts = a.parts;
-    }
-    const int b = bh / a.H, h = bh % a.H;
-    const int tid = threadIdx.x;
+    // One unit (b, h): its planes come from its own projection (publish: also copied to global
+    // memory and flagged for another workgroup) or, `fill`, from the copy another workgroup
+    // published; then the query tiles [ntiles lo / den, ntiles hi / den) of the unit.
+    auto run_unit = [&](int bh, bool fill, bool publish, int lo, int hi, int den) __attribute__((always_inline)) {
+    // with several units per workgroup, the per-lane constants are derived inside each unit
+    // (through an opaque copy of the thread index), so that the compiler does not share them
+    // between the units and keep them live across the projection's register-heavy loop
+    uint32_t tid_o = threadIdx.x;
+    if constexpr (HANDOFF) asm volatile("" : "+v"(tid_o));
+    const int tid = (int)tid_o;
+    const uint32_t lds0 = HANDOFF ? opaque(lds_addr(smem)) : lds_addr(smem);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int b = bh / a.H, h = bh % a.H;
     const int L = clamp_len(a.lengths, b, a.n);
     const int ntiles = (L + kTileQ - 1) / kTileQ;
-    const int t0 = ntiles * part / nparts, t1 = ntiles * (part + 1) / nparts;
+    const int t0 = ntiles * lo / den, t1 = ntiles * hi / den;
     const size_t rowbase = (size_t)bh * a.n;
+    __syncthreads();   // the previous unit's readers are done with the LDS
 
     // ---- the first tile's Q, in flight during the projection
     u32x4 qraw[4];
@@ -95,13 +126,14 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
     if (t0 + wave < t1) load_q(t0 + wave);
 
     // ---- zero the rows past the last valid tile (streaming stores, drained under the work)
-    if (part == 0) {
+    if (lo == 0 && hi > 0) {   // the workgroup that attends the unit's first tiles
         const u32x4 zero = {0u, 0u, 0u, 0u};
         u32x4* blk = (u32x4*)(a.O + (rowbase + (size_t)ntiles * kTileQ) * kHeadDim);
         const int nz = (a.n - ntiles * kTileQ) * 8;   // 16-byte chunks
         for (int c = tid; c < nz; c += kThreads) __builtin_nontemporal_store(zero, &blk[c]);
     }
 
+    if (!fill) {
     // ---- projection.  Sequence form: the slot rows are E's (positions contiguous), the columns
     // the head's K, V rows (read transposed), 64 positions per stage, over the valid length.
     // Stack form: the slot rows are the head's batch item's projected input Xbar_b (features
@@ -134,12 +166,12 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
                 const int lc = lpc ^ swz_e(r);
                 const size_t e = STACK ? ((size_t)step * K + r) * kHeadDim + lc * 8
                                        : (size_t)r * a.n + t0 + lc * 8;
-                dma16(rsrc_e, sbase + j * 1024, (uint32_t)(e * 2));
+                dma16u(rsrc_e, sbase + j * 1024, (uint32_t)(e * 2));
             } else if constexpr (STACK) {   // W rows: 64 of W_K then 64 of W_V, as slot rows are
                 const int wr = (j - K / 8) * 8 + lrow;
                 const int lc = lpc ^ swz_e(wr);
                 const size_t grow = (size_t)(wr >> 6) * a.dm + 64 * h + (wr & 63);
-                dma16(rsrc_k, sbase + FL::E_STAGE + (j - K / 8) * 1024,
+                dma16u(rsrc_k, sbase + FL::E_STAGE + (j - K / 8) * 1024,
                       (uint32_t)((grow * a.dm + t0 + lc * 8) * 2));
             } else {                      // K (then V) positions 8 q .. 8 q + 7, 32-byte blocks
                 const int jj = j - K / 8;  // swizzled by the position's low bits
@@ -148,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
                 const int lc = 2 * ((lpc >> 1) ^ (tl & 3)) + (lpc & 1);
                 const uint32_t off = (uint32_t)(((t0 + tl) * kHeadDim + lc * 8) * 2);
                 const uint32_t dst = sbase + FL::E_STAGE + (jj >> 3) * FL::X_TILE + q * 1024;
-                dma16((jj >> 3) ? rsrc_v : rsrc_k, dst, off);
+                dma16u((jj >> 3) ? rsrc_v : rsrc_k, dst, off);
             }
         }
     };
@@ -260,8 +292,69 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
     }
     __syncthreads();
 
+    if (publish) {
+        // the planes, un-swizzled, to the unit's global copy (the attention kernel's format)
+        // with agent-coherent stores; then the flag, once every wave's stores have completed
+        const size_t off = (size_t)bh * K * kHeadDim;
+        const __amdgpu_buffer_rsrc_t gh = __builtin_amdgcn_make_buffer_rsrc(a.Khi + off, 0, Ly::PLANE, 0x00020000);
+        const __amdgpu_buffer_rsrc_t gv = __builtin_amdgcn_make_buffer_rsrc(a.Vb + off, 0, Ly::PLANE, 0x00020000);
+        const __amdgpu_buffer_rsrc_t gl = __builtin_amdgcn_make_buffer_rsrc(a.Klo + off, 0, Ly::LOB, 0x00020000);
+        const __amdgpu_buffer_rsrc_t gs = __builtin_amdgcn_make_buffer_rsrc(a.Ksc + (size_t)bh * K * 2, 0, K * 2, 0x00020000);
+        for (int c = tid; c < K * 8; c += kThreads) {   // 16-byte chunk c % 8 of row c / 8
+            const int r = c >> 3, lc = c & 7;
+            const u32x4 vh = *(const u32x4*)(smem + r * 128 + ((lc ^ swz16(r)) << 4));
+            const u32x4 vv = *(const u32x4*)(smem + Ly::OFF_V + r * 128 +
+                                              ((2 * ((lc >> 1) ^ (r & 3)) + (lc & 1)) << 4));
+            __builtin_amdgcn_raw_buffer_store_b128(vh, gh, c * 16, 0, kSC1);
+            __builtin_amdgcn_raw_buffer_store_b128(vv, gv, c * 16, 0, kSC1);
+        }
+        for (int c = tid; c < K * 4; c += kThreads) {   // 16-byte chunk c % 4 of residual row c / 4
+            const int r = c >> 2, ch = c & 3;
+            const u32x4 vl = *(const u32x4*)(smem + Ly::OFF_L + r * 64 + ((ch ^ ((r >> 1) & 3)) << 4));
+            __builtin_amdgcn_raw_buffer_store_b128(vl, gl, c * 16, 0, kSC1);
+        }
+        if (tid < K * 2 / 16)
+            __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(smem + Ly::OFF_S + tid * 16), gs,
+                                                   tid * 16, 0, kSC1);
+        vmcnt_le<0>();     // this wave's stores have reached the coherence point
+        __syncthreads();   // everyone's
+        if (tid == 0)
+            __hip_atomic_store(a.flags + bh, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    } else {
+        // the unit's planes from the copy its projecting workgroup (of lower index, so already
+        // running) publishes; the bound only guards against a flag that never arrives
+        if (tid == 0) {
+            for (int it = 0; it < (1 << 22) &&
+                             __hip_atomic_load(a.flags + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch;
+                 ++it)
+                __builtin_amdgcn_s_sleep(2);
+        }
+        __syncthreads();
+        const size_t off = (size_t)bh * K * kHeadDim;
+        const i32x4 rh = make_rsrc(a.Khi + off, Ly::PLANE);
+        const i32x4 rv = make_rsrc(a.Vb + off, Ly::PLANE);
+        const i32x4 rl = make_rsrc(a.Klo + off, Ly::LOB);
+        const i32x4 rs = make_rsrc(a.Ksc + (size_t)bh * K * 2, K * 2);
+        const int lrow = lane >> 3, lpc = lane & 7;
+        for (int I = wave; I < K / 8; I += 8) {   // 8 rows of 128 bytes per instruction
+            const int r = I * 8 + lrow;
+            const int lck = lpc ^ swz16(r);
+            const int lcv = 2 * ((lpc >> 1) ^ (r & 3)) + (lpc & 1);
+            dma16_coherent(rh, lds0 + I * 1024, (uint32_t)(r * 128 + lck * 16));
+            dma16_coherent(rv, lds0 + Ly::OFF_V + I * 1024, (uint32_t)(r * 128 + lcv * 16));
+        }
+        for (int I = wave; I < K / 16; I += 8) {  // 16 rows of 64 bytes per instruction
+            const int r = I * 16 + (lane >> 2), ch = lane & 3;
+            dma16_coherent(rl, lds0 + Ly::OFF_L + I * 1024, (uint32_t)(r * 64 + ((ch ^ ((r >> 1) & 3)) << 4)));
+        }
+        if (wave == 0) dma16_coherent(rs, lds0 + Ly::OFF_S, (uint32_t)(lane * 16));   // past K*2: zeros
+        vmcnt_le<0>();
+        __syncthreads();
+    }
+
     // ---- attention over this workgroup's query tiles t0 .. t1 - 1, tile t0 + j to wave j % 8
-    if (t0 + wave >= t1) return;
+    if (t0 + wave < t1) {
     const Lanes ln = attn_lanes<KB>(lds0, lane);
     int scl[2];
     attn_scales<KB>(smem, lane, scl);
@@ -283,6 +376,29 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
         tile_store(stg, coff, lane, o0, o1, z, a.O + (rowbase + (size_t)tile * kTileQ) * kHeadDim,
                    tile * kTileQ, L);
     }
+    }
+    };
+
+    const int w = blockIdx.x;
+    if constexpr (!HANDOFF) {
+        int bh = w, lo = 0, den = 1;
+        if (w >= a.whole) {
+            const int r = w - a.whole;
+            bh = a.whole + r / a.parts;
+            lo = r % a.parts;
+            den = a.parts;
+        }
+        run_unit(bh, false, false, lo, lo + 1, den);
+    } else {
+        // `grid` workgroups for grid + extra units: workgroup 2 j projects and publishes the extra
+        // unit grid + j before its own unit; workgroup 2 j + 1 attends it after its own
+        const int units = a.B * a.H;
+        const bool paired = w < 2 * (units - a.grid);
+        const int extra = a.grid + (w >> 1);
+        if (paired && (w & 1) == 0) run_unit(extra, false, true, 0, 0, 1);
+        run_unit(w, false, false, 0, 1, 1);
+        if (paired && (w & 1) == 1) run_unit(extra, true, false, 0, 1, 1);
+    }
 }
 
 }  // namespace
@@ -291,18 +407,29 @@ bool fused_supported(int n, int k) { return n <= 1024 && (k == 128 || k == 256);
 
 hipError_t launch_fused_bf16(const FusedBf16Args& a, hipStream_t stream) {
     const int units = a.B * a.H;
-    if (a.whole < 0 || a.whole > units || a.parts < 1) return hipErrorInvalidValue;
-    const dim3 grid(a.whole + (units - a.whole) * a.parts), block(kThreads);
+    int nwg;
+    if (a.mode == 2) {
+        if (a.grid >= units || 2 * (units - a.grid) > a.grid || !a.flags || !a.epoch || a.dm > 0)
+            return hipErrorInvalidValue;
+        nwg = a.grid;
+    } else {
+        if (a.mode != 0 || a.whole < 0 || a.whole > units || a.parts < 1) return hipErrorInvalidValue;
+        nwg = a.whole + (units - a.whole) * a.parts;
+    }
+    const dim3 grid(nwg), block(kThreads);
     if (a.dm > 0 && (a.dm % kStep || a.dm != 64 * a.H)) return hipErrorInvalidValue;
     const bool stack = a.dm > 0;
+    const bool ho = a.mode == 2;
     switch (a.k) {
         case 128:
-            if (stack) hipLaunchKernelGGL((fused_bf16_kernel<4, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((fused_bf16_kernel<4, false>), grid, block, 0, stream, a);
+            if (stack) hipLaunchKernelGGL((fused_bf16_kernel<4, true, false>), grid, block, 0, stream, a);
+            else if (ho) hipLaunchKernelGGL((fused_bf16_kernel<4, false, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((fused_bf16_kernel<4, false, false>), grid, block, 0, stream, a);
             break;
         case 256:
-            if (stack) hipLaunchKernelGGL((fused_bf16_kernel<8, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((fused_bf16_kernel<8, false>), grid, block, 0, stream, a);
+            if (stack) hipLaunchKernelGGL((fused_bf16_kernel<8, true, false>), grid, block, 0, stream, a);
+            else if (ho) hipLaunchKernelGGL((fused_bf16_kernel<8, false, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((fused_bf16_kernel<8, false, false>), grid, block, 0, stream, a);
             break;
         default: return hipErrorInvalidValue;
     }

@@ -255,11 +255,24 @@ struct FusedBf16Args {
     int e_heads;            // H (per-head E_h) or 1
     float c;                // scale * log2(e)
     int dm;                 // 0, or d_model for the stack form
-    // Work split: workgroups 0 .. whole - 1 take (b, h) = their index, all of its query tiles;
-    // the units after those are each taken by `parts` workgroups that all project the unit and
-    // attend contiguous shares of its tiles (a last round of fewer units than compute units)
+    // Work split, mode 0: workgroups 0 .. whole - 1 take (b, h) = their index, all of its query
+    // tiles; the units after those are each taken by `parts` workgroups that all project the unit
+    // and attend contiguous shares of its tiles (a last round of fewer units than compute units).
+    // Mode 2 (grid < units <= 3 grid / 2, sequence form): `grid` workgroups each take unit w;
+    // workgroup 2 j also projects the extra unit grid + j first and publishes its planes in
+    // global memory (Khi, Klo, Ksc, Vb in the attention kernel's format, then an epoch-tagged
+    // flag per unit), and workgroup 2 j + 1 attends all of it after its own unit.  A workgroup
+    // only waits for a unit published by a workgroup of lower index.
     int whole;
     int parts;
+    int mode;
+    int grid;
+    uint16_t* Khi;
+    uint8_t* Klo;
+    uint8_t* Ksc;
+    uint16_t* Vb;
+    unsigned long long* flags;   // one per unit
+    unsigned long long epoch;    // this call's tag (nonzero)
 };
 bool fused_supported(int n, int k);
 hipError_t launch_fused_bf16(const FusedBf16Args& a, hipStream_t stream);

@@ -104,7 +104,8 @@ typedef struct lf_problem {
 const char* linformer_status_string(int status);
 
 /* Bytes of device workspace linformer_forward() and linformer_project_kv() need for `p`
- * (it covers Kbar/Vbar staging and the projection's split partial sums).  Host only. */
+ * (it covers Kbar/Vbar staging, the projection's split partial sums and, for shapes the
+ * one-launch short-sequence path takes, one 8-byte hand-off flag per (b, h)).  Host only. */
 int linformer_workspace_size(const lf_problem* p, size_t* bytes);
 
 /* Bytes of the Kbar and Vbar buffers linformer_project_kv() writes and linformer_attend() reads.

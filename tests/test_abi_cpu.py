@@ -66,12 +66,14 @@ def _r256(x):
     (32, 12, 512, 256, L.LF_SHARE_KV, 1),         # short reduction over many tiles: unsplit
 ])
 def test_workspace_holds_partials_only_for_split_projections(B, H, n, k, share, splits):
-    """The forward workspace is Kbar | Vbar | fp32 partial sums of the position splits, each
-    region 256-byte aligned; an unsplit projection needs no partials.  Three or more splits keep
-    [splits, 2, B, H, k, 64] for the fixup pass; two splits are paired inside the projection
-    kernel, which needs one block of sums per workgroup tile (128 slots x 4 units x 64 columns
-    at the bench shape: 2 (keys, values) x 12 heads x 2 slot tiles x 2 unit tiles) and one
-    8-byte counter per tile.  Pins the host's split plan for a few shapes."""
+    """The forward workspace is Kbar | Vbar | fp32 partial sums of the position splits | the
+    one-launch kernel's hand-off flags, each region 256-byte aligned; an unsplit projection needs
+    no partials.  Three or more splits keep [splits, 2, B, H, k, 64] for the fixup pass; two
+    splits are paired inside the projection kernel, which needs one block of sums per workgroup
+    tile (128 slots x 4 units x 64 columns at the bench shape: 2 (keys, values) x 12 heads x 2
+    slot tiles x 2 unit tiles) and one 8-byte counter per tile.  Shapes the one-launch
+    short-sequence kernel takes (bf16, n <= 1024, k of 128 or 256) add one 8-byte flag per
+    (b, h).  Pins the host's split plan for a few shapes."""
     p = L.problem(B, H, n, 64, k, L.LF_BF16, share)
     kb, vb = L.linformer_kv_sizes(p)
     if splits == 2:
@@ -79,7 +81,8 @@ def test_workspace_holds_partials_only_for_split_projections(B, H, n, k, share, 
         part = _r256(tiles * 128 * 4 * 64 * 4) + 8 * tiles
     else:
         part = splits * 2 * B * H * k * 64 * 4 if splits > 1 else 0
-    assert L.linformer_workspace_size(p) == _r256(kb) + _r256(vb) + _r256(part)
+    flags = 8 * B * H if n <= 1024 and k in (128, 256) else 0
+    assert L.linformer_workspace_size(p) == _r256(kb) + _r256(vb) + _r256(part) + _r256(flags)
 
 
 @pytest.mark.parametrize("field,value,code", [
