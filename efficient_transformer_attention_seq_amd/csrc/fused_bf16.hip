@@ -29,8 +29,9 @@
 // copies its planes, un-swizzled, to the workspace in the attention kernel's format with
 // agent-coherent stores, then sets the unit's flag to the call's tag; workgroup 2 j + 1, after
 // its own unit, waits for that flag (set by a workgroup of lower index, which is already
-// running), loads the planes with agent-coherent loads and attends all of the unit's tiles.  The
-// planes are the same bytes either way, so the output is bitwise that of the plain split.
+// running), loads the planes with agent-coherent loads, clears the flag (a replayed graph reuses
+// the captured call's tag) and attends all of the unit's tiles.  The planes are the same bytes
+// either way, so the output is bitwise that of the plain split.
 #include "attend_core.h"
 
 namespace lf {
@@ -351,6 +352,9 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(FusedBf16Args a) {
         if (wave == 0) dma16_coherent(rs, lds0 + Ly::OFF_S, (uint32_t)(lane * 16));   // past K*2: zeros
         vmcnt_le<0>();
         __syncthreads();
+        // consumed: clear the flag, so that a replay of this call (a captured graph reuses its
+        // tag) waits for its own publication again
+        if (tid == 0) __hip_atomic_store(a.flags + bh, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // ---- attention over this workgroup's query tiles t0 .. t1 - 1, tile t0 + j to wave j % 8

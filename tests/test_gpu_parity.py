@@ -718,6 +718,58 @@ def test_error_paths_on_device():
     torch.cuda.synchronize()
 
 
+def test_forward_fused_handoff_in_hip_graph():
+    """The hand-off captured in a HIP graph: replays carry the tag of the captured call, so each
+    consumer clears its flag once it has read the planes.  Replays back to back on one workspace,
+    each with new inputs copied into the captured buffers, equal the eager results bitwise."""
+    torch = G.torch_mod()
+    B, H, n, k = 24, 12, 256, 256   # 288 (b, h) units: 32 of them handed off
+    lens = [256, 200, 77, 256] * 6
+    inputs = [synth.random_inputs(B, H, n, 64, k, BF, KV, seed=60 + i, lengths=lens)
+              for i in range(3)]
+    wl = inputs[0].wl
+    p = G.prob(wl)
+    shp = (B, H, n, 64)
+    Q, K, V = (G.empty(shp, BF) for _ in range(3))
+    E = G.dev(inputs[0].E, BF)
+    lensd = G.lengths_dev(lens)
+    O = G.empty(shp, BF)
+    wsb = L.linformer_workspace_size(p)
+    ws, ws2 = (torch.empty(wsb, dtype=torch.uint8, device="cuda") for _ in range(2))
+
+    def load(inp):
+        Q.copy_(G.dev(inp.Q, BF))
+        K.copy_(G.dev(inp.K, BF))
+        V.copy_(G.dev(inp.V, BF))
+
+    refs = []
+    for inp in inputs:   # eager results, on another workspace
+        load(inp)
+        ref = G.empty(shp, BF)
+        L.linformer_forward(p, Q, K, V, E, None, lensd, ref, ws2, wsb)
+        torch.cuda.synchronize()
+        refs.append(ref)
+    load(inputs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm up on the capture stream
+        L.linformer_forward(p, Q, K, V, E, None, lensd, O, ws, wsb)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        L.linformer_forward(p, Q, K, V, E, None, lensd, O, ws, wsb)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for inp, ref in zip(inputs, refs):
+            load(inp)
+            O.fill_(7.0)
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(O, ref), rep
+    G.log("hand-off graph replays equal the eager calls")
+
+
 def test_forward_in_hip_graph():
     """linformer_forward captured once into a HIP graph and replayed: every replay, with new
     inputs copied into the captured buffers and eager work between replays, equals the eager
