@@ -208,6 +208,30 @@ def test_k_equals_one_gives_projected_value_row():
     np.testing.assert_allclose(O[0, 0], np.tile(want, (n, 1)), rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("share", [orc.SHARE_NONE, orc.SHARE_KV])
+def test_one_token_item_closed_form(share):
+    """An item of one valid position: every projected key is E[r, 0] K_0 and every projected value
+    F[r, 0] V_0, so row 0 of the output is (sum_r w_r F[r, 0]) V_0 with w the softmax over r of
+    scale (q_0 . K_0) E[r, 0], written here with plain loops (a weighted mean of one column of
+    F times one value row), and rows past the length are zero."""
+    rng = np.random.default_rng(31)
+    n, d, k = 6, 4, 5
+    Q, K, V = _rand(rng, 1, 1, n, d), _rand(rng, 1, 1, n, d), _rand(rng, 1, 1, n, d)
+    E = _rand(rng, 1, k, n)
+    F = _rand(rng, 1, k, n) if share == orc.SHARE_NONE else None
+    Fm = (F if F is not None else E)[0]
+    O = orc.forward(Q, K, V, E, F, share, lengths=[1])
+    scale = 1.0 / math.sqrt(d)
+    qk = sum(Q[0, 0, 0, c] * K[0, 0, 0, c] for c in range(d))
+    logits = [scale * qk * E[0, r, 0] for r in range(k)]
+    top = max(logits)
+    z = sum(math.exp(x - top) for x in logits)
+    coef = sum(math.exp(logits[r] - top) / z * Fm[r, 0] for r in range(k))
+    want = np.zeros((n, d))
+    want[0] = [coef * V[0, 0, 0, c] for c in range(d)]
+    np.testing.assert_allclose(O[0, 0], want, rtol=1e-12, atol=1e-14)
+
+
 def test_zero_queries_give_mean_of_vbar():
     rng = np.random.default_rng(23)
     n, d, k = 10, 4, 6
