@@ -53,6 +53,28 @@ def test_conv_parity(B, H, n, k, share, lengths):
     assert ek <= KBAR_TOL and ev <= VBAR_TOL and eo <= 2e-2
 
 
+def _random_conv_case(seed):
+    """A seeded shape: k of 32 to 256, window n / k of 1 to 64 with n <= 4096, batch and heads
+    1-4, any sharing mode, lengths drawn from 1, n, a random value and 0 (one item of every
+    multi-item batch)."""
+    rng = np.random.default_rng(9100 + seed)
+    k = int(rng.choice([32, 64, 128, 256]))
+    windows = [w for w in (1, 2, 4, 8, 16, 32, 64) if w * k <= 4096 and (w * k) % 64 == 0]
+    n = k * int(rng.choice(windows))
+    B, H = int(rng.integers(1, 5)), int(rng.integers(1, 5))
+    share = [NONE, HEAD, KV, LAYER][int(rng.integers(0, 4))]
+    pool = [1, n, int(rng.integers(1, n + 1))]
+    lens = [pool[int(rng.integers(0, len(pool)))] for _ in range(B)]
+    if B > 1:
+        lens[int(rng.integers(0, B))] = 0
+    return B, H, n, k, share, lens
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_conv_random_shapes(seed):
+    test_conv_parity(*_random_conv_case(seed))
+
+
 def test_mean_pooling_matches_dense_banded_projection():
     """Mean pooling through the convolution path and through the dense projection with the
     banded E materialised: both against the oracle, and against each other."""
