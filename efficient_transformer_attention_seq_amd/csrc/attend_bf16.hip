@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendBf16Args a)
     const int w = xcd_remap(blockIdx.x, G);   // G is a multiple of 8, so every block is mapped
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int lane = tid & 63, hh = lane >> 5;
 
     // ---- lengths -> LDS: clamped length per batch item and the valid-tile prefix over batch items
     // (one round of loads, then a scan), so no later step waits on global memory for them

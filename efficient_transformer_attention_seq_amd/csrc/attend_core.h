@@ -282,7 +282,6 @@ __device__ __forceinline__ void tile_math(const Lanes& ln, const bf16x8 (&qop)[4
         o1[j] = 0.0f;
     }
     z = 0.0f;
-    float mref = 0.0f;
 
     scores(0, sc[0]);
 #pragma unroll
@@ -309,7 +308,6 @@ __device__ __forceinline__ void tile_math(const Lanes& ln, const bf16x8 (&qop)[4
                 o1 *= alpha;
                 z *= alpha;
             }
-            mref += sh;
             // in place (tied operands), so the common path needs no register copies
 #pragma unroll
             for (int j = 0; j < 16; ++j) asm volatile("v_sub_f32 %0, %0, %1" : "+v"(bias[j]) : "v"(sh));

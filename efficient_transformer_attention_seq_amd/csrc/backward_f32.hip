@@ -376,9 +376,6 @@ __global__ __launch_bounds__(64 * kAttWaves) void bw_attend_kernel(BwAttendArgs 
         qr.load(rsq, q, g);
         gr.load(rsg, q, g);
     };
-    // per-lane LDS offsets of the transposed Kbar^T reads: source lane s = l of group g reads
-    // columns 16 cb + 4 (l % 4) of rows 32 j + 4 g + l / 4 (+ 16)
-    const int tr_row = 4 * g + (l >> 2), tr_col = 4 * (l & 3);
     // the first block's rows are in flight while Kbar and Vbar are staged
     bool loaded = false;
     if (blk0 < blk1 && blk0 * kAttRows + wave * 16 < min(a.n, L)) {

@@ -84,7 +84,7 @@ __device__ __forceinline__ void vmcnt_le() {
 template <int BT>
 __global__ __launch_bounds__(LinTile<BT>::kThreads) void linear_bf16_kernel(LinearBf16Args a) {
     using Tl = LinTile<BT>;
-    constexpr int kWaves = Tl::kWaves, kTileX = Tl::kTileX, kStage = Tl::kStage;
+    constexpr int kWaves = Tl::kWaves, kStage = Tl::kStage;
     constexpr int kDmaW = Tl::kDmaW, kPer = Tl::kPer;
     constexpr int kBT = BT;
     __shared__ __attribute__((aligned(16))) uint8_t smem[kNS * kStage];
