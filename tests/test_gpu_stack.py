@@ -104,6 +104,36 @@ def test_stack_fused_parity(batch, n, d_model, k, layers, lens):
     assert diff <= 1e-2
 
 
+def _random_stack_case(seed):
+    """A seeded shape: batch 1-3, n a multiple of 64 up to 512, d_model of 192 or 384 (whole
+    192-feature tiles of the output map), k a multiple of 32 up to 256, one to three layers, and
+    lengths from 1 to n (or none)."""
+    rng = np.random.default_rng(9300 + seed)
+    batch = int(rng.integers(1, 4))
+    n = 64 * int(rng.integers(1, 9))
+    d_model = int(rng.choice([192, 384]))
+    k = 32 * int(rng.integers(1, 9))
+    layers = int(rng.integers(1, 4))
+    lens = None if rng.random() < 0.3 else [int(x) for x in rng.integers(1, n + 1, size=batch)]
+    return batch, n, d_model, k, layers, lens
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_stack_random_shapes(seed):
+    batch, n, d_model, k, layers, lens = _random_stack_case(seed)
+    wl = _stack_wl(batch, n, d_model, k, layers, seed=20 + seed)
+    G.log(f"stack random {wl.name} lengths {lens}")
+    si = synth.make_stack_inputs(wl, lengths=lens)
+    Y, ok = G.run_stack(si, keep_layers=True, guard=True)
+    assert ok, "stray writes outside Y"
+    assert np.all(np.isfinite(Y))
+    _check_layers(si, Y)
+    if lens is not None:
+        for l in range(layers):
+            for b, Lb in enumerate(lens):
+                assert np.all(Y[l][b, Lb:] == 0.0)
+
+
 def test_stack_last_layer_only_matches_kept():
     wl = _stack_wl(2, 256, 384, 64, 3)
     si = synth.make_stack_inputs(wl)
