@@ -14,9 +14,12 @@ from tests import gpu_util as G
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # B, H, n, k, share, lengths: the first needs split partials in the scratch, the second not
+    # B, H, n, k, share, lengths: the first needs split partials in the scratch, the second not;
+    # the third has more (b, h) units than a 256-unit device has compute units, so the one-launch
+    # kernel hands extra units between workgroups through the scratch's planes and flags
     (4, 6, 2048, 256, synth.SHARE_NONE, [2048, 1500, 700, 33]),
     (2, 3, 512, 128, synth.SHARE_KV, [512, 257]),
+    (24, 12, 256, 256, synth.SHARE_KV, [256, 200, 77, 0] * 6),
 ]
 
 
@@ -54,3 +57,6 @@ def test_noalloc_forward_twice_second_smaller():
     _run_both(CASES[1], seed=32)
     # the larger problem again, after the smaller one left its values in the buffer
     _run_both(CASES[0], seed=33)
+    # the hand-off twice: the second call finds the first one's planes and cleared flags
+    _run_both(CASES[2], seed=34)
+    _run_both(CASES[2], seed=35)
