@@ -645,8 +645,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures a single GPU; --gpus N > 1 is not supported by this build "
-              "(the path is per-GPU; see the sharding notes)", file=sys.stderr)
+        print("bench.py measures one GPU: --gpus N > 1 is not supported (every kernel runs on "
+              "one device's share of the work)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
